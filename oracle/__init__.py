@@ -1,0 +1,34 @@
+"""fp64 CPU oracle for one DFlash draft-and-verify step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product path (the HIP library
+and its Python binding) never imports, links or executes anything here, and
+this package imports nothing from the product.
+
+Parity status per function (what pins it is listed in the tests that check
+it; see ``tests/test_oracle_*.py``):
+
+* ``rms_norm``, ``rope``, ``silu``, ``linear``, ``attention``,
+  ``argmax_lowest``, ``accept``, ``inject``, ``draft_forward``, ``verify``,
+  ``speedup``: pinned by brute force, closed forms and invariants.
+* End-to-end drafted token values on random weights have no external
+  reference value; they are pinned only through the invariants above
+  (permutation equivariance, position-shift invariance, incremental
+  injection) and compared with the GPU under the logit-gap rule.
+"""
+from .dflash_oracle import (  # noqa: F401
+    OracleCache,
+    accept,
+    argmax_lowest,
+    attention,
+    draft_block,
+    draft_forward,
+    inject,
+    linear,
+    rms_norm,
+    rope,
+    silu,
+    speedup,
+    step,
+    verify,
+)

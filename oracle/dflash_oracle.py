@@ -1,0 +1,289 @@
+"""Plain fp64 reference of one DFlash draft-and-verify step (numpy).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+
+Sources (page title, then section):
+
+* [Report/KP]  "DFlash, Diffusion LLMs, dLLM, MTP and Speculative Decoding:
+  A Deep Research Report", "Key points": target-context features from
+  several layers are injected into the K/V projections of every draft layer
+  and kept in the draft KV cache; the drafter fills a block of 16 masked
+  positions in one forward pass.
+* [Report/Why]  same page, "Why DFlash beats EAGLE-3", item 3, and the
+  MTP-vs-diffusion comparison table: attention is bidirectional inside the
+  block.
+* [Term/WF]  "Term: DFlash speculative decoding", "DFlash: architecture and
+  workflow": anchor at the frontier, one drafting pass, the target computes
+  logits at every block position and checks the draft against its argmax,
+  the longest contiguous accepted prefix is emitted and decoding falls back
+  to the target for the next token.
+* [Term/Math]  same page, "Mathematical view of acceptance and speedup":
+  S ~= C_AR / (C_DF / E[L]).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): one drafting pass (T = 1); B drafted tokens, one per block
+slot, slot 0 holding the last accepted token; B + 1 verify rows so the
+fallback ("bonus") token always exists; rotate-half RoPE with
+omega_i = theta^(-2i/d) on q and k of the block and on k of injected rows;
+contiguous GQA grouping; softmax scale 1/sqrt(d) with no mask; RMSNorm with
+eps inside the square root and a per-channel gain; SwiGLU MLP; no biases;
+the injected context c = RMSNorm(W_fc [f_0 .. f_{n-1}]) is projected by each
+layer's own W_k / W_v; block K/V are not stored in the cache; ties in argmax
+go to the lowest index.
+
+Everything is computed in float64 from the stored input values (bf16 inputs
+arrive as exactly-representable float32 values and are widened, never
+re-rounded).  Large matrices are widened one row chunk at a time.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_CHUNK_ROWS = 8192
+
+
+# --------------------------------------------------------------- primitives
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = x W^T for W stored [out, in] (the PyTorch Linear convention).
+
+    ``x`` is [..., in]; W is widened to fp64 in row chunks so that a
+    151936 x 4096 matrix never exists in fp64 all at once."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape[:-1] + (w.shape[0],), dtype=np.float64)
+    for r0 in range(0, w.shape[0], _CHUNK_ROWS):
+        wc = np.asarray(w[r0:r0 + _CHUNK_ROWS], dtype=np.float64)
+        out[..., r0:r0 + wc.shape[0]] = x @ wc.T
+    return out
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain, over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x) = x / (1 + exp(-x))."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half rotary embedding.
+
+    ``x`` is [n, heads, d]; ``positions`` is [n].  Channel i < d/2 is paired
+    with channel i + d/2 and the pair is rotated by the angle
+    position * theta^(-2i/d).  theta == 0 disables the rotation."""
+    x = np.asarray(x, dtype=np.float64)
+    if theta == 0:
+        return x.copy()
+    d = x.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = float(theta) ** (-2.0 * i / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Unmasked softmax attention with grouped K/V heads.
+
+    q: [Bq, n_q, d]; k, v: [T, n_kv, d].  Query head h reads K/V head
+    h // (n_q / n_kv).  Every query sees every key (bidirectional inside the
+    block and the whole injected context, [Report/Why], [Term/WF])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, nkv, d = q.shape[1], k.shape[1], q.shape[2]
+    group = nq // nkv
+    out = np.empty_like(q)
+    for h in range(nq):
+        g = h // group
+        s = (q[:, h, :] @ k[:, g, :].T) / np.sqrt(d)          # [Bq, T]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, g, :]
+    return out
+
+
+def argmax_lowest(logits: np.ndarray):
+    """Index of the maximum along the last axis, lowest index on ties, and
+    the gap between the largest and second-largest logit (0 on a tie)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    idx = np.argmax(logits, axis=-1)          # numpy returns the first maximum
+    top1 = np.take_along_axis(logits, idx[..., None], axis=-1)[..., 0]
+    masked = logits.copy()
+    np.put_along_axis(masked, idx[..., None], -np.inf, axis=-1)
+    top2 = masked.max(axis=-1)
+    return idx.astype(np.int64), top1 - top2
+
+
+def accept(draft: np.ndarray, target_argmax: np.ndarray):
+    """Greedy acceptance ([Term/WF] stages three and four).
+
+    draft: [b, B]; target_argmax: [b, B+1].  L is the length of the longest
+    prefix on which the drafted tokens equal the target's argmax; the
+    fallback token is the target's argmax at the first mismatch (row B when
+    the whole block matches)."""
+    draft = np.asarray(draft)
+    tgt = np.asarray(target_argmax)
+    b, B = draft.shape
+    L = np.zeros(b, dtype=np.int64)
+    bonus = np.zeros(b, dtype=np.int64)
+    for s in range(b):
+        n = 0
+        while n < B and draft[s, n] == tgt[s, n]:
+            n += 1
+        L[s] = n
+        bonus[s] = tgt[s, n]
+    return L, bonus
+
+
+def speedup(c_ar: float, c_df: float, mean_accept: float) -> float:
+    """S ~= C_AR / (C_DF / E[L]) ([Term/Math])."""
+    return c_ar / (c_df / mean_accept)
+
+
+# ------------------------------------------------------------------ the step
+
+@dataclass
+class OracleCache:
+    """Draft KV cache in fp64: k, v are [n_layers, batch, n_kv, capacity, d];
+    ``length`` holds the number of valid positions per sequence."""
+
+    k: np.ndarray
+    v: np.ndarray
+    length: np.ndarray
+
+    @classmethod
+    def empty(cls, dims, batch: int, capacity: int) -> "OracleCache":
+        shape = (dims.n_layers, batch, dims.n_kv_heads, capacity, dims.head_dim)
+        return cls(np.zeros(shape), np.zeros(shape), np.zeros(batch, dtype=np.int64))
+
+
+def _get(w, name):
+    return getattr(w, name) if not isinstance(w, dict) else w[name]
+
+
+def inject(dims, weights, cache: OracleCache, feats: Sequence[np.ndarray],
+           pos_offset: int = 0) -> List[np.ndarray]:
+    """KV injection ([Report/KP]).
+
+    For sequence s with new feature rows F_s [n_s, n_f * H] written at cache
+    slots len_s + i (rotary position len_s + i + pos_offset):
+    c = RMSNorm(W_fc F_s) * g_fc; for every layer l, K = RoPE(W_k^l c, P) and
+    V = W_v^l c are written at those slots.  Returns the fused context rows c
+    per sequence (for inspection)."""
+    nkv, d = dims.n_kv_heads, dims.head_dim
+    fused = []
+    for s, F in enumerate(feats):
+        n = F.shape[0]
+        start = int(cache.length[s])
+        if start + n > cache.k.shape[3]:
+            raise ValueError("cache capacity exceeded")
+        u = linear(F, _get(weights, "w_fc"))
+        c = rms_norm(u, _get(weights, "fc_norm"), dims.rms_eps)
+        pos = np.arange(start, start + n) + pos_offset
+        for l, lw in enumerate(_get(weights, "layers")):
+            k = linear(c, lw["wk"]).reshape(n, nkv, d)
+            v = linear(c, lw["wv"]).reshape(n, nkv, d)
+            k = rope(k, pos, dims.rope_theta)
+            cache.k[l, s, :, start:start + n, :] = k.transpose(1, 0, 2)
+            cache.v[l, s, :, start:start + n, :] = v.transpose(1, 0, 2)
+        cache.length[s] = start + n
+        fused.append(c)
+    return fused
+
+
+def draft_forward(dims, weights, cache: OracleCache, last_tok: np.ndarray,
+                  keep_logits: bool = False, pos_offset: int = 0) -> Dict[str, np.ndarray]:
+    """One block-diffusion drafting pass ([Report/KP], [Term/WF] stage two).
+
+    The block holds the last accepted token followed by B-1 mask tokens at
+    positions len_s .. len_s + B - 1.  Each layer: RMSNorm, q/k/v
+    projections, RoPE on q and k, attention over the injected context K/V of
+    that layer followed by the block's own K/V (no mask), output projection
+    and residual, RMSNorm, SwiGLU MLP and residual.  A final RMSNorm and the
+    shared lm_head give logits whose lowest-index argmax is the drafted
+    token of each slot.
+
+    Returns tokens [b, B], gaps [b, B], per-layer attention outputs
+    (pre-projection, [L][b, B, n_q*d]), the residual after the attention
+    half and after each full layer, and the final normed hidden."""
+    last_tok = np.asarray(last_tok, dtype=np.int64)
+    toks = np.full((last_tok.shape[0], dims.block_size), dims.mask_id, dtype=np.int64)
+    toks[:, 0] = last_tok
+    return draft_block(dims, weights, cache, toks, keep_logits, pos_offset)
+
+
+def draft_block(dims, weights, cache: OracleCache, toks: np.ndarray,
+                keep_logits: bool = False, pos_offset: int = 0) -> Dict[str, np.ndarray]:
+    """The drafting pass over an arbitrary block of token ids [b, B]
+    (``draft_forward`` supplies [last token, mask, ..., mask])."""
+    toks = np.asarray(toks, dtype=np.int64)
+    b, B = toks.shape
+    H, nq, nkv, d = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    embed = _get(weights, "embed")
+    layers = _get(weights, "layers")
+    h = np.asarray(embed[toks.reshape(-1)], dtype=np.float64).reshape(b, B, H)
+    attn_outs, mids, hiddens = [], [], [h.copy()]
+    for l, lw in enumerate(layers):
+        a = rms_norm(h, lw["attn_norm"], dims.rms_eps)
+        q = linear(a, lw["wq"]).reshape(b, B, nq, d)
+        k = linear(a, lw["wk"]).reshape(b, B, nkv, d)
+        v = linear(a, lw["wv"]).reshape(b, B, nkv, d)
+        o = np.empty((b, B, nq, d))
+        for s in range(b):
+            C = int(cache.length[s])
+            pos = np.arange(C, C + B) + pos_offset
+            qs = rope(q[s], pos, dims.rope_theta)
+            ks = rope(k[s], pos, dims.rope_theta)
+            keys = np.concatenate([cache.k[l, s, :, :C, :].transpose(1, 0, 2), ks], axis=0)
+            vals = np.concatenate([cache.v[l, s, :, :C, :].transpose(1, 0, 2), v[s]], axis=0)
+            o[s] = attention(qs, keys, vals)
+        o = o.reshape(b, B, nq * d)
+        attn_outs.append(o)
+        h = h + linear(o, lw["wo"])
+        mids.append(h.copy())
+        a = rms_norm(h, lw["mlp_norm"], dims.rms_eps)
+        act = silu(linear(a, lw["w_gate"])) * linear(a, lw["w_up"])
+        h = h + linear(act, lw["w_down"])
+        hiddens.append(h.copy())
+    z = rms_norm(h, _get(weights, "final_norm"), dims.rms_eps)
+    logits = linear(z, _get(weights, "lm_head"))
+    tokens, gaps = argmax_lowest(logits)
+    out = {"tokens": tokens, "gaps": gaps, "attn_out": attn_outs, "mid": mids,
+           "hidden": hiddens, "final": z}
+    if keep_logits:
+        out["logits"] = logits
+    return out
+
+
+def verify(dims, lm_head: np.ndarray, target_hidden: np.ndarray):
+    """Target argmax at every block row ([Term/WF] stage three).
+
+    target_hidden is the target's final (post-norm) hidden state at the
+    B + 1 rows of its pass over [x, d_0 .. d_{B-1}], shape [b, B+1, H].
+    Returns the lowest-index argmax [b, B+1] and the top-1/top-2 gaps."""
+    th = np.asarray(target_hidden, dtype=np.float64)
+    logits = linear(th, lm_head)
+    return argmax_lowest(logits)
+
+
+def step(dims, weights, cache: OracleCache, feats, last_tok, target_hidden):
+    """inject + draft + verify + accept, in that order."""
+    inject(dims, weights, cache, feats)
+    dr = draft_forward(dims, weights, cache, last_tok)
+    g, vgaps = verify(dims, _get(weights, "lm_head"), target_hidden)
+    L, bonus = accept(dr["tokens"], g)
+    return {"draft": dr, "target_argmax": g, "verify_gaps": vgaps, "accept_len": L, "bonus": bonus}

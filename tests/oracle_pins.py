@@ -1,0 +1,442 @@
+"""Checks that pin the fp64 oracle to facts fixed by the pages and by
+mathematics, independent of the oracle's own formulas.
+
+Each ``check_*`` function raises AssertionError when the oracle is wrong.  The
+functions are called by ``test_oracle_pins.py`` and, against deliberately
+broken copies of the oracle, by ``test_oracle_mutations.py`` (which requires
+every planted mistake to be caught by at least one check).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.dflash_oracle as O
+from block_diffusion_speculative_amd.configs import Dims
+from block_diffusion_speculative_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+SMALL = Dims(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, n_layers=2,
+             intermediate=48, vocab=64, n_feat_layers=2, block_size=6,
+             rope_theta=1e4, rms_eps=1e-6, dtype="f32")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def small_weights(dims=SMALL, seed=3, gain_std=0.2, std=0.3):
+    """Weights with a large spread so that every term visibly matters."""
+    w = I.make_weights(dims, seed, gain_std=gain_std)
+    scale = std / I.WEIGHT_STD
+    for name in ("w_fc", "embed", "lm_head"):
+        setattr(w, name, getattr(w, name) * scale)
+    for lw in w.layers:
+        for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+            lw[k] = lw[k] * scale
+    return w
+
+
+# ------------------------------------------------------------ primitives
+
+def check_linear_triple_loop():
+    g = np.random.default_rng(1)
+    x = g.standard_normal((3, 5))
+    w = g.standard_normal((4, 5))
+    y = O.linear(x, w)
+    for i in range(3):
+        for j in range(4):
+            acc = 0.0
+            for k in range(5):
+                acc += x[i, k] * w[j, k]
+            assert abs(y[i, j] - acc) < 1e-12
+
+
+def check_silu():
+    # silu(0) = 0; silu(x) - silu(-x) = x; silu(x) -> x for large x; sigmoid derivative at 0
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    xs = np.linspace(-6, 6, 25)
+    assert np.allclose(O.silu(xs) - O.silu(-xs), xs, atol=1e-12)
+    assert abs(O.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(O.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    # derivative at zero is 1/2
+    h = 1e-6
+    assert abs((O.silu(np.array([h]))[0] - O.silu(np.array([-h]))[0]) / (2 * h) - 0.5) < 1e-9
+
+
+def check_rms_norm_golden():
+    for case in _golden("rmsnorm_cases.json")["cases"]:
+        y = O.rms_norm(np.array(case["x"]), np.array(case["gain"]), case["eps"])
+        assert np.allclose(y, case["y"], rtol=0, atol=1e-12), (case, y)
+
+
+def check_rms_norm_invariants():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((4, 16))
+    gain = np.ones(16)
+    y = O.rms_norm(x, gain, 0.0)
+    # unit root-mean-square and positive-scale invariance
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-12)
+    assert np.allclose(O.rms_norm(7.5 * x, gain, 0.0), y, atol=1e-12)
+
+
+def check_rope_golden():
+    for case in _golden("rope_cases.json")["cases"]:
+        x = np.array(case["x"], dtype=np.float64).reshape(1, 1, -1)
+        y = O.rope(x, np.array([case["pos"]]), case["theta"])[0, 0]
+        assert np.allclose(y, case["y"], rtol=0, atol=1e-12), (case, y)
+
+
+def check_rope_invariants():
+    g = np.random.default_rng(4)
+    d = 16
+    x = g.standard_normal((5, 3, d))
+    pos = np.array([0, 1, 7, 100, 4095])
+    y = O.rope(x, pos, 1e4)
+    # position 0 is the identity; rotations keep the norm
+    assert np.allclose(y[0], x[0], atol=1e-14)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), atol=1e-12)
+    # complex form: z_i = x_i + 1j x_{i+d/2} is multiplied by exp(1j * pos * theta^(-2i/d))
+    half = d // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    w = np.exp(1j * pos[:, None, None] * (1e4 ** (-2.0 * np.arange(half) / d))[None, None, :])
+    zr = z * w
+    assert np.allclose(y[..., :half], zr.real, atol=1e-12)
+    assert np.allclose(y[..., half:], zr.imag, atol=1e-12)
+    # relative position: <rope(q, a), rope(k, b)> depends only on a - b
+    q = g.standard_normal((1, 1, d))
+    k = g.standard_normal((1, 1, d))
+    for a, b, shift in [(5, 2, 17), (40, 3, 1000), (0, 9, 33)]:
+        s1 = float(np.sum(O.rope(q, np.array([a]), 1e4) * O.rope(k, np.array([b]), 1e4)))
+        s2 = float(np.sum(O.rope(q, np.array([a + shift]), 1e4) * O.rope(k, np.array([b + shift]), 1e4)))
+        assert abs(s1 - s2) < 1e-10
+
+
+def check_argmax_bruteforce():
+    g = np.random.default_rng(5)
+    for trial in range(50):
+        n = int(g.integers(1, 12))
+        vals = g.integers(-3, 4, size=n).astype(np.float64)   # many exact ties
+        idx, gap = O.argmax_lowest(vals[None, :])
+        best, bi = -math.inf, -1
+        for i, v in enumerate(vals):
+            if v > best:
+                best, bi = v, i
+        assert idx[0] == bi
+        srt = sorted(vals, reverse=True)
+        want_gap = (srt[0] - srt[1]) if n > 1 else math.inf
+        assert gap[0] == want_gap
+
+
+def check_attention_bruteforce():
+    g = np.random.default_rng(6)
+    Bq, T, nq, nkv, d = 4, 9, 4, 2, 8
+    q = g.standard_normal((Bq, nq, d))
+    k = g.standard_normal((T, nkv, d))
+    v = g.standard_normal((T, nkv, d))
+    o = O.attention(q, k, v)
+    group = nq // nkv
+    for i in range(Bq):
+        for h in range(nq):
+            kvh = h // group
+            num = [0.0] * d
+            den = 0.0
+            for t in range(T):
+                s = 0.0
+                for c in range(d):
+                    s += q[i, h, c] * k[t, kvh, c]
+                e = math.exp(s / math.sqrt(d))
+                den += e
+                for c in range(d):
+                    num[c] += e * v[t, kvh, c]
+            for c in range(d):
+                assert abs(o[i, h, c] - num[c] / den) < 1e-12
+
+
+def check_attention_closed_forms():
+    g = np.random.default_rng(7)
+    d = 8
+    # all keys equal -> mean of the values
+    q = g.standard_normal((3, 2, d))
+    k = np.repeat(g.standard_normal((1, 2, d)), 6, axis=0)
+    v = g.standard_normal((6, 2, d))
+    o = O.attention(q, k, v)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-12)
+    # one dominant key -> its value
+    k = g.standard_normal((6, 1, d)) * 0.01
+    k[4, 0] = 50.0 * np.ones(d)
+    q = np.ones((2, 1, d))
+    o = O.attention(q, k, np.arange(6 * d, dtype=np.float64).reshape(6, 1, d))
+    assert np.allclose(o, np.arange(4 * d, 5 * d).reshape(1, 1, d).repeat(2, 0), atol=1e-9)
+    # grouped heads equal full multi-head attention on repeated K/V heads
+    q = g.standard_normal((5, 6, d))
+    k = g.standard_normal((7, 2, d))
+    v = g.standard_normal((7, 2, d))
+    o_g = O.attention(q, k, v)
+    o_m = O.attention(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1))
+    assert np.allclose(o_g, o_m, atol=1e-12)
+    # a single key -> its value; scale: two keys with score gap ln 3 * sqrt(d) weigh 1:3
+    for case in _golden("attention_cases.json")["cases"]:
+        o = O.attention(np.array(case["q"])[:, None, :], np.array(case["k"])[:, None, :],
+                        np.array(case["v"])[:, None, :])[:, 0, :]
+        assert np.allclose(o, case["out"], atol=1e-12), (case["name"], o)
+
+
+def check_accept_exhaustive():
+    for B in range(0, 7):
+        for pattern in itertools.product([True, False], repeat=B):
+            tgt = np.arange(B + 1)[None, :] + 100
+            draft = np.array([[tgt[0, j] if m else -1 - j for j, m in enumerate(pattern)]],
+                             dtype=np.int64).reshape(1, B)
+            L, bonus = O.accept(draft, tgt)
+            want = 0
+            for n in range(B + 1):
+                if all(pattern[:n]):
+                    want = n
+            assert L[0] == want and 0 <= L[0] <= B
+            assert (L[0] == B) == all(pattern)
+            assert bonus[0] == tgt[0, want]
+
+
+def check_accept_golden():
+    for case in _golden("accept_cases.json")["cases"]:
+        L, bonus = O.accept(np.array([case["draft"]]), np.array([case["target_argmax"]]))
+        assert L[0] == case["accept_len"] and bonus[0] == case["bonus"], case
+
+
+# ------------------------------------------------------------ whole step
+
+def _prefill(dims, w, batch, C, seed=11, pos_offset=0):
+    cache = O.OracleCache.empty(dims, batch, C + 32)
+    feats = [I.normal(seed, (1, s), (C, dims.feat_dim), 1.0, "f32") for s in range(batch)]
+    O.inject(dims, w, cache, feats, pos_offset=pos_offset)
+    return cache, feats
+
+
+def check_incremental_injection():
+    dims = SMALL
+    w = small_weights(dims)
+    F = I.normal(9, (1,), (11, dims.feat_dim), 1.0, "f32")
+    a = O.OracleCache.empty(dims, 1, 32)
+    O.inject(dims, w, a, [F])
+    b = O.OracleCache.empty(dims, 1, 32)
+    O.inject(dims, w, b, [F[:4]])
+    O.inject(dims, w, b, [F[4:9]])
+    O.inject(dims, w, b, [F[9:]])
+    assert a.length[0] == b.length[0] == 11
+    assert np.allclose(a.k, b.k, atol=1e-12) and np.allclose(a.v, b.v, atol=1e-12)
+
+
+def check_inject_scale_invariance():
+    dims = SMALL
+    w = small_weights(dims)
+    F = I.normal(9, (2,), (5, dims.feat_dim), 1.0, "f32")
+    a = O.OracleCache.empty(dims, 1, 16)
+    O.inject(dims, w, a, [F])
+    b = O.OracleCache.empty(dims, 1, 16)
+    O.inject(dims, w, b, [3.0 * F])
+    # invariant up to eps = 1e-6 against a mean square of order 1
+    assert np.allclose(a.k, b.k, rtol=1e-5, atol=1e-7) and np.allclose(a.v, b.v, rtol=1e-5, atol=1e-7)
+    # the cached V of one row is exactly W_v^l applied to the unit-RMS fused row
+    c = O.inject(dims, w, O.OracleCache.empty(dims, 1, 16), [F])[0]
+    assert np.allclose(np.sqrt(np.mean((c / w.fc_norm) ** 2, axis=-1)), 1.0, atol=1e-6)
+    for l, lw in enumerate(w.layers):
+        v_row = lw["wv"] @ c[2]
+        assert np.allclose(a.v[l, 0, :, 2, :].reshape(-1), v_row, atol=1e-10)
+
+
+def check_inject_layer_major_features():
+    """Feature layer k occupies columns [kH, (k+1)H): zeroing one layer's
+    features equals zeroing the matching block of W_fc."""
+    dims = SMALL
+    w = small_weights(dims)
+    H = dims.hidden
+    F = I.normal(9, (3,), (3, dims.feat_dim), 1.0, "f32").astype(np.float64)
+    F0 = F.copy()
+    F0[:, H:2 * H] = 0.0
+    a = O.OracleCache.empty(dims, 1, 8)
+    O.inject(dims, w, a, [F0])
+    w2 = small_weights(dims)
+    w2.w_fc = w2.w_fc.copy()
+    w2.w_fc[:, H:2 * H] = 0.0
+    b = O.OracleCache.empty(dims, 1, 8)
+    O.inject(dims, w2, b, [F])
+    assert np.allclose(a.k, b.k, atol=1e-12)
+
+
+def check_permutation_equivariance():
+    """With RoPE off, the block is bidirectional and unmasked, so permuting
+    the block's tokens permutes every output row, and all mask slots of
+    [x, m, ..., m] are identical."""
+    dims = Dims(**{**SMALL.__dict__, "rope_theta": 0.0})
+    w = small_weights(dims)
+    cache, _ = _prefill(dims, w, 1, 10)
+    g = np.random.default_rng(8)
+    toks = g.integers(0, dims.vocab - 1, size=(1, dims.block_size))
+    perm = g.permutation(dims.block_size)
+    a = O.draft_block(dims, w, cache, toks, keep_logits=True)
+    b = O.draft_block(dims, w, cache, toks[:, perm], keep_logits=True)
+    assert np.allclose(a["logits"][:, perm], b["logits"], atol=1e-10)
+    for l in range(dims.n_layers):
+        assert np.allclose(a["attn_out"][l][:, perm], b["attn_out"][l], atol=1e-10)
+    d = O.draft_forward(dims, w, cache, toks[:, 0], keep_logits=True)
+    assert np.allclose(d["logits"][0, 1:], d["logits"][0, 1:2].repeat(dims.block_size - 1, 0), atol=1e-10)
+    assert not np.allclose(d["logits"][0, 0], d["logits"][0, 1])
+
+
+def check_position_shift_invariance():
+    """RoPE scores depend on position differences only, so shifting every
+    position (context and block) by the same amount changes nothing."""
+    dims = SMALL
+    w = small_weights(dims)
+    a_cache, _ = _prefill(dims, w, 2, 12)
+    b_cache, _ = _prefill(dims, w, 2, 12, pos_offset=37)
+    last = np.array([5, 17])
+    a = O.draft_forward(dims, w, a_cache, last, keep_logits=True)
+    b = O.draft_forward(dims, w, b_cache, last, keep_logits=True, pos_offset=37)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-9)
+    assert not np.allclose(a_cache.k, b_cache.k)
+
+
+def check_context_matters():
+    """The block attends to the injected context of every layer through that
+    layer's own cache: perturbing layer l's cached K or V changes the
+    attention output of layer l and of no earlier layer."""
+    dims = SMALL
+    w = small_weights(dims)
+    cache, _ = _prefill(dims, w, 1, 10)
+    a = O.draft_forward(dims, w, cache, np.array([3]), keep_logits=True)
+    for which in ("k", "v"):
+        for l in range(dims.n_layers):
+            c2 = O.OracleCache(cache.k.copy(), cache.v.copy(), cache.length.copy())
+            getattr(c2, which)[l, 0, :, 4, :] += 1.0
+            b = O.draft_forward(dims, w, c2, np.array([3]), keep_logits=True)
+            for m in range(l):
+                assert np.allclose(a["attn_out"][m], b["attn_out"][m], atol=1e-13)
+            assert not np.allclose(a["attn_out"][l], b["attn_out"][l])
+    # rows beyond the cached length are never read
+    c3 = O.OracleCache(cache.k.copy(), cache.v.copy(), cache.length.copy())
+    c3.k[:, 0, :, 10:, :] = 1e3
+    c3.v[:, 0, :, 10:, :] = 1e3
+    b = O.draft_forward(dims, w, c3, np.array([3]), keep_logits=True)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-13)
+
+
+def check_draft_layer_structure():
+    """One layer, recomputed by hand from the weights on a 1-row block with
+    no context: attention over a single key returns that key's value, so the
+    layer reduces to closed-form projections."""
+    dims = Dims(**{**SMALL.__dict__, "n_layers": 1, "block_size": 1})
+    w = small_weights(dims)
+    cache = O.OracleCache.empty(dims, 1, 4)
+    out = O.draft_forward(dims, w, cache, np.array([7]), keep_logits=True)
+    lw = w.layers[0]
+    eps = dims.rms_eps
+    h = w.embed[7].astype(np.float64)
+    a = h / math.sqrt(np.mean(h * h) + eps) * lw["attn_norm"]
+    v = lw["wv"] @ a                                  # [n_kv * d]
+    d = dims.head_dim
+    group = dims.n_q_heads // dims.n_kv_heads
+    o = np.concatenate([v[(hq // group) * d:(hq // group + 1) * d] for hq in range(dims.n_q_heads)])
+    assert np.allclose(out["attn_out"][0][0, 0], o, atol=1e-10)
+    h = h + lw["wo"] @ o
+    a = h / math.sqrt(np.mean(h * h) + eps) * lw["mlp_norm"]
+    gt = lw["w_gate"] @ a
+    act = gt / (1 + np.exp(-gt)) * (lw["w_up"] @ a)
+    h = h + lw["w_down"] @ act
+    z = h / math.sqrt(np.mean(h * h) + eps) * w.final_norm
+    logits = w.lm_head @ z
+    assert np.allclose(out["logits"][0, 0], logits, atol=1e-9)
+    assert out["tokens"][0, 0] == int(np.argmax(logits))
+
+
+def _identity_drafter():
+    """A 2-dimensional drafter whose step can be written out with scalar
+    trigonometry: identity projections, a zero MLP, unit gains, eps 0 and one
+    rotary pair rotated by exactly ``position`` radians (d = 2)."""
+    dims = Dims(hidden=2, n_q_heads=1, n_kv_heads=1, head_dim=2, n_layers=1,
+                intermediate=2, vocab=4, n_feat_layers=1, block_size=1,
+                rope_theta=1e4, rms_eps=0.0, dtype="f32")
+    eye = np.eye(2)
+    zero = np.zeros((2, 2))
+    embed = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [1.0, -1.0]])
+    w = I.Weights(w_fc=eye, fc_norm=np.ones(2), embed=embed, final_norm=np.ones(2),
+                  lm_head=embed, layers=[{"attn_norm": np.ones(2), "wq": eye, "wk": eye, "wv": eye,
+                                          "wo": eye, "mlp_norm": np.ones(2), "w_gate": zero,
+                                          "w_up": zero, "w_down": zero}])
+    return dims, w
+
+
+def check_draft_closed_form():
+    """Context rows e0 (position 0) and e1 (position 1), block [e1] at
+    position C: every score is a cosine of a position difference."""
+    dims, w = _identity_drafter()
+    r2 = math.sqrt(2.0)
+    for C in (1, 2):
+        cache = O.OracleCache.empty(dims, 1, 8)
+        feats = np.array([[1.0, 0.0], [0.0, 1.0]])[:C]
+        O.inject(dims, w, cache, [feats])
+        out = O.draft_forward(dims, w, cache, np.array([1]), keep_logits=True)
+        # normed rows: e0 -> (r2, 0), e1 -> (0, r2).  Rotating (0, r2) by P gives
+        # r2 (-sin P, cos P); the score between rotated e1 at P and rotated e_k at Q
+        # is 2 cos(angle between them) / r2.
+        q_ang = C + math.pi / 2                      # direction of the block query
+        ctx_ang = [0.0, 1.0 + math.pi / 2][:C]       # key directions of the context rows
+        scores = [2.0 * math.cos(q_ang - a) / r2 for a in ctx_ang] + [2.0 / r2]
+        vals = [np.array([r2, 0.0]), np.array([0.0, r2])][:C] + [np.array([0.0, r2])]
+        e = [math.exp(x) for x in scores]
+        o = sum(ei * v for ei, v in zip(e, vals)) / sum(e)
+        assert np.allclose(out["attn_out"][0][0, 0], o, atol=1e-12), (C, out["attn_out"][0][0, 0], o)
+        h = np.array([0.0, 1.0]) + o
+        z = h / math.sqrt(float(np.mean(h * h)))
+        assert np.allclose(out["logits"][0, 0], w.embed @ z, atol=1e-12)
+
+
+def check_planted_recovery():
+    """Verify on planted target states recovers the planted accept length
+    and fallback token exactly (the self-logit margin is large)."""
+    dims = Dims(**{**SMALL.__dict__, "block_size": 16, "vocab": 1024, "hidden": 256})
+    w = I.make_weights(dims, 21)
+    for trial in range(6):
+        draft = np.random.default_rng(trial).integers(0, dims.vocab - 1, size=(3, 16))
+        L = I.planted_accept(21, trial, 3, 0.12, 16)
+        t, hid = I.planted_targets(dims, 21, trial, w.lm_head, draft, L)
+        g, gaps = O.verify(dims, w.lm_head, hid)
+        assert np.array_equal(g, t)
+        acc, bonus = O.accept(draft, g)
+        assert np.array_equal(acc, L)
+        assert np.array_equal(bonus, t[np.arange(3), L])
+
+
+def check_cost_model_simulation():
+    """S = C_AR / (C_DF / E[n]) equals the ratio of autoregressive time to
+    speculative time for the same emitted tokens in a simulated decode loop."""
+    p = I.geom_p_for_mean(7.8, 16)
+    L = np.concatenate([I.planted_accept(5, s, 64, p, 16) for s in range(200)])
+    n_commit = L + 1
+    c_ar, c_df = 1.7e-3, 2.9e-3
+    t_spec = len(n_commit) * c_df
+    t_ar = n_commit.sum() * c_ar
+    assert abs(O.speedup(c_ar, c_df, n_commit.mean()) - t_ar / t_spec) < 1e-9
+    # and the mean emitted per step is E[L] + 1 within a 5-sigma interval
+    mean = I.geometric_mean_accept(p, 16) + 1
+    se = n_commit.std() / math.sqrt(len(n_commit))
+    assert abs(n_commit.mean() - mean) < 5 * se
+
+
+ALL_CHECKS = [
+    check_linear_triple_loop, check_silu, check_rms_norm_golden, check_rms_norm_invariants,
+    check_rope_golden, check_rope_invariants, check_argmax_bruteforce,
+    check_attention_bruteforce, check_attention_closed_forms, check_accept_exhaustive,
+    check_accept_golden, check_incremental_injection, check_inject_scale_invariance,
+    check_inject_layer_major_features, check_permutation_equivariance,
+    check_position_shift_invariance, check_context_matters, check_draft_layer_structure,
+    check_draft_closed_form,
+    check_planted_recovery, check_cost_model_simulation,
+]
