@@ -1,0 +1,698 @@
+// C ABI: validation, workspace layout, launch plans and the three step calls.
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(DFLASH_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t packed_bytes(int dtype, long long rows, long long cols) {
+  const int kt = kt_of(dtype);
+  return size_t((rows + 15) / 16) * size_t((cols + kt - 1) / kt) * 1024;
+}
+
+constexpr int MAX_BATCH = 64;
+constexpr int TARGET_WGS = 1024;
+
+struct GemmPlan {
+  int M, N, K;
+  int MT, NB, m_tiles, m_blocks, n_tiles, n_blocks, k_tiles, splits, kt_per_split, n_groups;
+  size_t partial_bytes, lvl1_bytes, lvl2_bytes;
+};
+
+GemmPlan plan_gemm(int dtype, int M, int N, int K, bool argmax) {
+  GemmPlan g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  const int kt = kt_of(dtype);
+  g.m_tiles = (M + 15) / 16;
+  g.MT = g.m_tiles <= 1 ? 1 : (g.m_tiles <= 2 ? 2 : 4);
+  g.m_blocks = std::max(1, (g.m_tiles + g.MT - 1) / g.MT);
+  g.NB = argmax ? 2 : 4;
+  g.n_tiles = (N + 15) / 16;
+  g.n_blocks = (g.n_tiles + g.NB - 1) / g.NB;
+  g.k_tiles = (K + kt - 1) / kt;
+  if (argmax) {
+    g.splits = 1;
+    g.kt_per_split = g.k_tiles;
+    g.n_groups = (g.n_blocks + ARGMAX_GROUP - 1) / ARGMAX_GROUP;
+    g.lvl1_bytes = size_t(g.m_blocks) * g.n_blocks * g.MT * 16 * 8;
+    g.lvl2_bytes = size_t(g.m_blocks) * g.n_groups * g.MT * 16 * 8;
+  } else {
+    const int base = g.n_blocks * g.m_blocks;
+    const int want = (TARGET_WGS + base - 1) / base;
+    const int cap = std::max(1, g.k_tiles / 8);
+    const int s = std::max(1, std::min(want, cap));
+    g.kt_per_split = (g.k_tiles + s - 1) / s;
+    g.splits = (g.k_tiles + g.kt_per_split - 1) / g.kt_per_split;
+    g.partial_bytes = g.splits > 1 ? size_t(g.m_blocks) * g.n_blocks * g.splits * g.MT * g.NB * 1024 : 0;
+  }
+  return g;
+}
+
+int attn_splits(const dflash_dims *d, int batch) {
+  const int s = 256 / std::max(1, batch * d->n_kv_heads);
+  return std::min(16, std::max(1, s));
+}
+
+struct Bump {
+  size_t off = WS_COUNTER_BYTES;
+  size_t take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    const size_t r = off;
+    off += bytes;
+    return r;
+  }
+};
+
+// bf16 activations produced inside the step travel as hi + lo planes.
+int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
+
+struct DraftLayout {
+  size_t hidden, mid, attn, final_, xa, xo, xact, qbuf, kblk, vblk, apart, gpart, lvl1, lvl2, end;
+  size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
+  int M, Mp, S, xs;
+  GemmPlan qkv, o, gu, down, lm;
+};
+
+DraftLayout draft_layout(const dflash_dims *d, int batch) {
+  DraftLayout L{};
+  const int es = esize_of(d->dtype), kt = kt_of(d->dtype);
+  const int H = d->hidden, NQD = d->n_q_heads * d->head_dim, I = d->intermediate, hd = d->head_dim;
+  L.M = batch * d->block_size;
+  L.Mp = (L.M + 15) / 16 * 16;
+  L.S = attn_splits(d, batch);
+  L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, false);
+  L.o = plan_gemm(d->dtype, L.M, H, NQD, false);
+  L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, false);
+  L.down = plan_gemm(d->dtype, L.M, H, I, false);
+  L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, true);
+  Bump b;
+  const size_t row = size_t(L.M) * H * 4;
+  L.hidden = b.take(row * (d->n_layers + 1));
+  L.mid = b.take(row * d->n_layers);
+  L.attn = b.take(size_t(L.M) * NQD * 4 * d->n_layers);
+  L.final_ = b.take(row);
+  L.xs = act_planes(d);
+  L.pa = packed_bytes(d->dtype, L.Mp, H);
+  L.po = packed_bytes(d->dtype, L.Mp, NQD);
+  L.pact = packed_bytes(d->dtype, L.Mp, I);
+  L.pq = size_t(batch) * d->n_q_heads * (hd / kt) * 1024;
+  L.xa = b.take(L.pa * L.xs);
+  L.xo = b.take(L.po * L.xs);
+  L.xact = b.take(L.pact * L.xs);
+  L.qbuf = b.take(L.pq * L.xs);
+  L.kblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
+  L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
+  L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
+  L.gpart = b.take(std::max({L.qkv.partial_bytes, L.o.partial_bytes, L.gu.partial_bytes, L.down.partial_bytes}));
+  L.lvl1 = b.take(L.lm.lvl1_bytes);
+  L.lvl2 = b.take(L.lm.lvl2_bytes);
+  L.end = b.off;
+  return L;
+}
+
+struct VerifyLayout {
+  size_t lvl1, lvl2, end;
+  GemmPlan lm;
+};
+
+VerifyLayout verify_layout(const dflash_dims *d, int batch) {
+  VerifyLayout L{};
+  L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, true);
+  Bump b;
+  L.lvl1 = b.take(L.lm.lvl1_bytes);
+  L.lvl2 = b.take(L.lm.lvl2_bytes);
+  L.end = b.off;
+  return L;
+}
+
+struct InjectLayout {
+  size_t u, fused, xc, gpart, end, pc;
+  int Rp, xs;
+  GemmPlan fc, kv;
+};
+
+InjectLayout inject_layout(const dflash_dims *d, int rows) {
+  InjectLayout L{};
+  const int H = d->hidden;
+  L.Rp = (rows + 15) / 16 * 16;
+  L.fc = plan_gemm(d->dtype, rows, H, d->n_feat_layers * H, false);
+  L.kv = plan_gemm(d->dtype, rows, d->n_layers * 2 * d->n_kv_heads * d->head_dim, H, false);
+  Bump b;
+  L.u = b.take(size_t(rows) * H * 4);
+  L.fused = b.take(size_t(rows) * H * 4);
+  L.xs = act_planes(d);
+  L.pc = packed_bytes(d->dtype, L.Rp, H);
+  L.xc = b.take(L.pc * L.xs);
+  L.gpart = b.take(std::max(L.fc.partial_bytes, L.kv.partial_bytes));
+  L.end = b.off;
+  return L;
+}
+
+int check_dims(const dflash_dims *d) {
+  if (!d) return fail(DFLASH_ERR_NULL, "dims is NULL");
+  if (d->dtype != DFLASH_BF16 && d->dtype != DFLASH_F32) return fail(DFLASH_ERR_DTYPE, "dtype must be DFLASH_BF16 or DFLASH_F32");
+  if (d->hidden <= 0 || d->hidden % 64 || d->hidden > 8192) return fail(DFLASH_ERR_SHAPE, "hidden must be a positive multiple of 64, at most 8192");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(DFLASH_ERR_SHAPE, "head_dim must be 64 or 128");
+  if (d->n_kv_heads <= 0 || d->n_q_heads <= 0 || d->n_q_heads % d->n_kv_heads) return fail(DFLASH_ERR_SHAPE, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (d->n_q_heads / d->n_kv_heads > 16) return fail(DFLASH_ERR_SHAPE, "at most 16 query heads per KV head");
+  if (d->n_layers < 1 || d->n_layers > MAX_SEGMENTS) return fail(DFLASH_ERR_SHAPE, "n_layers must be in [1, 16]");
+  if (d->intermediate <= 0 || d->intermediate % 32) return fail(DFLASH_ERR_SHAPE, "intermediate must be a positive multiple of 32");
+  if (d->n_feat_layers < 1) return fail(DFLASH_ERR_SHAPE, "n_feat_layers must be >= 1");
+  if (d->vocab < 32 || d->vocab % 32) return fail(DFLASH_ERR_SHAPE, "vocab must be a positive multiple of 32");
+  if (d->mask_id < 0 || d->mask_id >= d->vocab) return fail(DFLASH_ERR_SHAPE, "mask_id must be in [0, vocab)");
+  if (d->block_size < 1 || d->block_size > 16) return fail(DFLASH_ERR_SHAPE, "block_size must be in [1, 16]");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta >= 0.f)) return fail(DFLASH_ERR_SHAPE, "rms_eps and rope_theta must be >= 0");
+  return DFLASH_OK;
+}
+
+int check_kv(const dflash_dims *d, const dflash_kv *kv) {
+  if (!kv) return fail(DFLASH_ERR_NULL, "kv is NULL");
+  if (!kv->k || !kv->v || !kv->ctx_len || !kv->status) return fail(DFLASH_ERR_NULL, "kv->k, v, ctx_len and status must be set");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(DFLASH_ERR_ALIGN, "kv->k and kv->v must be 16-byte aligned");
+  if (kv->capacity <= 0 || kv->capacity % 32) return fail(DFLASH_ERR_SHAPE, "kv->capacity must be a positive multiple of 32");
+  if (kv->max_batch < 1 || kv->max_batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "kv->max_batch must be in [1, 64]");
+  (void)d;
+  return DFLASH_OK;
+}
+
+int check_ptr(const void *p, const char *name, bool align = true) {
+  if (!p) return fail(DFLASH_ERR_NULL, std::string(name) + " is NULL");
+  if (align && !aligned16(p)) return fail(DFLASH_ERR_ALIGN, std::string(name) + " must be 16-byte aligned");
+  return DFLASH_OK;
+}
+
+#define TRY(x)                 \
+  do {                         \
+    const int _r = (x);        \
+    if (_r != DFLASH_OK) return _r; \
+  } while (0)
+
+int check_weights(const dflash_dims *d, const dflash_weights *w, bool need_fc, bool need_draft) {
+  if (!w) return fail(DFLASH_ERR_NULL, "weights is NULL");
+  if (!w->layers) return fail(DFLASH_ERR_NULL, "weights->layers is NULL");
+  if (need_fc) {
+    TRY(check_ptr(w->w_fc, "w_fc"));
+    TRY(check_ptr(w->fc_norm, "fc_norm"));
+  }
+  if (need_draft) {
+    TRY(check_ptr(w->embed, "embed"));
+    TRY(check_ptr(w->final_norm, "final_norm"));
+    TRY(check_ptr(w->lm_head, "lm_head"));
+  }
+  for (int l = 0; l < d->n_layers; ++l) {
+    const dflash_layer &L = w->layers[l];
+    TRY(check_ptr(L.w_qkv, "layers[].w_qkv"));
+    if (need_draft) {
+      TRY(check_ptr(L.attn_norm, "layers[].attn_norm"));
+      TRY(check_ptr(L.w_o, "layers[].w_o"));
+      TRY(check_ptr(L.mlp_norm, "layers[].mlp_norm"));
+      TRY(check_ptr(L.w_gate_up, "layers[].w_gate_up"));
+      TRY(check_ptr(L.w_down, "layers[].w_down"));
+    }
+  }
+  return DFLASH_OK;
+}
+
+void fill_gemm(GemmParams &p, const GemmPlan &g) {
+  p.M = g.M;
+  p.N = g.N;
+  p.m_tiles = g.m_tiles;
+  p.m_blocks = g.m_blocks;
+  p.MT = g.MT;
+  p.n_tiles = g.n_tiles;
+  p.n_blocks = g.n_blocks;
+  p.NB = g.NB;
+  p.k_tiles = g.k_tiles;
+  p.splits = g.splits;
+  p.kt_per_split = g.kt_per_split;
+  p.n_groups = g.n_groups;
+  p.seg_ntiles = g.n_tiles;
+  p.xs = 1;
+  p.out_planes = 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+const char *dflash_last_error(void) { return g_err.c_str(); }
+
+const char *dflash_status_str(int s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_NULL: return "null pointer";
+    case DFLASH_ERR_SHAPE: return "bad shape";
+    case DFLASH_ERR_DTYPE: return "bad dtype";
+    case DFLASH_ERR_WORKSPACE: return "workspace too small";
+    case DFLASH_ERR_ALIGN: return "misaligned pointer";
+    case DFLASH_ERR_HIP: return "HIP error";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+size_t dflash_packed_bytes(int32_t dtype, int32_t rows, int32_t cols) {
+  if ((dtype != DFLASH_BF16 && dtype != DFLASH_F32) || rows <= 0 || cols <= 0) return 0;
+  return packed_bytes(dtype, rows, cols);
+}
+
+int dflash_pack_matrix(int32_t dtype, const void *src, int32_t rows, int32_t cols, void *dst, hipStream_t stream) {
+  if (dtype != DFLASH_BF16 && dtype != DFLASH_F32) return fail(DFLASH_ERR_DTYPE, "bad dtype");
+  if (rows <= 0 || cols <= 0) return fail(DFLASH_ERR_SHAPE, "rows and cols must be positive");
+  TRY(check_ptr(src, "src"));
+  TRY(check_ptr(dst, "dst"));
+  if ((size_t(cols) * esize_of(dtype)) % 16) return fail(DFLASH_ERR_ALIGN, "row pitch must be a multiple of 16 bytes");
+  const hipError_t e = launch_pack_matrix(dtype, src, rows, cols, dst, 0, 1, 1, 0, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_matrix");
+}
+
+int dflash_pack_qkv(const dflash_dims *d, const void *wq, const void *wk, const void *wv, void *dst, hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_ptr(wq, "wq"));
+  TRY(check_ptr(wk, "wk"));
+  TRY(check_ptr(wv, "wv"));
+  TRY(check_ptr(dst, "dst"));
+  const int hd = d->head_dim, H = d->hidden;
+  const int qr = d->n_q_heads * hd, kr = d->n_kv_heads * hd;
+  hipError_t e = launch_pack_matrix(d->dtype, wq, qr, H, dst, 0, 1, hd, qr, stream);
+  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wk, kr, H, dst, qr / 16, 1, hd, kr, stream);
+  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wv, kr, H, dst, (qr + kr) / 16, 1, hd, 0, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_qkv");
+}
+
+int dflash_pack_gate_up(const dflash_dims *d, const void *wg, const void *wu, void *dst, hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_ptr(wg, "w_gate"));
+  TRY(check_ptr(wu, "w_up"));
+  TRY(check_ptr(dst, "dst"));
+  const int I = d->intermediate, H = d->hidden;
+  hipError_t e = launch_pack_matrix(d->dtype, wg, I, H, dst, 0, 2, 1, 0, stream);
+  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wu, I, H, dst, 1, 2, 1, 0, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_gate_up");
+}
+
+size_t dflash_kv_bytes(const dflash_dims *d, int32_t capacity, int32_t max_batch) {
+  if (check_dims(d) != DFLASH_OK || capacity <= 0 || max_batch <= 0) return 0;
+  return size_t(d->n_layers) * max_batch * d->n_kv_heads * size_t(capacity) * d->head_dim * esize_of(d->dtype);
+}
+
+static int kv_convert(const dflash_dims *d, const dflash_kv *kv, void *kp, void *vp, bool to_packed, hipStream_t s) {
+  TRY(check_dims(d));
+  TRY(check_kv(d, kv));
+  TRY(check_ptr(kp, "k_plain"));
+  TRY(check_ptr(vp, "v_plain"));
+  const long long regions = (long long)d->n_layers * kv->max_batch * d->n_kv_heads;
+  const hipError_t e = launch_kv_convert(d->dtype, to_packed, kv->k, kv->v, kp, vp, regions, kv->capacity, d->head_dim, s);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "kv convert");
+}
+
+int dflash_kv_import(const dflash_dims *d, const dflash_kv *kv, const void *k, const void *v, hipStream_t s) {
+  return kv_convert(d, kv, const_cast<void *>(k), const_cast<void *>(v), true, s);
+}
+
+int dflash_kv_export(const dflash_dims *d, const dflash_kv *kv, void *k, void *v, hipStream_t s) {
+  return kv_convert(d, kv, k, v, false, s);
+}
+
+size_t dflash_workspace_bytes(const dflash_dims *d, int32_t max_batch, int32_t max_rows) {
+  if (check_dims(d) != DFLASH_OK || max_batch < 1 || max_batch > MAX_BATCH || max_rows < 0) return 0;
+  size_t need = draft_layout(d, max_batch).end;
+  need = std::max(need, verify_layout(d, max_batch).end);
+  need = std::max(need, inject_layout(d, std::max(1, max_rows)).end);
+  return (need + 255) & ~size_t(255);
+}
+
+int dflash_workspace_init(void *ws, size_t bytes, hipStream_t stream) {
+  TRY(check_ptr(ws, "ws"));
+  if (bytes < WS_COUNTER_BYTES) return fail(DFLASH_ERR_WORKSPACE, "workspace smaller than its counter area");
+  const hipError_t e = launch_zero(ws, bytes & ~size_t(15), stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "workspace_init");
+}
+
+int dflash_workspace_view(const dflash_dims *d, int32_t what, int32_t count, int32_t layer, size_t *offset, size_t *bytes) {
+  TRY(check_dims(d));
+  if (!offset || !bytes) return fail(DFLASH_ERR_NULL, "offset and bytes must be set");
+  if (count < 1) return fail(DFLASH_ERR_SHAPE, "count must be >= 1");
+  const int H = d->hidden, NQD = d->n_q_heads * d->head_dim;
+  if (what == DFLASH_VIEW_FUSED) {
+    const InjectLayout L = inject_layout(d, count);
+    *offset = L.fused;
+    *bytes = size_t(count) * H * 4;
+    return DFLASH_OK;
+  }
+  if (count > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch too large");
+  const DraftLayout L = draft_layout(d, count);
+  const size_t row = size_t(L.M) * H * 4;
+  switch (what) {
+    case DFLASH_VIEW_HIDDEN:
+      if (layer < -1 || layer >= d->n_layers) return fail(DFLASH_ERR_SHAPE, "layer out of range");
+      *offset = L.hidden + row * (layer + 1);
+      *bytes = row;
+      return DFLASH_OK;
+    case DFLASH_VIEW_MID:
+      if (layer < 0 || layer >= d->n_layers) return fail(DFLASH_ERR_SHAPE, "layer out of range");
+      *offset = L.mid + row * layer;
+      *bytes = row;
+      return DFLASH_OK;
+    case DFLASH_VIEW_ATTN:
+      if (layer < 0 || layer >= d->n_layers) return fail(DFLASH_ERR_SHAPE, "layer out of range");
+      *offset = L.attn + size_t(L.M) * NQD * 4 * layer;
+      *bytes = size_t(L.M) * NQD * 4;
+      return DFLASH_OK;
+    case DFLASH_VIEW_FINAL:
+      *offset = L.final_;
+      *bytes = row;
+      return DFLASH_OK;
+    default:
+      return fail(DFLASH_ERR_SHAPE, "unknown view");
+  }
+}
+
+int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const void *feats,
+                     const int32_t *cu_new, int32_t batch, int32_t rows, void *ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_weights(d, w, true, false));
+  TRY(check_kv(d, kv));
+  TRY(check_ptr(cu_new, "cu_new", false));
+  TRY(check_ptr(ws, "ws"));
+  if (batch < 1 || batch > kv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  if (rows < 0) return fail(DFLASH_ERR_SHAPE, "rows must be >= 0");
+  if (rows == 0) return DFLASH_OK;
+  TRY(check_ptr(feats, "feats"));
+  const InjectLayout L = inject_layout(d, rows);
+  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this many rows");
+  if (L.fc.m_blocks * L.fc.n_blocks > 131072 || L.kv.m_blocks * L.kv.n_blocks > 131072)
+    return fail(DFLASH_ERR_UNSUPPORTED, "too many rows in one injection");
+  char *wsb = static_cast<char *>(ws);
+  const int H = d->hidden, kt = kt_of(d->dtype);
+  int *counters = reinterpret_cast<int *>(wsb);
+
+  GemmParams fc{};
+  fill_gemm(fc, L.fc);
+  fc.w_seg[0] = static_cast<const char *>(w->w_fc);
+  fc.x = static_cast<const char *>(feats);
+  fc.x_ld = d->n_feat_layers * H;
+  fc.partial = reinterpret_cast<float *>(wsb + L.gpart);
+  fc.counters = counters;
+  fc.out_f32 = reinterpret_cast<float *>(wsb + L.u);
+  fc.ld_out = H;
+  hipError_t e = launch_gemm(d->dtype, EPI_STORE, fc, stream);
+  if (e != hipSuccess) return hip_fail(e, "inject fc");
+
+  NormParams np{};
+  np.src = reinterpret_cast<const float *>(wsb + L.u);
+  np.gain = static_cast<const char *>(w->fc_norm);
+  np.eps = d->rms_eps;
+  np.M = rows;
+  np.rows_pad = L.Rp;
+  np.H = H;
+  np.xpacked = wsb + L.xc;
+  np.x_kt = H / kt;
+  np.planes = L.xs;
+  np.x_plane = L.pc;
+  np.normed = reinterpret_cast<float *>(wsb + L.fused);
+  e = launch_norm_pack(d->dtype, np, stream);
+  if (e != hipSuccess) return hip_fail(e, "inject norm");
+
+  GemmParams g{};
+  fill_gemm(g, L.kv);
+  const int hd = d->head_dim;
+  const size_t layer_bytes = packed_bytes(d->dtype, (long long)(d->n_q_heads + 2 * d->n_kv_heads) * hd, H);
+  (void)layer_bytes;
+  for (int l = 0; l < d->n_layers; ++l)
+    g.w_seg[l] = static_cast<const char *>(w->layers[l].w_qkv) + size_t(d->n_q_heads * hd / 16) * (H / kt) * 1024;
+  g.seg_ntiles = 2 * d->n_kv_heads * hd / 16;
+  g.x = wsb + L.xc;
+  g.x_ld = 0;
+  g.xs = L.xs;
+  g.x_plane = L.pc;
+  g.partial = reinterpret_cast<float *>(wsb + L.gpart);
+  g.counters = counters;
+  g.n_q = d->n_q_heads;
+  g.n_kv = d->n_kv_heads;
+  g.head_dim = hd;
+  g.rope_theta = d->rope_theta;
+  g.ctx_len = kv->ctx_len;
+  g.kcache = static_cast<char *>(kv->k);
+  g.vcache = static_cast<char *>(kv->v);
+  g.layer0 = 0;
+  g.capacity = kv->capacity;
+  g.max_batch = kv->max_batch;
+  g.cu_new = cu_new;
+  g.batch = batch;
+  g.status = kv->status;
+  e = launch_gemm(d->dtype, EPI_KVINJ, g, stream);
+  if (e != hipSuccess) return hip_fail(e, "inject kv");
+  return DFLASH_OK;
+}
+
+int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
+                         int32_t batch, int32_t *draft, void *ws, size_t ws_bytes, hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_weights(d, w, false, true));
+  TRY(check_kv(d, kv));
+  TRY(check_ptr(last_tok, "last_tok", false));
+  TRY(check_ptr(draft, "draft", false));
+  TRY(check_ptr(ws, "ws"));
+  if (batch < 1 || batch > kv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  const DraftLayout L = draft_layout(d, batch);
+  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
+  if (L.lm.m_blocks * L.lm.n_blocks > 131072) return fail(DFLASH_ERR_UNSUPPORTED, "vocabulary too large");
+  char *wsb = static_cast<char *>(ws);
+  int *counters = reinterpret_cast<int *>(wsb);
+  const int H = d->hidden, kt = kt_of(d->dtype), hd = d->head_dim, NL = d->n_layers;
+  const int NQD = d->n_q_heads * hd, I = d->intermediate;
+  const size_t row = size_t(L.M) * H * 4;
+  float *hidden = reinterpret_cast<float *>(wsb + L.hidden);
+  float *mid = reinterpret_cast<float *>(wsb + L.mid);
+  const size_t region_layer = size_t(kv->max_batch) * d->n_kv_heads * size_t(kv->capacity) * hd * esize_of(d->dtype);
+  hipError_t e;
+
+  NormParams np{};
+  np.embed = static_cast<const char *>(w->embed);
+  np.last_tok = last_tok;
+  np.block = d->block_size;
+  np.mask_id = d->mask_id;
+  np.vocab = d->vocab;
+  np.status = kv->status;
+  np.gathered = hidden;
+  np.gain = static_cast<const char *>(w->layers[0].attn_norm);
+  np.eps = d->rms_eps;
+  np.M = L.M;
+  np.rows_pad = L.Mp;
+  np.H = H;
+  np.xpacked = wsb + L.xa;
+  np.x_kt = H / kt;
+  np.planes = L.xs;
+  np.x_plane = L.pa;
+  e = launch_norm_pack(d->dtype, np, stream);
+  if (e != hipSuccess) return hip_fail(e, "draft embed");
+
+  for (int l = 0; l < NL; ++l) {
+    const dflash_layer &lw = w->layers[l];
+    float *h_in = reinterpret_cast<float *>(reinterpret_cast<char *>(hidden) + row * l);
+    float *h_mid = reinterpret_cast<float *>(reinterpret_cast<char *>(mid) + row * l);
+    float *h_out = reinterpret_cast<float *>(reinterpret_cast<char *>(hidden) + row * (l + 1));
+
+    GemmParams q{};
+    fill_gemm(q, L.qkv);
+    q.w_seg[0] = static_cast<const char *>(lw.w_qkv);
+    q.x = wsb + L.xa;
+    q.xs = L.xs;
+    q.x_plane = L.pa;
+    q.q_plane = L.pq;
+    q.partial = reinterpret_cast<float *>(wsb + L.gpart);
+    q.counters = counters;
+    q.block = d->block_size;
+    q.n_q = d->n_q_heads;
+    q.n_kv = d->n_kv_heads;
+    q.head_dim = hd;
+    q.rope_theta = d->rope_theta;
+    q.ctx_len = kv->ctx_len;
+    q.qbuf = wsb + L.qbuf;
+    q.kblk = wsb + L.kblk;
+    q.vblk = wsb + L.vblk;
+    e = launch_gemm(d->dtype, EPI_QKV, q, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft qkv");
+
+    AttnParams a{};
+    a.qbuf = wsb + L.qbuf;
+    a.q_plane = L.pq;
+    a.xs = L.xs;
+    a.xo_plane = L.po;
+    a.kblk = wsb + L.kblk;
+    a.vblk = wsb + L.vblk;
+    a.kcache = static_cast<const char *>(kv->k) + region_layer * l;
+    a.vcache = static_cast<const char *>(kv->v) + region_layer * l;
+    a.ctx_len = kv->ctx_len;
+    a.part = reinterpret_cast<float *>(wsb + L.apart);
+    a.block = d->block_size;
+    a.n_q = d->n_q_heads;
+    a.n_kv = d->n_kv_heads;
+    a.head_dim = hd;
+    a.group = d->n_q_heads / d->n_kv_heads;
+    a.splits = L.S;
+    a.capacity = kv->capacity;
+    a.scale_log2 = 1.4426950408889634f / sqrtf(float(hd));
+    a.attn_out = reinterpret_cast<float *>(wsb + L.attn + size_t(L.M) * NQD * 4 * l);
+    a.xo = wsb + L.xo;
+    a.xo_kt = NQD / kt;
+    e = launch_attention(d->dtype, a, batch, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft attention");
+    e = launch_attn_merge(d->dtype, a, batch, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft attention merge");
+
+    GemmParams o{};
+    fill_gemm(o, L.o);
+    o.w_seg[0] = static_cast<const char *>(lw.w_o);
+    o.x = wsb + L.xo;
+    o.xs = L.xs;
+    o.x_plane = L.po;
+    o.partial = reinterpret_cast<float *>(wsb + L.gpart);
+    o.counters = counters;
+    o.out_f32 = h_mid;
+    o.resid = h_in;
+    o.ld_out = H;
+    e = launch_gemm(d->dtype, EPI_RESID, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft o_proj");
+
+    NormParams n2{};
+    n2.src = h_mid;
+    n2.gain = static_cast<const char *>(lw.mlp_norm);
+    n2.eps = d->rms_eps;
+    n2.M = L.M;
+    n2.rows_pad = L.Mp;
+    n2.H = H;
+    n2.xpacked = wsb + L.xa;
+    n2.x_kt = H / kt;
+    n2.planes = L.xs;
+    n2.x_plane = L.pa;
+    e = launch_norm_pack(d->dtype, n2, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft mlp norm");
+
+    GemmParams gu{};
+    fill_gemm(gu, L.gu);
+    gu.w_seg[0] = static_cast<const char *>(lw.w_gate_up);
+    gu.x = wsb + L.xa;
+    gu.xs = L.xs;
+    gu.x_plane = L.pa;
+    gu.out_planes = L.xs;
+    gu.out_plane = L.pact;
+    gu.partial = reinterpret_cast<float *>(wsb + L.gpart);
+    gu.counters = counters;
+    gu.out_packed = wsb + L.xact;
+    gu.out_kt = I / kt;
+    e = launch_gemm(d->dtype, EPI_SWIGLU, gu, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft gate_up");
+
+    GemmParams dn{};
+    fill_gemm(dn, L.down);
+    dn.w_seg[0] = static_cast<const char *>(lw.w_down);
+    dn.x = wsb + L.xact;
+    dn.xs = L.xs;
+    dn.x_plane = L.pact;
+    dn.partial = reinterpret_cast<float *>(wsb + L.gpart);
+    dn.counters = counters;
+    dn.out_f32 = h_out;
+    dn.resid = h_mid;
+    dn.ld_out = H;
+    e = launch_gemm(d->dtype, EPI_RESID, dn, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft down");
+
+    NormParams n3{};
+    n3.src = h_out;
+    n3.gain = static_cast<const char *>(l + 1 < NL ? w->layers[l + 1].attn_norm : w->final_norm);
+    n3.eps = d->rms_eps;
+    n3.M = L.M;
+    n3.rows_pad = L.Mp;
+    n3.H = H;
+    n3.xpacked = wsb + L.xa;
+    n3.x_kt = H / kt;
+    n3.planes = L.xs;
+    n3.x_plane = L.pa;
+    n3.normed = l + 1 < NL ? nullptr : reinterpret_cast<float *>(wsb + L.final_);
+    e = launch_norm_pack(d->dtype, n3, stream);
+    if (e != hipSuccess) return hip_fail(e, "draft norm");
+  }
+
+  GemmParams lm{};
+  fill_gemm(lm, L.lm);
+  lm.w_seg[0] = static_cast<const char *>(w->lm_head);
+  lm.x = wsb + L.xa;
+  lm.xs = L.xs;
+  lm.x_plane = L.pa;
+  lm.counters = counters;
+  lm.vocab = d->vocab;
+  lm.lvl1 = reinterpret_cast<unsigned long long *>(wsb + L.lvl1);
+  lm.lvl2 = reinterpret_cast<unsigned long long *>(wsb + L.lvl2);
+  lm.tok_out = draft;
+  lm.verify = 0;
+  lm.block = d->block_size;
+  lm.batch = batch;
+  e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
+  if (e != hipSuccess) return hip_fail(e, "draft lm_head");
+  return DFLASH_OK;
+}
+
+int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,
+                         int32_t batch, int32_t *target_argmax, int32_t *accept_len, int32_t *bonus, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_ptr(lm_head, "lm_head"));
+  TRY(check_ptr(target_hidden, "target_hidden"));
+  TRY(check_ptr(draft, "draft", false));
+  TRY(check_ptr(target_argmax, "target_argmax", false));
+  TRY(check_ptr(accept_len, "accept_len", false));
+  TRY(check_ptr(bonus, "bonus", false));
+  TRY(check_ptr(ws, "ws"));
+  if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
+  const VerifyLayout L = verify_layout(d, batch);
+  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
+  if (L.lm.m_blocks * L.lm.n_blocks > 131072) return fail(DFLASH_ERR_UNSUPPORTED, "vocabulary too large");
+  char *wsb = static_cast<char *>(ws);
+  GemmParams lm{};
+  fill_gemm(lm, L.lm);
+  lm.w_seg[0] = static_cast<const char *>(lm_head);
+  lm.x = static_cast<const char *>(target_hidden);
+  lm.x_ld = d->hidden;
+  lm.counters = reinterpret_cast<int *>(wsb);
+  lm.vocab = d->vocab;
+  lm.lvl1 = reinterpret_cast<unsigned long long *>(wsb + L.lvl1);
+  lm.lvl2 = reinterpret_cast<unsigned long long *>(wsb + L.lvl2);
+  lm.tok_out = target_argmax;
+  lm.draft_in = draft;
+  lm.accept_len = accept_len;
+  lm.bonus = bonus;
+  lm.verify = 1;
+  lm.block = d->block_size;
+  lm.batch = batch;
+  const hipError_t e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
+  if (e != hipSuccess) return hip_fail(e, "verify lm_head");
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Kernel parameter blocks and host-side launchers shared by the kernel
+// translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash {
+
+// Counter slots in the first bytes of every workspace (zeroed once; every
+// user returns its slots to zero).
+constexpr size_t WS_COUNTER_BYTES = size_t(1) << 20;
+constexpr int CNT_TILE = 0;          // split-K tiles            [0, 131072)
+constexpr int CNT_GROUP = 131072;    // argmax groups            [.., +65536)
+constexpr int CNT_MBLK = 196608;     // argmax / inject m-blocks [.., +32768)
+constexpr int CNT_FINAL = 229376;    // one-per-launch completion
+constexpr int MAX_SEGMENTS = 16;
+constexpr int ARGMAX_GROUP = 64;     // n-blocks reduced by one group leader
+
+enum Epilogue : int {
+  EPI_STORE = 0,   // out_f32[m, n] = y
+  EPI_RESID = 1,   // out_f32[m, n] = resid[m, n] + y
+  EPI_SWIGLU = 2,  // packed act[m, j] = silu(gate) * up (tiles alternate gate / up)
+  EPI_QKV = 3,     // RoPE on q and k of the block; q -> qbuf, k/v -> kblk/vblk
+  EPI_KVINJ = 4,   // RoPE on injected k; k/v appended to the cache
+  EPI_ARGMAX = 5,  // lowest-index argmax over the vocabulary (+ acceptance)
+};
+
+struct GemmParams {
+  // A operand: packed weights, one pointer per segment of seg_ntiles 16-row tiles.
+  const char *w_seg[MAX_SEGMENTS];
+  int seg_ntiles;
+  // B operand: activations, packed (x_ld == 0) or row-major with x_ld elements per row.
+  // Packed activations may carry xs = 2 planes (hi, lo) x_plane bytes apart.
+  const char *x;
+  int x_ld;
+  int xs;
+  size_t x_plane;
+  int M, m_tiles, m_blocks, MT;
+  int N, n_tiles, n_blocks, NB;
+  int k_tiles, splits, kt_per_split;
+  float *partial;
+  int *counters;
+  // EPI_STORE / EPI_RESID
+  float *out_f32;
+  const float *resid;
+  int ld_out;
+  // EPI_SWIGLU (output planes out_planes, out_plane bytes apart)
+  char *out_packed;
+  int out_kt, out_planes;
+  size_t out_plane;
+  // EPI_QKV / EPI_KVINJ
+  int block, n_q, n_kv, head_dim;
+  float rope_theta;
+  const int *ctx_len;
+  char *qbuf, *kblk, *vblk;
+  size_t q_plane;
+  char *kcache, *vcache;
+  int layer0, capacity, max_batch;
+  const int *cu_new;
+  int batch;
+  unsigned *status;
+  // EPI_ARGMAX
+  int vocab, n_groups, verify;
+  unsigned long long *lvl1, *lvl2;
+  int *tok_out;
+  const int *draft_in;
+  int *accept_len, *bonus;
+};
+
+struct AttnParams {
+  const char *qbuf, *kblk, *vblk;   // per-step block operands
+  size_t q_plane;                   // bytes between the q hi and lo planes
+  int xs;                           // 2: q and P carried as hi + lo bf16 planes
+  const char *kcache, *vcache;      // this layer's cache (sequence-major regions)
+  const int *ctx_len;
+  float *part;                      // [batch][n_q][splits] partial records
+  int block, n_q, n_kv, head_dim, group, splits, capacity;
+  float scale_log2;                 // log2(e) / sqrt(head_dim)
+  // merge
+  float *attn_out;                  // fp32 [batch*block, n_q*d]
+  char *xo;                         // packed T [.., n_q*d] for the output projection
+  int xo_kt;
+  size_t xo_plane;
+};
+
+struct NormParams {
+  const float *src;        // fp32 rows [M, H], or nullptr with embed set
+  const char *embed;       // T [V, H] gathered by token
+  const int *last_tok;     // [batch]
+  int block, mask_id, vocab;
+  unsigned *status;
+  float *gathered;         // fp32 copy of the gathered rows (embed mode)
+  const char *gain;        // T [H]
+  float eps;
+  int M, rows_pad, H;
+  char *xpacked;           // packed T output [rows_pad, H]
+  int x_kt, planes;        // planes: 1, or 2 (hi, lo) x_plane bytes apart
+  size_t x_plane;
+  float *normed;           // optional fp32 copy of the normed rows
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s);
+hipError_t launch_attention(int dtype, const AttnParams &p, int batch, hipStream_t s);
+hipError_t launch_attn_merge(int dtype, const AttnParams &p, int batch, hipStream_t s);
+hipError_t launch_norm_pack(int dtype, const NormParams &p, hipStream_t s);
+hipError_t launch_pack_matrix(int dtype, const void *src, int rows, int cols, void *dst,
+                              int dst_tile_offset, int dst_tile_stride, int rot_head_dim,
+                              int rot_rows, hipStream_t s);
+hipError_t launch_kv_convert(int dtype, bool to_packed, void *packed_k, void *packed_v,
+                             void *plain_k, void *plain_v, long long regions, int capacity,
+                             int head_dim, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace dflash

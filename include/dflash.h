@@ -1,0 +1,254 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) library for one DFlash
+ * block-diffusion draft-and-verify step.
+ *
+ * The step has three parts, one entry point each:
+ *
+ *   dflash_inject_kv      target features of newly accepted positions, taken
+ *                         from several target layers, are fused (fc + RMSNorm)
+ *                         and projected into the K/V of every draft layer, then
+ *                         appended to the draft KV cache.
+ *                         ("DFlash, Diffusion LLMs, dLLM, MTP and Speculative
+ *                         Decoding: A Deep Research Report", section "Key
+ *                         points": KV injection into every draft layer.)
+ *   dflash_draft_forward  one drafting pass over a block of B slots (the last
+ *                         accepted token, then B-1 mask tokens), attention
+ *                         bidirectional inside the block and over the whole
+ *                         injected context, shared lm_head, argmax per slot.
+ *                         (Same page, "Key points" and "Why DFlash beats
+ *                         EAGLE-3" item 3; "Term: DFlash speculative
+ *                         decoding", section "DFlash: architecture and
+ *                         workflow", stage two.)
+ *   dflash_verify_accept  target lm_head argmax at the B+1 block rows, the
+ *                         longest prefix on which the draft matches, and the
+ *                         target's token at the first mismatch.
+ *                         ("Term: DFlash speculative decoding", "DFlash:
+ *                         architecture and workflow", stages three and four.)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless marked [host].  The caller owns all
+ *   memory (weights, cache, inputs, outputs, workspace); the library never
+ *   allocates or frees.
+ * - Every call enqueues work on the given HIP stream and returns without
+ *   synchronising.  Host-side validation runs first and is all-or-nothing:
+ *   on a negative return nothing was enqueued.  dflash_last_error() gives a
+ *   thread-local message for the last failure.
+ * - Element type: dims->dtype selects the storage type of weights, features,
+ *   target hidden states and the KV cache: DFLASH_BF16 (bfloat16) or
+ *   DFLASH_F32.  Accumulation is always fp32; the residual stream is fp32.
+ * - Matrices are given to the pack calls in PyTorch Linear layout
+ *   [out_features, in_features], row-major.  The step calls take PACKED
+ *   matrices (see "Packed layout").
+ * - Device-side faults (a KV capacity overflow, a token id outside
+ *   [0, vocab)) set sticky bits in kv->status and never fault the GPU.
+ * - A workspace must be zero-filled once (dflash_workspace_init) before its
+ *   first use.  Calls that share one workspace must run in stream order on
+ *   one stream; two calls overlapping on one workspace race.
+ *
+ * Packed layout ("fragment tiles")
+ * --------------------------------
+ * A packed matrix of R rows and K columns is a sequence of 1 KiB tiles of 16
+ * rows x KT columns (KT = 32 for bf16, 16 for fp32), ordered row-tile major
+ * then column tile.  Inside a tile, the 16 bytes at offset 16*l hold row
+ * (l % 16) and columns (l / 16) * E .. (l / 16) * E + E - 1 with E = KT / 4.
+ * This is the register image of one 64-lane MFMA operand, so a wavefront
+ * reads a tile with one fully coalesced 1 KiB load.  Rows and columns beyond
+ * R and K are zero.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_ABI_VERSION 1
+
+typedef enum { DFLASH_BF16 = 0, DFLASH_F32 = 1 } dflash_dtype;
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_NULL = -1,        /* a required pointer is NULL */
+  DFLASH_ERR_SHAPE = -2,       /* a size or dimension is out of range */
+  DFLASH_ERR_DTYPE = -3,       /* unknown dtype */
+  DFLASH_ERR_WORKSPACE = -4,   /* workspace too small */
+  DFLASH_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+  DFLASH_ERR_HIP = -6,         /* a HIP call or kernel launch failed */
+  DFLASH_ERR_UNSUPPORTED = -7  /* a valid but unsupported configuration */
+} dflash_status;
+
+/* Sticky bits OR-ed into *kv->status by device code. */
+#define DFLASH_STATUS_CAPACITY 1u  /* an injection would exceed kv->capacity */
+#define DFLASH_STATUS_TOKEN 2u     /* a token id outside [0, vocab) was clamped */
+
+/* Drafter dimensions [host].  Limits checked by every call:
+ * hidden, intermediate, n_feat_layers*hidden and n_q_heads*head_dim are
+ * multiples of 32; head_dim is 64 or 128; n_q_heads % n_kv_heads == 0 with
+ * n_q_heads / n_kv_heads <= 16; 1 <= block_size <= 16; 1 <= n_layers <= 16;
+ * vocab is a multiple of 32; 0 <= mask_id < vocab; rope_theta == 0 turns
+ * rotary embedding off. */
+typedef struct {
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_layers;
+  int32_t intermediate;
+  int32_t vocab;
+  int32_t n_feat_layers;
+  int32_t block_size;
+  int32_t mask_id;
+  float rope_theta;
+  float rms_eps;
+  int32_t dtype;
+} dflash_dims;
+
+/* One draft layer.  Norm gains are plain vectors [hidden] of the storage
+ * type; matrices are packed by the dflash_pack_* calls. */
+typedef struct {
+  const void *attn_norm;  /* [H] */
+  const void *w_qkv;      /* dflash_pack_qkv output */
+  const void *w_o;        /* dflash_pack_matrix of W_o [H, n_q*d] */
+  const void *mlp_norm;   /* [H] */
+  const void *w_gate_up;  /* dflash_pack_gate_up output */
+  const void *w_down;     /* dflash_pack_matrix of W_down [H, I] */
+} dflash_layer;
+
+typedef struct {
+  const void *w_fc;        /* dflash_pack_matrix of W_fc [H, n_f*H] */
+  const void *fc_norm;     /* [H] */
+  const void *embed;       /* plain row-major [V, H] (rows are gathered) */
+  const void *final_norm;  /* [H] */
+  const void *lm_head;     /* dflash_pack_matrix of W_lm [V, H] */
+  const dflash_layer *layers;  /* [host] array of n_layers */
+} dflash_weights;
+
+/* Draft KV cache.  k and v each hold n_layers * max_batch * n_kv_heads
+ * regions of `capacity` positions (dflash_kv_bytes each), in the packed
+ * cache layout that dflash_kv_import / dflash_kv_export convert from / to the
+ * plain layout [n_layers][max_batch][n_kv_heads][capacity][head_dim].
+ * ctx_len[s] is the number of valid positions of sequence s. */
+typedef struct {
+  void *k;
+  void *v;
+  int32_t *ctx_len;   /* [max_batch] */
+  uint32_t *status;   /* one word of sticky DFLASH_STATUS_* bits */
+  int32_t capacity;   /* [host] positions per sequence, a multiple of 32 */
+  int32_t max_batch;  /* [host] */
+} dflash_kv;
+
+/* ---------------------------------------------------------------- packing */
+
+/* Bytes of a packed R x K matrix of the given dtype (rows rounded up to 16,
+ * columns to KT). */
+size_t dflash_packed_bytes(int32_t dtype, int32_t rows, int32_t cols);
+
+/* Pack a row-major [rows, cols] matrix.  dst must hold
+ * dflash_packed_bytes(dtype, rows, cols); src and dst 16-byte aligned. */
+int dflash_pack_matrix(int32_t dtype, const void *src, int32_t rows, int32_t cols,
+                       void *dst, hipStream_t stream);
+
+/* Pack the q, k and v projections of one layer (W_q [n_q*d, H],
+ * W_k / W_v [n_kv*d, H]) into one matrix of (n_q + 2 n_kv) * d rows.  Rows of
+ * q and k heads are reordered so that each rotary pair (channels i and
+ * i + d/2) shares a 16-row tile; v keeps its order.  dst holds
+ * dflash_packed_bytes(dtype, (n_q + 2 n_kv) * d, H). */
+int dflash_pack_qkv(const dflash_dims *dims, const void *wq, const void *wk, const void *wv,
+                    void *dst, hipStream_t stream);
+
+/* Pack W_gate and W_up ([I, H] each) into one matrix of 2I rows whose 16-row
+ * tiles alternate gate, up, gate, up...  dst holds
+ * dflash_packed_bytes(dtype, 2 * I, H). */
+int dflash_pack_gate_up(const dflash_dims *dims, const void *w_gate, const void *w_up,
+                        void *dst, hipStream_t stream);
+
+/* --------------------------------------------------------------- KV cache */
+
+/* Bytes of each of kv->k and kv->v. */
+size_t dflash_kv_bytes(const dflash_dims *dims, int32_t capacity, int32_t max_batch);
+
+/* Copy a whole cache between the plain layout
+ * [n_layers][max_batch][n_kv][capacity][head_dim] (storage dtype) and the
+ * packed layout.  ctx_len is neither read nor written. */
+int dflash_kv_import(const dflash_dims *dims, const dflash_kv *kv, const void *k_plain,
+                     const void *v_plain, hipStream_t stream);
+int dflash_kv_export(const dflash_dims *dims, const dflash_kv *kv, void *k_plain,
+                     void *v_plain, hipStream_t stream);
+
+/* -------------------------------------------------------------- workspace */
+
+/* Workspace bytes for calls with at most max_batch sequences and at most
+ * max_rows injected rows per dflash_inject_kv call. */
+size_t dflash_workspace_bytes(const dflash_dims *dims, int32_t max_batch, int32_t max_rows);
+
+/* Zero-fill a workspace (once, after allocation). */
+int dflash_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Where the last call of a given kind left an intermediate, for checks:
+ *   DFLASH_VIEW_FUSED     fp32 [rows, H]: fused, normed injected context c
+ *   DFLASH_VIEW_HIDDEN    fp32 [batch*B, H]: residual after layer `layer`
+ *                         (layer = -1: the block embeddings)
+ *   DFLASH_VIEW_MID       fp32 [batch*B, H]: residual after the attention
+ *                         half of layer `layer`
+ *   DFLASH_VIEW_ATTN      fp32 [batch*B, n_q*d]: attention output of layer
+ *                         `layer`, before the output projection
+ *   DFLASH_VIEW_FINAL     fp32 [batch*B, H]: final normed hidden
+ * `count` is rows for FUSED and batch otherwise.  Offsets are from ws. */
+enum {
+  DFLASH_VIEW_FUSED = 0,
+  DFLASH_VIEW_HIDDEN = 1,
+  DFLASH_VIEW_MID = 2,
+  DFLASH_VIEW_ATTN = 3,
+  DFLASH_VIEW_FINAL = 4
+};
+int dflash_workspace_view(const dflash_dims *dims, int32_t what, int32_t count, int32_t layer,
+                          size_t *offset, size_t *bytes);
+
+/* ------------------------------------------------------------- the step */
+
+/* KV injection.  feats: [rows, n_feat_layers * H] row-major, storage dtype,
+ * feature layer k in columns [k H, (k+1) H).  cu_new: [batch + 1] prefix sums
+ * of rows per sequence (cu_new[0] = 0, cu_new[batch] = rows).  Row i of
+ * sequence s is written at cache position ctx_len[s] + i with rotary
+ * position ctx_len[s] + i; then ctx_len[s] += n_s.  A sequence whose new
+ * length would exceed kv->capacity is skipped whole and sets
+ * DFLASH_STATUS_CAPACITY.  rows [host] must equal cu_new[batch]. */
+int dflash_inject_kv(const dflash_dims *dims, const dflash_weights *w, const dflash_kv *kv,
+                     const void *feats, const int32_t *cu_new, int32_t batch, int32_t rows,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Drafting pass.  last_tok: [batch].  Block slot j of sequence s holds
+ * last_tok[s] (j = 0) or dims->mask_id (j > 0) at rotary position
+ * ctx_len[s] + j and attends to every cached position < ctx_len[s] and to
+ * every block slot (ctx_len values above kv->capacity are read as
+ * kv->capacity).  draft: [batch, B] out, the lowest-index argmax of the
+ * shared lm_head logits per slot.  The cache is read, never written. */
+int dflash_draft_forward(const dflash_dims *dims, const dflash_weights *w, const dflash_kv *kv,
+                         const int32_t *last_tok, int32_t batch, int32_t *draft,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Greedy verification.  target_hidden: [batch, B+1, H] row-major, storage
+ * dtype: the target's final hidden states at its pass over
+ * [x, d_0, ..., d_{B-1}].  lm_head: packed [V, H].  Outputs:
+ * target_argmax [batch, B+1] (lowest index on ties), accept_len [batch] =
+ * first j < B with draft[s][j] != target_argmax[s][j], else B, and
+ * bonus [batch] = target_argmax[s][accept_len[s]]. */
+int dflash_verify_accept(const dflash_dims *dims, const void *lm_head, const void *target_hidden,
+                         const int32_t *draft, int32_t batch, int32_t *target_argmax,
+                         int32_t *accept_len, int32_t *bonus, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------- misc */
+const char *dflash_status_str(int status);
+const char *dflash_last_error(void);
+int dflash_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */
