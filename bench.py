@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of one DFlash draft-and-verify step on one MI355X.
+
+A step is the whole hot path for one batch: KV injection of the newly
+accepted rows, the drafting pass over a B = 16 block and greedy verification
+with acceptance.  The default workload is the Qwen3-8B-shaped drafter at
+batch 1 with a 2048-position injected context.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  Inputs are seeded and synthetic; weights are random
+with the drafter's shapes.  Every step first rewinds ctx_len to the
+configured context, so each timed step runs at the same shape.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_model(d, batch, ctx, rows):
+    """Algorithmic HBM bytes and flops of one step.  Weights are counted once
+    per step, except the lm_head, which the draft head and the verify head
+    each stream (a target pass lies between them).  The K/V projection
+    weights of injection are the drafter's own and are counted once."""
+    es = 2 if d.dtype == "bf16" else 4
+    H, I, V, hd = d.hidden, d.intermediate, d.vocab, d.head_dim
+    nqd = d.n_q_heads * hd
+    per_layer = (d.qkv_rows * H + H * nqd + 2 * I * H + H * I)
+    w_bytes = (H * d.feat_dim + d.n_layers * per_layer + 2 * V * H) * es
+    ctx_after = np.asarray(ctx) + np.asarray(rows)
+    kv_read = int(np.sum(ctx_after)) * d.n_layers * 2 * d.n_kv_heads * hd * es
+    kv_write = int(np.sum(rows)) * d.n_layers * 2 * d.n_kv_heads * hd * es
+    io = int(np.sum(rows)) * d.feat_dim * es + batch * (d.block_size + 1) * H * es
+    B = d.block_size
+    M = batch * B
+    R = int(np.sum(rows))
+    flops = 2 * (R * H * d.feat_dim + R * H * d.n_layers * 2 * d.n_kv_heads * hd)
+    flops += 2 * M * d.n_layers * per_layer + 2 * M * V * H + 2 * batch * (B + 1) * V * H
+    flops += sum(4 * d.n_q_heads * B * (int(c) + B) * hd * d.n_layers for c in ctx_after)
+    return {"bytes": w_bytes + kv_read + kv_write + io, "weight_bytes": w_bytes,
+            "kv_bytes": kv_read + kv_write, "flops": flops}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3-8b-b1")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the draft-and-verify step of a batch runs on one "
+              "device, and this build has no multi-GPU path (sequences shard across GPUs with "
+              "no exchange; see the design notes).  Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from block_diffusion_speculative_amd import configs as C
+    from block_diffusion_speculative_amd import inputs as I
+    from block_diffusion_speculative_amd.engine import Drafter, upload
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    w = C.get(args.workload)
+    d = w.dims
+    B = d.block_size
+    b = w.batch
+    seed = args.seed
+    t0 = time.time()
+    weights = I.make_weights(d, seed)
+    log(f"[bench] weights generated in {time.time() - t0:.1f}s")
+    ctx = I.context_lengths(w, seed)
+    if w.new_rows is not None:
+        rows = I.new_row_counts(w, seed, 0)
+    else:
+        rows = np.full(b, int(round(w.mean_accept)) + 1, dtype=np.int32)
+    cap = C.kv_capacity(int(ctx.max()))
+    p_acc = I.workload_geom_p(w)
+
+    # Context K/V generated directly (seeded bf16 values), one step of injection on top.
+    shape = (d.n_layers, b, d.n_kv_heads, cap, d.head_dim)
+    k_plain = np.zeros(shape, dtype=np.float32)
+    v_plain = np.zeros(shape, dtype=np.float32)
+    for l in range(d.n_layers):
+        for s in range(b):
+            ks, vs = I.kv_entries(d, seed, l, s, int(ctx[s]))
+            k_plain[l, s, :, :ctx[s]] = ks
+            v_plain[l, s, :, :ctx[s]] = vs
+    feats = [I.features(d, seed, 0, s, int(rows[s])) for s in range(b)]
+    last = I.last_tokens(d, seed, 0, b)
+    L_plant = I.planted_accept(seed, 0, b, p_acc, B)
+
+    cpu = None
+    oracle_tokens = None
+    if not args.no_cpu_baseline:
+        import oracle.dflash_oracle as O
+        cache = O.OracleCache(k_plain.astype(np.float64), v_plain.astype(np.float64),
+                              ctx.astype(np.int64).copy())
+        log("[bench] oracle step on the host ...")
+        tc = time.perf_counter()
+        O.inject(d, weights, cache, feats)
+        dr = O.draft_forward(d, weights, cache, last)
+        oracle_tokens = dr["tokens"]
+        t_plant, hid = I.planted_targets(d, seed, 0, weights.lm_head, oracle_tokens, L_plant)
+        g, _ = O.verify(d, weights.lm_head, hid)
+        O.accept(oracle_tokens, g)
+        osec = time.perf_counter() - tc
+        del cache
+        cpu = {"value": b / osec, "unit": "block-steps/s",
+               "cores": int(max(blas_threads(), 1)),
+               "affinity_cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "seconds_per_step": osec,
+               "sample": f"one full step of the same workload ({args.workload}: inject {int(np.sum(rows))} rows, "
+                         f"draft, verify, accept), fp64 numpy, timed once"}
+        log(f"[bench] oracle step {osec:.1f}s")
+    else:
+        oracle_tokens = I.stream(seed, 99, 0).integers(0, d.vocab - 1, size=(b, B))
+        t_plant, hid = I.planted_targets(d, seed, 0, weights.lm_head, oracle_tokens, L_plant)
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    dr_gpu = Drafter(d, weights, b, cap, int(max(17 * b, np.sum(rows))), device=dev)
+    dr_gpu.kv_import(upload(k_plain.reshape(-1, d.head_dim), dr_gpu.dt, dev).reshape(shape),
+                     upload(v_plain.reshape(-1, d.head_dim), dr_gpu.dt, dev).reshape(shape))
+    del k_plain, v_plain
+    log(f"[bench] device setup in {time.time() - t0:.1f}s")
+    ctx0 = torch.as_tensor(ctx).to(dev)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)).to(dev)
+    R = int(np.sum(rows))
+    feats_t = upload(np.concatenate(feats, axis=0), dr_gpu.dt, dev)
+    last_t = torch.as_tensor(last).to(dev)
+    th = upload(hid.reshape(b * (B + 1), d.hidden), dr_gpu.dt, dev).reshape(b, B + 1, d.hidden)
+    draft_out = torch.empty((b, B), dtype=torch.int32, device=dev)
+    tgt = torch.empty((b, B + 1), dtype=torch.int32, device=dev)
+    acc = torch.empty(b, dtype=torch.int32, device=dev)
+    bonus = torch.empty(b, dtype=torch.int32, device=dev)
+    n_ev = args.steps
+    ev_v0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_v1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i=None):
+        dr_gpu.ctx_len[:b].copy_(ctx0)
+        dr_gpu.inject(feats_t, cu, b, R)
+        dr_gpu.draft(last_t, draft_out, b)
+        if i is not None:
+            ev_v0[i].record()
+        dr_gpu.verify(th, draft_out, tgt, acc, bonus, b)
+        if i is not None:
+            ev_v1[i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    verify_ms = float(np.mean([a.elapsed_time(z) for a, z in zip(ev_v0, ev_v1)]))
+    status = dr_gpu.read_status()
+
+    got_draft = draft_out.cpu().numpy()
+    got_acc = acc.cpu().numpy()
+    match = None
+    if not args.no_cpu_baseline:
+        match = int(np.sum(got_draft == oracle_tokens))
+
+    model = step_model(d, b, ctx, rows)
+    es = 2 if d.dtype == "bf16" else 4
+    lm_bytes = d.vocab * d.hidden * es + b * (B + 1) * d.hidden * es + b * (B + 3) * 4
+    achieved = lm_bytes / (verify_ms * 1e-3) / 1e9
+    step_gbs = model["bytes"] / (ms_step * 1e-3) / 1e9
+    t_hbm = model["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = model["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    t_roof = max(t_hbm, t_mfma)
+    value = b * 1000.0 / ms_step
+    out = {
+        "metric": "draft+verify block-steps/s (B=16)",
+        "value": round(value, 2),
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": d.dtype,
+        "data": "synthetic (seeded random weights of the drafter's shapes; seeded context K/V, features and planted targets)",
+        "config": {"workload": args.workload, "batch": b, "ctx": [int(c) for c in ctx] if b <= 4 else
+                   {"min": int(ctx.min()), "max": int(ctx.max()), "mean": float(ctx.mean())},
+                   "block": B, "injected_rows": int(R), "hidden": d.hidden, "layers": d.n_layers,
+                   "vocab": d.vocab},
+        "drafted_tokens_per_s": round(value * B, 1),
+        "step_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                          "algorithmic_bytes": model["bytes"], "flops": model["flops"],
+                          "t_roofline_ms": round(t_roof * 1e3, 4),
+                          "frac": round(t_roof * 1e3 / ms_step, 4),
+                          "achieved_GBs": round(step_gbs, 1)},
+        "roofline": {"kernel": "gemm_kernel<bf16,MT=2,NB=2,ARGMAX> (verify lm_head + argmax + accept)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": lm_bytes, "avg_launch_ms": round(verify_ms, 5)},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+        "accept": {"mean_len": float(np.mean(got_acc)), "planted_mean": float(np.mean(L_plant))},
+        "draft_matches_oracle": match,
+        "status": status,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -30,15 +30,15 @@ size_t packed_bytes(int dtype, long long rows, long long cols) {
 }
 
 constexpr int MAX_BATCH = 64;
-constexpr int TARGET_WGS = 1024;
 
 struct GemmPlan {
   int M, N, K;
-  int MT, NB, m_tiles, m_blocks, n_tiles, n_blocks, k_tiles, splits, kt_per_split, n_groups;
-  size_t partial_bytes, lvl1_bytes, lvl2_bytes;
+  int MT, NB, m_tiles, m_blocks, n_tiles, n_blocks, k_tiles;
 };
 
-GemmPlan plan_gemm(int dtype, int M, int N, int K, bool argmax) {
+// nb: weight tiles per workgroup (2 for the gate/up pairs and the argmax,
+// 1 otherwise); the workgroup's wavefronts split K.
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int nb) {
   GemmPlan g{};
   g.M = M;
   g.N = N;
@@ -47,25 +47,10 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, bool argmax) {
   g.m_tiles = (M + 15) / 16;
   g.MT = g.m_tiles <= 1 ? 1 : (g.m_tiles <= 2 ? 2 : 4);
   g.m_blocks = std::max(1, (g.m_tiles + g.MT - 1) / g.MT);
-  g.NB = argmax ? 2 : 4;
+  g.NB = nb;
   g.n_tiles = (N + 15) / 16;
   g.n_blocks = (g.n_tiles + g.NB - 1) / g.NB;
   g.k_tiles = (K + kt - 1) / kt;
-  if (argmax) {
-    g.splits = 1;
-    g.kt_per_split = g.k_tiles;
-    g.n_groups = (g.n_blocks + ARGMAX_GROUP - 1) / ARGMAX_GROUP;
-    g.lvl1_bytes = size_t(g.m_blocks) * g.n_blocks * g.MT * 16 * 8;
-    g.lvl2_bytes = size_t(g.m_blocks) * g.n_groups * g.MT * 16 * 8;
-  } else {
-    const int base = g.n_blocks * g.m_blocks;
-    const int want = (TARGET_WGS + base - 1) / base;
-    const int cap = std::max(1, g.k_tiles / 8);
-    const int s = std::max(1, std::min(want, cap));
-    g.kt_per_split = (g.k_tiles + s - 1) / s;
-    g.splits = (g.k_tiles + g.kt_per_split - 1) / g.kt_per_split;
-    g.partial_bytes = g.splits > 1 ? size_t(g.m_blocks) * g.n_blocks * g.splits * g.MT * g.NB * 1024 : 0;
-  }
   return g;
 }
 
@@ -88,7 +73,7 @@ struct Bump {
 int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
 
 struct DraftLayout {
-  size_t hidden, mid, attn, final_, xa, xo, xact, qbuf, kblk, vblk, apart, gpart, lvl1, lvl2, end;
+  size_t hidden, mid, attn, final_, xa, xo, xact, qbuf, kblk, vblk, apart, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
   int M, Mp, S, xs;
   GemmPlan qkv, o, gu, down, lm;
@@ -101,11 +86,11 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.M = batch * d->block_size;
   L.Mp = (L.M + 15) / 16 * 16;
   L.S = attn_splits(d, batch);
-  L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, false);
-  L.o = plan_gemm(d->dtype, L.M, H, NQD, false);
-  L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, false);
-  L.down = plan_gemm(d->dtype, L.M, H, I, false);
-  L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, true);
+  L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1);
+  L.o = plan_gemm(d->dtype, L.M, H, NQD, 1);
+  L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2);
+  L.down = plan_gemm(d->dtype, L.M, H, I, 1);
+  L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, 2);
   Bump b;
   const size_t row = size_t(L.M) * H * 4;
   L.hidden = b.take(row * (d->n_layers + 1));
@@ -124,30 +109,24 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.kblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
-  L.gpart = b.take(std::max({L.qkv.partial_bytes, L.o.partial_bytes, L.gu.partial_bytes, L.down.partial_bytes}));
-  L.lvl1 = b.take(L.lm.lvl1_bytes);
-  L.lvl2 = b.take(L.lm.lvl2_bytes);
   L.end = b.off;
   return L;
 }
 
 struct VerifyLayout {
-  size_t lvl1, lvl2, end;
+  size_t end;
   GemmPlan lm;
 };
 
 VerifyLayout verify_layout(const dflash_dims *d, int batch) {
   VerifyLayout L{};
-  L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, true);
-  Bump b;
-  L.lvl1 = b.take(L.lm.lvl1_bytes);
-  L.lvl2 = b.take(L.lm.lvl2_bytes);
-  L.end = b.off;
+  L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, 2);
+  L.end = WS_COUNTER_BYTES;
   return L;
 }
 
 struct InjectLayout {
-  size_t u, fused, xc, gpart, end, pc;
+  size_t u, fused, xc, end, pc;
   int Rp, xs;
   GemmPlan fc, kv;
 };
@@ -156,15 +135,14 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   InjectLayout L{};
   const int H = d->hidden;
   L.Rp = (rows + 15) / 16 * 16;
-  L.fc = plan_gemm(d->dtype, rows, H, d->n_feat_layers * H, false);
-  L.kv = plan_gemm(d->dtype, rows, d->n_layers * 2 * d->n_kv_heads * d->head_dim, H, false);
+  L.fc = plan_gemm(d->dtype, rows, H, d->n_feat_layers * H, 1);
+  L.kv = plan_gemm(d->dtype, rows, d->n_layers * 2 * d->n_kv_heads * d->head_dim, H, 1);
   Bump b;
   L.u = b.take(size_t(rows) * H * 4);
   L.fused = b.take(size_t(rows) * H * 4);
   L.xs = act_planes(d);
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
-  L.gpart = b.take(std::max(L.fc.partial_bytes, L.kv.partial_bytes));
   L.end = b.off;
   return L;
 }
@@ -244,9 +222,6 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.n_blocks = g.n_blocks;
   p.NB = g.NB;
   p.k_tiles = g.k_tiles;
-  p.splits = g.splits;
-  p.kt_per_split = g.kt_per_split;
-  p.n_groups = g.n_groups;
   p.seg_ntiles = g.n_tiles;
   p.xs = 1;
   p.out_planes = 1;
@@ -405,19 +380,14 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   TRY(check_ptr(feats, "feats"));
   const InjectLayout L = inject_layout(d, rows);
   if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this many rows");
-  if (L.fc.m_blocks * L.fc.n_blocks > 131072 || L.kv.m_blocks * L.kv.n_blocks > 131072)
-    return fail(DFLASH_ERR_UNSUPPORTED, "too many rows in one injection");
   char *wsb = static_cast<char *>(ws);
   const int H = d->hidden, kt = kt_of(d->dtype);
-  int *counters = reinterpret_cast<int *>(wsb);
 
   GemmParams fc{};
   fill_gemm(fc, L.fc);
   fc.w_seg[0] = static_cast<const char *>(w->w_fc);
   fc.x = static_cast<const char *>(feats);
   fc.x_ld = d->n_feat_layers * H;
-  fc.partial = reinterpret_cast<float *>(wsb + L.gpart);
-  fc.counters = counters;
   fc.out_f32 = reinterpret_cast<float *>(wsb + L.u);
   fc.ld_out = H;
   hipError_t e = launch_gemm(d->dtype, EPI_STORE, fc, stream);
@@ -450,8 +420,6 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   g.x_ld = 0;
   g.xs = L.xs;
   g.x_plane = L.pc;
-  g.partial = reinterpret_cast<float *>(wsb + L.gpart);
-  g.counters = counters;
   g.n_q = d->n_q_heads;
   g.n_kv = d->n_kv_heads;
   g.head_dim = hd;
@@ -467,6 +435,8 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   g.status = kv->status;
   e = launch_gemm(d->dtype, EPI_KVINJ, g, stream);
   if (e != hipSuccess) return hip_fail(e, "inject kv");
+  e = launch_commit_rows(kv->ctx_len, cu_new, batch, kv->capacity, stream);
+  if (e != hipSuccess) return hip_fail(e, "inject commit");
   return DFLASH_OK;
 }
 
@@ -481,9 +451,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   if (batch < 1 || batch > kv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
   const DraftLayout L = draft_layout(d, batch);
   if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
-  if (L.lm.m_blocks * L.lm.n_blocks > 131072) return fail(DFLASH_ERR_UNSUPPORTED, "vocabulary too large");
   char *wsb = static_cast<char *>(ws);
-  int *counters = reinterpret_cast<int *>(wsb);
   const int H = d->hidden, kt = kt_of(d->dtype), hd = d->head_dim, NL = d->n_layers;
   const int NQD = d->n_q_heads * hd, I = d->intermediate;
   const size_t row = size_t(L.M) * H * 4;
@@ -525,8 +493,6 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     q.xs = L.xs;
     q.x_plane = L.pa;
     q.q_plane = L.pq;
-    q.partial = reinterpret_cast<float *>(wsb + L.gpart);
-    q.counters = counters;
     q.block = d->block_size;
     q.n_q = d->n_q_heads;
     q.n_kv = d->n_kv_heads;
@@ -572,8 +538,6 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     o.x = wsb + L.xo;
     o.xs = L.xs;
     o.x_plane = L.po;
-    o.partial = reinterpret_cast<float *>(wsb + L.gpart);
-    o.counters = counters;
     o.out_f32 = h_mid;
     o.resid = h_in;
     o.ld_out = H;
@@ -602,8 +566,6 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     gu.x_plane = L.pa;
     gu.out_planes = L.xs;
     gu.out_plane = L.pact;
-    gu.partial = reinterpret_cast<float *>(wsb + L.gpart);
-    gu.counters = counters;
     gu.out_packed = wsb + L.xact;
     gu.out_kt = I / kt;
     e = launch_gemm(d->dtype, EPI_SWIGLU, gu, stream);
@@ -615,8 +577,6 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     dn.x = wsb + L.xact;
     dn.xs = L.xs;
     dn.x_plane = L.pact;
-    dn.partial = reinterpret_cast<float *>(wsb + L.gpart);
-    dn.counters = counters;
     dn.out_f32 = h_out;
     dn.resid = h_mid;
     dn.ld_out = H;
@@ -645,16 +605,18 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   lm.x = wsb + L.xa;
   lm.xs = L.xs;
   lm.x_plane = L.pa;
-  lm.counters = counters;
   lm.vocab = d->vocab;
-  lm.lvl1 = reinterpret_cast<unsigned long long *>(wsb + L.lvl1);
-  lm.lvl2 = reinterpret_cast<unsigned long long *>(wsb + L.lvl2);
-  lm.tok_out = draft;
-  lm.verify = 0;
-  lm.block = d->block_size;
-  lm.batch = batch;
+  lm.keys = reinterpret_cast<unsigned long long *>(wsb);
   e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
   if (e != hipSuccess) return hip_fail(e, "draft lm_head");
+  ArgmaxFinishParams fp{};
+  fp.keys = lm.keys;
+  fp.rows_per_seq = d->block_size;
+  fp.block = d->block_size;
+  fp.verify = 0;
+  fp.tok_out = draft;
+  e = launch_argmax_finish(fp, batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "draft argmax");
   return DFLASH_OK;
 }
 
@@ -672,26 +634,27 @@ int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *
   if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
   const VerifyLayout L = verify_layout(d, batch);
   if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
-  if (L.lm.m_blocks * L.lm.n_blocks > 131072) return fail(DFLASH_ERR_UNSUPPORTED, "vocabulary too large");
   char *wsb = static_cast<char *>(ws);
   GemmParams lm{};
   fill_gemm(lm, L.lm);
   lm.w_seg[0] = static_cast<const char *>(lm_head);
   lm.x = static_cast<const char *>(target_hidden);
   lm.x_ld = d->hidden;
-  lm.counters = reinterpret_cast<int *>(wsb);
   lm.vocab = d->vocab;
-  lm.lvl1 = reinterpret_cast<unsigned long long *>(wsb + L.lvl1);
-  lm.lvl2 = reinterpret_cast<unsigned long long *>(wsb + L.lvl2);
-  lm.tok_out = target_argmax;
-  lm.draft_in = draft;
-  lm.accept_len = accept_len;
-  lm.bonus = bonus;
-  lm.verify = 1;
-  lm.block = d->block_size;
-  lm.batch = batch;
-  const hipError_t e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
+  lm.keys = reinterpret_cast<unsigned long long *>(wsb);
+  hipError_t e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
   if (e != hipSuccess) return hip_fail(e, "verify lm_head");
+  ArgmaxFinishParams fp{};
+  fp.keys = lm.keys;
+  fp.rows_per_seq = d->block_size + 1;
+  fp.block = d->block_size;
+  fp.verify = 1;
+  fp.tok_out = target_argmax;
+  fp.draft_in = draft;
+  fp.accept_len = accept_len;
+  fp.bonus = bonus;
+  e = launch_argmax_finish(fp, batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "verify accept");
   return DFLASH_OK;
 }
 

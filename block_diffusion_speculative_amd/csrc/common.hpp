@@ -161,26 +161,7 @@ __host__ __device__ inline int rot_channel(int r, int head_dim) {
   return p < 8 ? 8 * t + p : head_dim / 2 + 8 * t + (p - 8);
 }
 
-// ----------------------------------------------------- cross-WG handshakes
-
-// Called by every thread of a workgroup after it stored its results.  Returns
-// true in exactly one workgroup of the `expected` ones that arrive on
-// *counter: the last.  That workgroup resets the counter to zero and sees the
-// others' stores.
-__device__ inline bool arrive_last(int *counter, int expected, int *s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == expected - 1;
-    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last;
-  }
-  __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) __threadfence();
-  return last;
-}
+// ------------------------------------------------------------- dispatch
 
 // Workgroups of one launch are dispatched round-robin over the 8 XCDs; remap
 // so that consecutive logical ids share an XCD (and its L2).

@@ -1,16 +1,20 @@
-// Y = X W^T on MFMA for the skinny shapes of a draft step (M = 16 rows per
-// sequence), with split-K and fused epilogues.
+// Y = X W^T on MFMA for the skinny shapes of a draft step (16 rows per
+// sequence), with fused epilogues.
 //
 // Operands are packed fragment tiles (1 KiB = one 64-lane MFMA operand), so
 // every wavefront load is a single coalesced 1 KiB read.  The weight tile is
 // the A operand (rows = output features) and the activation tile the B
 // operand (rows = tokens); lane (c, g) of an accumulator then holds token c
-// and output features 4g..4g+3.  A workgroup owns NB 16-column weight tiles
-// and MT 16-row token tiles; its four wavefronts split the workgroup's K
-// range and add their partial sums in LDS in a fixed order.  When K is split
-// over workgroups, partial tiles go to the workspace and the last-arriving
-// workgroup of a tile adds them in split order and runs the epilogue, so the
-// result does not depend on scheduling.
+// and output features 4g..4g+3.
+//
+// A workgroup owns NB 16-column weight tiles for MT 16-row token tiles and the
+// whole K range.  Its 16 wavefronts split K, stream their weight tiles
+// with non-temporal loads, and add their partial tiles in LDS in a fixed
+// order, so the result does not depend on scheduling and no workgroup ever
+// waits on another.  The epilogue runs in the same workgroup.  The vocabulary
+// argmax is the one cross-workgroup reduction: each workgroup folds its best
+// (logit, index) key per row into one of 64 slots with a 64-bit atomic max,
+// and a small follow-up kernel reads the slots after the kernel boundary.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,21 +62,38 @@ __device__ inline int key_index(unsigned long long k) {
   return static_cast<int>(~static_cast<unsigned>(k & 0xffffffffull));
 }
 
+// Every GEMM workgroup has 16 wavefronts and splits K into the same 16
+// contiguous chunks whatever the row-tile count, so a row's result does not
+// depend on how many other rows share the launch.
+template <int MT> struct GemmShape {
+  static constexpr int WAVES = 16;
+  static constexpr int THREADS = WAVES * 64;
+};
+
+// Largest unroll (power of two, at most 8) whose in-flight fragments plus
+// accumulators fit about 25 x 16 bytes per lane (the 128-VGPR budget of a
+// 1024-thread workgroup, with room for addresses).
+constexpr int pick_unroll(int nb, int mt, int xs) {
+  int u = 8;
+  while (u > 1 && u * (nb + mt * xs) + mt * nb > 25) u >>= 1;
+  return u;
+}
+
 template <typename T, int MT, int NB, int EPI, int XS>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(GemmShape<MT>::THREADS) void gemm_kernel(const GemmParams p) {
   constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
-  constexpr int U = (MT * XS) >= 4 ? 2 : 4;
+  constexpr int WAVES = GemmShape<MT>::WAVES, NT = GemmShape<MT>::THREADS;
+  constexpr int U = pick_unroll(NB, MT, XS);  // k-tiles per batch of loads
   constexpr int NF = MT * NB;
   constexpr int R = MT * 16, CN = NB * 16;
-  __shared__ f32x4 red[4 * NF * 64];
-  __shared__ int s_flag;
+  constexpr int ROUND = (32 / NF) < WAVES ? (32 / NF) : WAVES;  // wavefronts per LDS round (<= 32 KiB)
+  static_assert(NF * 64 <= NT, "one accumulator element per thread");
+  __shared__ f32x4 red[ROUND * NF * 64];
 
-  const int total = p.m_blocks * p.n_blocks * p.splits;
+  const int total = p.m_blocks * p.n_blocks;
   const int bid = xcd_remap(blockIdx.x, total);
-  const int split = bid % p.splits;
-  const int t2 = bid / p.splits;
-  const int nblk = t2 % p.n_blocks;
-  const int mblk = t2 / p.n_blocks;
+  const int nblk = bid % p.n_blocks;
+  const int mblk = bid / p.n_blocks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
   const int nt0 = nblk * NB;
@@ -80,11 +101,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   const char *wbase = p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * p.k_tiles * 1024 + lane * 16;
   const size_t wstride = size_t(p.k_tiles) * 1024;
 
-  const int kb = split * p.kt_per_split;
-  const int ke = min(kb + p.kt_per_split, p.k_tiles);
-  const int per = (ke - kb + 3) >> 2;
-  const int k0 = kb + wave * per;
-  const int k1 = min(k0 + per, ke);
+  const int per = (p.k_tiles + WAVES - 1) / WAVES;
+  const int k0 = min(wave * per, p.k_tiles);
+  const int k1 = min(k0 + per, p.k_tiles);
   const int mt0 = mblk * MT;
 
   // B-operand chunk of token tile mt at column tile kt, activation plane xp
@@ -111,14 +130,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   for (; kt + U <= k1; kt += U) {
     uint4 wf[U][NB], xf[U][MT][XS];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) wf[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int xp = 0; xp < XS; ++xp) xf[u][mt][xp] = load_x(mt, kt + u, xp);
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -144,36 +164,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         for (int xp = 0; xp < XS; ++xp) acc[mt][nb] = mma<T>(acc[mt][nb], wf[nb], xf[mt][xp]);
   }
 
-  // Sum the four wavefronts' partial tiles in a fixed order.
+  // Sum the wavefronts' partial tiles in wavefront order, ROUND at a time.
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int e_own = threadIdx.x;  // element owned in the final tile
+  for (int r0 = 0; r0 < WAVES; r0 += ROUND) {
+    if (wave >= r0 && wave < r0 + ROUND) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) red[(wave * NF + mt * NB + nb) * 64 + lane] = acc[mt][nb];
-  __syncthreads();
-  for (int e = threadIdx.x; e < NF * 64; e += 256) {
-    f32x4 s = red[e];
-    s += red[NF * 64 + e];
-    s += red[2 * NF * 64 + e];
-    s += red[3 * NF * 64 + e];
-    red[e] = s;
-  }
-
-  if (p.splits > 1) {
-    const int tile_id = mblk * p.n_blocks + nblk;
-    f32x4 *part = reinterpret_cast<f32x4 *>(p.partial) + size_t(tile_id) * p.splits * NF * 64;
-    for (int e = threadIdx.x; e < NF * 64; e += 256) part[size_t(split) * NF * 64 + e] = red[e];
-    if (!arrive_last(p.counters + CNT_TILE + tile_id, p.splits, &s_flag)) return;
-    for (int e = threadIdx.x; e < NF * 64; e += 256) {
-      f32x4 s = part[e];
-      for (int z = 1; z < p.splits; ++z) s += part[size_t(z) * NF * 64 + e];
-      red[e] = s;
+        for (int nb = 0; nb < NB; ++nb) red[((wave - r0) * NF + mt * NB + nb) * 64 + lane] = acc[mt][nb];
     }
+    __syncthreads();
+    if (e_own < NF * 64) {
+      for (int w = 0; w < ROUND; ++w) {
+        if (r0 == 0 && w == 0) sum = red[e_own];
+        else sum += red[w * NF * 64 + e_own];
+      }
+    }
+    __syncthreads();
   }
+  if (e_own < NF * 64) red[e_own] = sum;
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogues
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-    for (int e = threadIdx.x; e < R * CN; e += 256) {
+    for (int e = threadIdx.x; e < R * CN; e += NT) {
       const int ml = e / CN, nl = e % CN;
       const int m = mblk * R + ml, n = nblk * CN + nl;
       if (m >= p.M || n >= p.N) continue;
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     constexpr int HALF = NB / 2;
-    for (int e = threadIdx.x; e < R * HALF * 16; e += 256) {
+    for (int e = threadIdx.x; e < R * HALF * 16; e += NT) {
       const int ml = e / (HALF * 16), q = e % (HALF * 16);
       const int pr = q >> 4, c = q & 15;
       const int m = mblk * R + ml;
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   } else if constexpr (EPI == EPI_QKV) {
     const int d = p.head_dim, nqd = p.n_q * d, nkd = p.n_kv * d;
     const int dt_count = d / KT;
-    for (int e = threadIdx.x; e < R * CN; e += 256) {
+    for (int e = threadIdx.x; e < R * CN; e += NT) {
       const int ml = e / CN, nl = e % CN;
       const int m = mblk * R + ml, n = nblk * CN + nl;
       if (m >= p.M) continue;
@@ -230,8 +245,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   } else if constexpr (EPI == EPI_KVINJ) {
     const int d = p.head_dim, nkd = p.n_kv * d, segn = 2 * nkd;
     const size_t region = size_t(p.capacity) * d * ES;
-    int *ctx_len = const_cast<int *>(p.ctx_len);
-    for (int e = threadIdx.x; e < R * CN; e += 256) {
+    for (int e = threadIdx.x; e < R * CN; e += NT) {
       const int ml = e / CN, nl = e % CN;
       const int m = mblk * R + ml, n = nblk * CN + nl;
       if (m >= p.M) continue;
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         if (p.cu_new[mid] <= m) lo = mid; else hi = mid;
       }
       const int s = lo, start = p.cu_new[s], ns = p.cu_new[s + 1] - start;
-      const int C = ctx_len[s];
+      const int C = p.ctx_len[s];
       if (C + ns > p.capacity) {
         if (m == start && n == 0) atomicOr(p.status, DFLASH_STATUS_CAPACITY);
         continue;
@@ -260,70 +274,74 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         store_elem<T>(base + vcache_offset<T>(pos, dd, d), v);
       }
     }
-    if (arrive_last(p.counters + CNT_FINAL, p.m_blocks * p.n_blocks, &s_flag)) {
-      for (int s = threadIdx.x; s < p.batch; s += 256) {
-        const int ns = p.cu_new[s + 1] - p.cu_new[s];
-        if (ctx_len[s] + ns <= p.capacity) ctx_len[s] += ns;
-      }
-    }
   } else if constexpr (EPI == EPI_ARGMAX) {
     if (threadIdx.x < R) {
       const int ml = threadIdx.x;
-      unsigned long long best = 0;
-      for (int nl = 0; nl < CN; ++nl) {
-        const int n = nblk * CN + nl;
-        if (n < p.vocab) {
-          const unsigned long long k = argmax_key(tile_at(red, NB, ml, nl), n);
-          best = k > best ? k : best;
-        }
-      }
-      p.lvl1[(size_t(mblk) * p.n_blocks + nblk) * R + ml] = best;
-    }
-    const int grp = nblk / ARGMAX_GROUP;
-    const int gsz = min(ARGMAX_GROUP, p.n_blocks - grp * ARGMAX_GROUP);
-    if (!arrive_last(p.counters + CNT_GROUP + mblk * p.n_groups + grp, gsz, &s_flag)) return;
-    if (threadIdx.x < R) {
-      const int ml = threadIdx.x;
-      unsigned long long best = 0;
-      for (int i = 0; i < gsz; ++i) {
-        const unsigned long long k = p.lvl1[(size_t(mblk) * p.n_blocks + grp * ARGMAX_GROUP + i) * R + ml];
-        best = k > best ? k : best;
-      }
-      p.lvl2[(size_t(mblk) * p.n_groups + grp) * R + ml] = best;
-    }
-    if (!arrive_last(p.counters + CNT_MBLK + mblk, p.n_groups, &s_flag)) return;
-    if (threadIdx.x < R) {
-      const int ml = threadIdx.x;
-      unsigned long long best = 0;
-      for (int g = 0; g < p.n_groups; ++g) {
-        const unsigned long long k = p.lvl2[(size_t(mblk) * p.n_groups + g) * R + ml];
-        best = k > best ? k : best;
-      }
       const int m = mblk * R + ml;
-      if (m < p.M) p.tok_out[m] = key_index(best);
-    }
-    if (!arrive_last(p.counters + CNT_FINAL, p.m_blocks, &s_flag)) return;
-    if (p.verify) {
-      const int B = p.block;
-      for (int s = threadIdx.x; s < p.batch; s += 256) {
-        int L = B;
-        for (int j = 0; j < B; ++j) {
-          if (p.draft_in[s * B + j] != p.tok_out[s * (B + 1) + j]) { L = j; break; }
+      if (m < p.M) {
+        unsigned long long best = 0;
+        for (int nl = 0; nl < CN; ++nl) {
+          const int n = nblk * CN + nl;
+          if (n < p.vocab) {
+            const unsigned long long k = argmax_key(tile_at(red, NB, ml, nl), n);
+            best = k > best ? k : best;
+          }
         }
-        p.accept_len[s] = L;
-        p.bonus[s] = p.tok_out[s * (B + 1) + L];
+        __hip_atomic_fetch_max(p.keys + size_t(m) * ARGMAX_SLOTS + (nblk % ARGMAX_SLOTS), best,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
 }
 
+// One workgroup per sequence: fold the argmax slots of its rows, clear them
+// for the next launch, write the token ids and, for verification, the
+// accepted length and the fallback token.
+__global__ __launch_bounds__(256) void argmax_finish_kernel(const ArgmaxFinishParams p) {
+  __shared__ int toks[32];
+  const int s = blockIdx.x;
+  const int R = p.rows_per_seq;
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const int m = s * R + r;
+    unsigned long long best = 0;
+    unsigned long long *k = p.keys + size_t(m) * ARGMAX_SLOTS;
+    for (int i = 0; i < ARGMAX_SLOTS; ++i) {
+      const unsigned long long v = k[i];
+      best = v > best ? v : best;
+      k[i] = 0;
+    }
+    const int tok = key_index(best);
+    p.tok_out[m] = tok;
+    toks[r] = tok;
+  }
+  __syncthreads();
+  if (p.verify && threadIdx.x == 0) {
+    const int B = p.block;
+    int L = B;
+    for (int j = 0; j < B; ++j) {
+      if (p.draft_in[s * B + j] != toks[j]) { L = j; break; }
+    }
+    p.accept_len[s] = L;
+    p.bonus[s] = toks[L];
+  }
+}
+
+// Commit the injected rows: ctx_len[s] += n_s unless that exceeds capacity
+// (the injection skipped such a sequence and flagged it).
+__global__ __launch_bounds__(64) void commit_rows_kernel(int *ctx_len, const int *cu_new, int batch, int capacity) {
+  for (int s = threadIdx.x; s < batch; s += blockDim.x) {
+    const int ns = cu_new[s + 1] - cu_new[s];
+    if (ctx_len[s] + ns <= capacity) ctx_len[s] += ns;
+  }
+}
+
 template <typename T, int EPI, int NB, int XS>
 static hipError_t launch_xs(const GemmParams &p, hipStream_t s) {
-  const dim3 grid(p.m_blocks * p.n_blocks * p.splits), block(256);
+  const dim3 grid(p.m_blocks * p.n_blocks);
   switch (p.MT) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, NB, EPI, XS>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, NB, EPI, XS>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<T, 4, NB, EPI, XS>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, NB, EPI, XS>), grid, dim3(GemmShape<1>::THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, NB, EPI, XS>), grid, dim3(GemmShape<2>::THREADS), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<T, 4, NB, EPI, XS>), grid, dim3(GemmShape<4>::THREADS), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -341,20 +359,29 @@ static hipError_t launch_mt(const GemmParams &p, hipStream_t s) {
 
 template <typename T>
 static hipError_t launch_t(int epi, const GemmParams &p, hipStream_t s) {
-  if (epi == EPI_ARGMAX) return p.NB == 2 ? launch_mt<T, EPI_ARGMAX, 2>(p, s) : hipErrorInvalidValue;
-  if (p.NB != 4) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_STORE: return launch_mt<T, EPI_STORE, 4>(p, s);
-    case EPI_RESID: return launch_mt<T, EPI_RESID, 4>(p, s);
-    case EPI_SWIGLU: return launch_mt<T, EPI_SWIGLU, 4>(p, s);
-    case EPI_QKV: return launch_mt<T, EPI_QKV, 4>(p, s);
-    case EPI_KVINJ: return launch_mt<T, EPI_KVINJ, 4>(p, s);
+    case EPI_STORE: return p.NB == 1 ? launch_mt<T, EPI_STORE, 1>(p, s) : hipErrorInvalidValue;
+    case EPI_RESID: return p.NB == 1 ? launch_mt<T, EPI_RESID, 1>(p, s) : hipErrorInvalidValue;
+    case EPI_QKV: return p.NB == 1 ? launch_mt<T, EPI_QKV, 1>(p, s) : hipErrorInvalidValue;
+    case EPI_KVINJ: return p.NB == 1 ? launch_mt<T, EPI_KVINJ, 1>(p, s) : hipErrorInvalidValue;
+    case EPI_SWIGLU: return p.NB == 2 ? launch_mt<T, EPI_SWIGLU, 2>(p, s) : hipErrorInvalidValue;
+    case EPI_ARGMAX: return p.NB == 2 ? launch_mt<T, EPI_ARGMAX, 2>(p, s) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s) {
   return dtype == DFLASH_BF16 ? launch_t<bf16_t>(epi, p, s) : launch_t<float>(epi, p, s);
+}
+
+hipError_t launch_argmax_finish(const ArgmaxFinishParams &p, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit_rows(int *ctx_len, const int *cu_new, int batch, int capacity, hipStream_t s) {
+  hipLaunchKernelGGL(commit_rows_kernel, dim3(1), dim3(64), 0, s, ctx_len, cu_new, batch, capacity);
+  return hipGetLastError();
 }
 
 }  // namespace dflash

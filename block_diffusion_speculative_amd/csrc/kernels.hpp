@@ -8,15 +8,13 @@
 
 namespace dflash {
 
-// Counter slots in the first bytes of every workspace (zeroed once; every
-// user returns its slots to zero).
+// The first bytes of every workspace hold the argmax key slots: zeroed once
+// at initialisation, cleared again by every reader.
+constexpr int ARGMAX_SLOTS = 64;     // atomic-max slots per row
+constexpr int MAX_KEY_ROWS = 1088;   // 64 sequences x 17 verify rows
 constexpr size_t WS_COUNTER_BYTES = size_t(1) << 20;
-constexpr int CNT_TILE = 0;          // split-K tiles            [0, 131072)
-constexpr int CNT_GROUP = 131072;    // argmax groups            [.., +65536)
-constexpr int CNT_MBLK = 196608;     // argmax / inject m-blocks [.., +32768)
-constexpr int CNT_FINAL = 229376;    // one-per-launch completion
+static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_COUNTER_BYTES, "key slots exceed the fixed area");
 constexpr int MAX_SEGMENTS = 16;
-constexpr int ARGMAX_GROUP = 64;     // n-blocks reduced by one group leader
 
 enum Epilogue : int {
   EPI_STORE = 0,   // out_f32[m, n] = y
@@ -39,9 +37,7 @@ struct GemmParams {
   size_t x_plane;
   int M, m_tiles, m_blocks, MT;
   int N, n_tiles, n_blocks, NB;
-  int k_tiles, splits, kt_per_split;
-  float *partial;
-  int *counters;
+  int k_tiles;
   // EPI_STORE / EPI_RESID
   float *out_f32;
   const float *resid;
@@ -62,8 +58,13 @@ struct GemmParams {
   int batch;
   unsigned *status;
   // EPI_ARGMAX
-  int vocab, n_groups, verify;
-  unsigned long long *lvl1, *lvl2;
+  int vocab;
+  unsigned long long *keys;   // [rows][ARGMAX_SLOTS]
+};
+
+struct ArgmaxFinishParams {
+  unsigned long long *keys;
+  int rows_per_seq, block, verify;
   int *tok_out;
   const int *draft_in;
   int *accept_len, *bonus;
@@ -103,6 +104,8 @@ struct NormParams {
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s);
+hipError_t launch_argmax_finish(const ArgmaxFinishParams &p, int batch, hipStream_t s);
+hipError_t launch_commit_rows(int *ctx_len, const int *cu_new, int batch, int capacity, hipStream_t s);
 hipError_t launch_attention(int dtype, const AttnParams &p, int batch, hipStream_t s);
 hipError_t launch_attn_merge(int dtype, const AttnParams &p, int batch, hipStream_t s);
 hipError_t launch_norm_pack(int dtype, const NormParams &p, hipStream_t s);
