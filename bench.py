@@ -76,6 +76,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="qwen3-8b-b1")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (reference dispatch for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: the draft-and-verify step of a batch runs on one "
@@ -178,6 +180,15 @@ def main(argv=None):
         if i is not None:
             ev_v1[i].record()
 
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src_c = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty(n, dtype=torch.uint8, device=dev)
+        src_c.fill_(1)
+        torch.cuda.synchronize()
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -2,6 +2,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "common.hpp"
@@ -84,13 +85,14 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   const int es = esize_of(d->dtype), kt = kt_of(d->dtype);
   const int H = d->hidden, NQD = d->n_q_heads * d->head_dim, I = d->intermediate, hd = d->head_dim;
   L.M = batch * d->block_size;
-  L.Mp = (L.M + 15) / 16 * 16;
   L.S = attn_splits(d, batch);
   L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1);
   L.o = plan_gemm(d->dtype, L.M, H, NQD, 1);
   L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2);
   L.down = plan_gemm(d->dtype, L.M, H, I, 1);
   L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, 2);
+  // packed activations hold whole row blocks (the GEMMs load them unguarded)
+  L.Mp = L.qkv.m_blocks * L.qkv.MT * 16;
   Bump b;
   const size_t row = size_t(L.M) * H * 4;
   L.hidden = b.take(row * (d->n_layers + 1));
@@ -134,9 +136,10 @@ struct InjectLayout {
 InjectLayout inject_layout(const dflash_dims *d, int rows) {
   InjectLayout L{};
   const int H = d->hidden;
-  L.Rp = (rows + 15) / 16 * 16;
+
   L.fc = plan_gemm(d->dtype, rows, H, d->n_feat_layers * H, 1);
   L.kv = plan_gemm(d->dtype, rows, d->n_layers * 2 * d->n_kv_heads * d->head_dim, H, 1);
+  L.Rp = L.kv.m_blocks * L.kv.MT * 16;
   Bump b;
   L.u = b.take(size_t(rows) * H * 4);
   L.fused = b.take(size_t(rows) * H * 4);
@@ -212,7 +215,30 @@ int check_weights(const dflash_dims *d, const dflash_weights *w, bool need_fc, b
   return DFLASH_OK;
 }
 
+// Compute units of the current device (cached per device): the persistent
+// GEMM launches at most one workgroup per compute unit.
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Rotary frequencies in turns per position, in fp64: theta^(-2i/d) / (2 pi).
+void fill_rope(GemmParams &p, const dflash_dims *d) {
+  p.rope_on = d->rope_theta != 0.f;
+  const int half = d->head_dim / 2;
+  for (int i = 0; i < half && i < 64; ++i)
+    p.rope_turns[i] = std::pow(double(d->rope_theta), -2.0 * i / d->head_dim) / (2.0 * M_PI);
+}
+
 void fill_gemm(GemmParams &p, const GemmPlan &g) {
+  p.grid_cap = compute_units();
   p.M = g.M;
   p.N = g.N;
   p.m_tiles = g.m_tiles;
@@ -423,7 +449,7 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   g.n_q = d->n_q_heads;
   g.n_kv = d->n_kv_heads;
   g.head_dim = hd;
-  g.rope_theta = d->rope_theta;
+  fill_rope(g, d);
   g.ctx_len = kv->ctx_len;
   g.kcache = static_cast<char *>(kv->k);
   g.vcache = static_cast<char *>(kv->v);
@@ -497,7 +523,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     q.n_q = d->n_q_heads;
     q.n_kv = d->n_kv_heads;
     q.head_dim = hd;
-    q.rope_theta = d->rope_theta;
+    fill_rope(q, d);
     q.ctx_len = kv->ctx_len;
     q.qbuf = wsb + L.qbuf;
     q.kblk = wsb + L.kblk;

@@ -161,6 +161,10 @@ __host__ __device__ inline int rot_channel(int r, int head_dim) {
   return p < 8 ? 8 * t + p : head_dim / 2 + 8 * t + (p - 8);
 }
 
+// Barrier for LDS traffic only: waits for this wavefront's LDS operations,
+// not for its outstanding global loads (which __syncthreads would drain).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------- dispatch
 
 // Workgroups of one launch are dispatched round-robin over the 8 XCDs; remap

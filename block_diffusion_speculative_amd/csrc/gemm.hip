@@ -26,21 +26,15 @@ __device__ inline float tile_at(const f32x4 *t, int NB, int ml, int nl) {
   return t[f * 64 + ln][nl & 3];
 }
 
-// cos and sin of pos * theta^(-2i/d), evaluated in fp64 and rounded once.
-__device__ inline void rope_cs(int pos, int i, int d, float theta, float *c, float *s) {
-  const double inv = pow(double(theta), -2.0 * double(i) / double(d));
-  const double a = double(pos) * inv;
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  *c = float(cd);
-  *s = float(sd);
-}
-
-__device__ inline float rope_apply(float v, float partner, int dd, int d, int pos, float theta) {
-  if (theta == 0.f) return v;
+// Rotate-half RoPE on one element.  The angle pos * theta^(-2i/d) is formed
+// in turns (host-computed theta^(-2i/d) / 2pi in fp64), reduced to [0, 1) in
+// fp64, and fed to the hardware sin/cos, which take turns.
+__device__ inline float rope_apply(float v, float partner, int dd, int d, int pos, const GemmParams &p) {
+  if (!p.rope_on) return v;
   const int half = d >> 1;
-  float c, s;
-  rope_cs(pos, dd % half, d, theta, &c, &s);
+  const double t = double(pos) * p.rope_turns[dd % half];
+  const float f = float(t - floor(t));
+  const float c = __builtin_amdgcn_cosf(f), s = __builtin_amdgcn_sinf(f);
   return dd < half ? v * c - partner * s : v * c + partner * s;
 }
 
@@ -62,131 +56,28 @@ __device__ inline int key_index(unsigned long long k) {
   return static_cast<int>(~static_cast<unsigned>(k & 0xffffffffull));
 }
 
-// Every GEMM workgroup has 16 wavefronts and splits K into the same 16
-// contiguous chunks whatever the row-tile count, so a row's result does not
-// depend on how many other rows share the launch.
-template <int MT> struct GemmShape {
-  static constexpr int WAVES = 16;
-  static constexpr int THREADS = WAVES * 64;
+// Every GEMM workgroup has 8 wavefronts (two per SIMD, so each may hold up to
+// 256 VGPRs) and splits K into the same 8 contiguous chunks whatever the
+// row-tile count.  Within a chunk, k-tiles are consumed in batches of two,
+// each tile of a batch feeding its own accumulator chain per activation plane;
+// chains and wavefronts are summed in a fixed order.  The summation order of a
+// row therefore never depends on how many other rows share the launch.
+constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_THREADS = GEMM_WAVES * 64;
+constexpr int GEMM_U = 2;
+
+template <int NB> struct WBatch { uint4 w[GEMM_U][NB]; };
+template <int MT, int NB, int XS> struct XWBatch {
+  uint4 w[GEMM_U][NB];
+  uint4 x[GEMM_U][MT][XS];
 };
 
-// Largest unroll (power of two, at most 8) whose in-flight fragments plus
-// accumulators fit about 25 x 16 bytes per lane (the 128-VGPR budget of a
-// 1024-thread workgroup, with room for addresses).
-constexpr int pick_unroll(int nb, int mt, int xs) {
-  int u = 8;
-  while (u > 1 && u * (nb + mt * xs) + mt * nb > 25) u >>= 1;
-  return u;
-}
-
-template <typename T, int MT, int NB, int EPI, int XS>
-__global__ __launch_bounds__(GemmShape<MT>::THREADS) void gemm_kernel(const GemmParams p) {
-  constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
-  constexpr int WAVES = GemmShape<MT>::WAVES, NT = GemmShape<MT>::THREADS;
-  constexpr int U = pick_unroll(NB, MT, XS);  // k-tiles per batch of loads
-  constexpr int NF = MT * NB;
-  constexpr int R = MT * 16, CN = NB * 16;
-  constexpr int ROUND = (32 / NF) < WAVES ? (32 / NF) : WAVES;  // wavefronts per LDS round (<= 32 KiB)
-  static_assert(NF * 64 <= NT, "one accumulator element per thread");
-  __shared__ f32x4 red[ROUND * NF * 64];
-
-  const int total = p.m_blocks * p.n_blocks;
-  const int bid = xcd_remap(blockIdx.x, total);
-  const int nblk = bid % p.n_blocks;
-  const int mblk = bid / p.n_blocks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-
-  const int nt0 = nblk * NB;
-  const int seg = nt0 / p.seg_ntiles;
-  const char *wbase = p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * p.k_tiles * 1024 + lane * 16;
-  const size_t wstride = size_t(p.k_tiles) * 1024;
-
-  const int per = (p.k_tiles + WAVES - 1) / WAVES;
-  const int k0 = min(wave * per, p.k_tiles);
-  const int k1 = min(k0 + per, p.k_tiles);
-  const int mt0 = mblk * MT;
-
-  // B-operand chunk of token tile mt at column tile kt, activation plane xp
-  // (zero past the rows).
-  auto load_x = [&](int mt, int kt, int xp) -> uint4 {
-    const int mtg = mt0 + mt;
-    if (p.x_ld == 0) {
-      if (mtg >= p.m_tiles) return make_uint4(0, 0, 0, 0);
-      return ld16(p.x + xp * p.x_plane + (size_t(mtg) * p.k_tiles + kt) * 1024 + lane * 16);
-    }
-    const int row = mtg * 16 + (lane & 15);
-    if (row >= p.M) return make_uint4(0, 0, 0, 0);
-    const int col = kt * KT + (lane >> 4) * E;
-    return ld16(p.x + (size_t(row) * p.x_ld + col) * ES);
-  };
-
-  f32x4 acc[MT][NB];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  int kt = k0;
-  for (; kt + U <= k1; kt += U) {
-    uint4 wf[U][NB], xf[U][MT][XS];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wf[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int xp = 0; xp < XS; ++xp) xf[u][mt][xp] = load_x(mt, kt + u, xp);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int xp = 0; xp < XS; ++xp) acc[mt][nb] = mma<T>(acc[mt][nb], wf[u][nb], xf[u][mt][xp]);
-  }
-  for (; kt < k1; ++kt) {
-    uint4 wf[NB], xf[MT][XS];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) wf[nb] = ld16_stream(wbase + nb * wstride + size_t(kt) * 1024);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int xp = 0; xp < XS; ++xp) xf[mt][xp] = load_x(mt, kt, xp);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int xp = 0; xp < XS; ++xp) acc[mt][nb] = mma<T>(acc[mt][nb], wf[nb], xf[mt][xp]);
-  }
-
-  // Sum the wavefronts' partial tiles in wavefront order, ROUND at a time.
-  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int e_own = threadIdx.x;  // element owned in the final tile
-  for (int r0 = 0; r0 < WAVES; r0 += ROUND) {
-    if (wave >= r0 && wave < r0 + ROUND) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) red[((wave - r0) * NF + mt * NB + nb) * 64 + lane] = acc[mt][nb];
-    }
-    __syncthreads();
-    if (e_own < NF * 64) {
-      for (int w = 0; w < ROUND; ++w) {
-        if (r0 == 0 && w == 0) sum = red[e_own];
-        else sum += red[w * NF * 64 + e_own];
-      }
-    }
-    __syncthreads();
-  }
-  if (e_own < NF * 64) red[e_own] = sum;
-  __syncthreads();
-
-  // ---------------------------------------------------------------- epilogues
+// Epilogue of one output tile (the reduced MT x NB fragment tile in LDS).
+template <typename T, int MT, int NB, int EPI>
+__device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int mblk, int nblk,
+                                     unsigned long long *best_row) {
+  constexpr int KT = Ty<T>::KT, ES = Ty<T>::SIZE;
+  constexpr int R = MT * 16, CN = NB * 16, NT = GEMM_THREADS;
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     for (int e = threadIdx.x; e < R * CN; e += NT) {
       const int ml = e / CN, nl = e % CN;
@@ -202,8 +93,7 @@ __global__ __launch_bounds__(GemmShape<MT>::THREADS) void gemm_kernel(const Gemm
     for (int e = threadIdx.x; e < R * HALF * 16; e += NT) {
       const int ml = e / (HALF * 16), q = e % (HALF * 16);
       const int pr = q >> 4, c = q & 15;
-      const int m = mblk * R + ml;
-      if (m >= p.m_tiles * 16) continue;
+      const int m = mblk * R + ml;  // padded rows get zeros
       const int col = (nblk * HALF + pr) * 16 + c;
       float out = 0.f;
       if (m < p.M) {
@@ -225,7 +115,7 @@ __global__ __launch_bounds__(GemmShape<MT>::THREADS) void gemm_kernel(const Gemm
       if (n < nqd + nkd) {
         const int dd = rot_channel(n % d, d);
         const int pos = p.ctx_len[s] + j;
-        v = rope_apply(v, tile_at(red, NB, ml, nl ^ 8), dd, d, pos, p.rope_theta);
+        v = rope_apply(v, tile_at(red, NB, ml, nl ^ 8), dd, d, pos, p);
         if (n < nqd) {
           const int h = n / d;
           char *base = p.qbuf + (size_t(s) * p.n_q + h) * dt_count * 1024;
@@ -265,7 +155,7 @@ __global__ __launch_bounds__(GemmShape<MT>::THREADS) void gemm_kernel(const Gemm
       const float v = tile_at(red, NB, ml, nl);
       if (c < nkd) {
         const int g = c / d, dd = rot_channel(c % d, d);
-        const float r = rope_apply(v, tile_at(red, NB, ml, nl ^ 8), dd, d, pos, p.rope_theta);
+        const float r = rope_apply(v, tile_at(red, NB, ml, nl ^ 8), dd, d, pos, p);
         char *base = p.kcache + ((size_t(layer) * p.max_batch + s) * p.n_kv + g) * region;
         store_elem<T>(base + kcache_offset<T>(pos, dd, d), r);
       } else {
@@ -275,22 +165,261 @@ __global__ __launch_bounds__(GemmShape<MT>::THREADS) void gemm_kernel(const Gemm
       }
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
-    if (threadIdx.x < R) {
-      const int ml = threadIdx.x;
-      const int m = mblk * R + ml;
-      if (m < p.M) {
-        unsigned long long best = 0;
-        for (int nl = 0; nl < CN; ++nl) {
-          const int n = nblk * CN + nl;
-          if (n < p.vocab) {
-            const unsigned long long k = argmax_key(tile_at(red, NB, ml, nl), n);
-            best = k > best ? k : best;
-          }
+    // Running best (logit, index) key per row over this workgroup's tiles:
+    // one element per thread, a 32-lane shuffle max per row (CN == 32), and
+    // the row's leader folds the result into best_row.
+    static_assert(CN == 32, "argmax epilogue expects 32 columns per tile");
+    for (int e0 = 0; e0 < R * CN; e0 += NT) {
+      const int e = e0 + int(threadIdx.x);
+      const int ml = e >> 5, nl = e & 31;
+      const int n = nblk * CN + nl;
+      unsigned long long k = 0;
+      if (ml < R && n < p.vocab) k = argmax_key(tile_at(red, NB, ml, nl), n);
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(k, off, 64);
+        k = o > k ? o : k;
+      }
+      if (nl == 0 && ml < R && k > best_row[ml]) best_row[ml] = k;
+    }
+  }
+}
+
+// XROW: activations are a row-major [M, x_ld] input (one plane); otherwise
+// packed fragment tiles padded to whole row blocks (so no load needs a guard).
+// KC > 0: every wavefront's K chunk (at most KC tiles) of activations is
+// loaded into registers once, and only weights stream through the loop (the
+// texture-address unit, not HBM, limits a loop that also streams
+// activations).  KC == 0: activations stream with the weights.
+template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) {
+  constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
+  constexpr int WAVES = GEMM_WAVES, NT = GEMM_THREADS, U = GEMM_U;
+  constexpr int NF = MT * NB;
+  constexpr int R = MT * 16;
+  constexpr bool XRES = KC > 0;
+  static_assert(!XRES || (KC % (2 * U)) == 0, "resident chunk: an even number of batches");
+  static_assert(NF * 64 <= NT, "one accumulator element per thread");
+  constexpr int ROUND = (16 / NF) < WAVES ? (16 / NF) : WAVES;  // wavefronts per LDS round (<= 16 KiB)
+  __shared__ f32x4 red[ROUND * NF * 64];
+  __shared__ f32x4 tile[NF * 64];
+  __shared__ unsigned long long best_row[R];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_items = p.m_blocks * p.n_blocks;
+  const int my_items = (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+  const int per = (p.k_tiles + WAVES - 1) / WAVES;      // k-tiles of every wavefront's chunk
+  const int k0 = min(wave * per, p.k_tiles);
+  const int k1 = min(k0 + per, p.k_tiles);
+  const int kclamp = k1 > 0 ? k1 - 1 : 0;
+  const int nbat = XRES ? KC / U : (per + U - 1) / U;   // batches per item, uniform over wavefronts
+  const size_t wstride = size_t(p.k_tiles) * 1024;
+
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (threadIdx.x < R) best_row[threadIdx.x] = 0;
+  }
+
+  auto item_of = [&](int i) { return int(blockIdx.x) + i * int(gridDim.x); };
+  auto w_addr = [&](int item) {
+    const int nt0 = (item % p.n_blocks) * NB;
+    const int seg = nt0 / p.seg_ntiles;
+    return p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride + lane * 16;
+  };
+  auto x_load = [&](int mtg, int kt, int xp) -> uint4 {
+    if constexpr (XROW) {
+      const int row = min(mtg * 16 + (lane & 15), p.M - 1);
+      return ld16(p.x + (size_t(row) * p.x_ld + kt * KT + (lane >> 4) * E) * ES);
+    } else {
+      return ld16(p.x + xp * p.x_plane + (size_t(mtg) * p.k_tiles + kt) * 1024 + lane * 16);
+    }
+  };
+
+  f32x4 acc[U][XS][MT][NB];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int c = 0; c < U; ++c)
+#pragma unroll
+      for (int xp = 0; xp < XS; ++xp)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[c][xp][mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Chain sum for tile (mt, nb): (c0 + c1) per plane, then hi + lo.
+  auto chain_sum = [&](int mt, int nb) -> f32x4 {
+    f32x4 r = acc[0][0][mt][nb];
+#pragma unroll
+    for (int c = 1; c < U; ++c) r += acc[c][0][mt][nb];
+#pragma unroll
+    for (int xp = 1; xp < XS; ++xp) {
+      f32x4 q = acc[0][xp][mt][nb];
+#pragma unroll
+      for (int c = 1; c < U; ++c) q += acc[c][xp][mt][nb];
+      r += q;
+    }
+    return r;
+  };
+  auto mma_tile = [&](int u, int b, const uint4 (&w)[U][NB], const uint4 (&x)[MT][XS], int mblk) {
+    const bool ok = k0 + b * U + u < k1;
+    bool row_ok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) row_ok[mt] = !XROW || (mblk * MT + mt) * 16 + (lane & 15) < p.M;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint4 wv = ok ? w[u][nb] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int xp = 0; xp < XS; ++xp) {
+          const uint4 xv = row_ok[mt] ? x[mt][xp] : make_uint4(0, 0, 0, 0);
+          acc[u][xp][mt][nb] = mma<T>(acc[u][xp][mt][nb], wv, xv);
         }
-        __hip_atomic_fetch_max(p.keys + size_t(m) * ARGMAX_SLOTS + (nblk % ARGMAX_SLOTS), best,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  int cur_mblk = -1;
+  auto flush_argmax = [&](int mblk) {
+    if constexpr (EPI == EPI_ARGMAX) {
+      if (threadIdx.x < R) {
+        const int m = mblk * R + threadIdx.x;
+        if (m < p.M && best_row[threadIdx.x] != 0)
+          __hip_atomic_fetch_max(p.keys + size_t(m) * ARGMAX_SLOTS + (blockIdx.x % ARGMAX_SLOTS),
+                                 best_row[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        best_row[threadIdx.x] = 0;
       }
     }
+  };
+  // Fold the wavefronts' partial tiles in wavefront order and run the epilogue.
+  auto finish_item = [&](int item) {
+    const int nblk = item % p.n_blocks, mblk = item / p.n_blocks;
+    if constexpr (EPI == EPI_ARGMAX) {
+      if (mblk != cur_mblk && cur_mblk >= 0) flush_argmax(cur_mblk);
+      cur_mblk = mblk;
+    }
+    if constexpr (NF <= 2) {
+      // All 8 partial tiles fit in LDS at once (<= 16 KiB).
+      constexpr int F = NF * 256;  // floats per tile
+      float *redf = reinterpret_cast<float *>(red);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) red[(wave * NF + mt * NB + nb) * 64 + lane] = chain_sum(mt, nb);
+      lds_barrier();
+      if (int(threadIdx.x) < F) {
+        const int f = threadIdx.x;
+        float v = redf[f];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += redf[w * F + f];
+        reinterpret_cast<float *>(tile)[f] = v;
+      }
+      lds_barrier();
+    } else {
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int e_own = threadIdx.x;
+      for (int r0 = 0; r0 < WAVES; r0 += ROUND) {
+        if (wave >= r0 && wave < r0 + ROUND) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) red[((wave - r0) * NF + mt * NB + nb) * 64 + lane] = chain_sum(mt, nb);
+        }
+        lds_barrier();
+        if (e_own < NF * 64) {
+          for (int w = 0; w < ROUND; ++w) {
+            if (r0 == 0 && w == 0) sum = red[e_own];
+            else sum += red[w * NF * 64 + e_own];
+          }
+        }
+        lds_barrier();
+      }
+      if (e_own < NF * 64) tile[e_own] = sum;
+      lds_barrier();
+    }
+    gemm_epilogue<T, MT, NB, EPI>(p, tile, mblk, nblk, best_row);
+    zero_acc();
+  };
+
+  zero_acc();
+  if constexpr (XRES) {
+    // Activations of this wavefront's chunk, loaded once (one row block).
+    uint4 xr[KC][MT][XS];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int kt = min(k0 + j, kclamp);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int xp = 0; xp < XS; ++xp) xr[j][mt][xp] = x_load(mt, kt, xp);
+    }
+    constexpr int NBAT = KC / U;
+    WBatch<NB> wb[2];
+    auto issue_w = [&](int item, int b, WBatch<NB> &f) {
+      const char *wbase = w_addr(item);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kt = min(k0 + b * U + u, kclamp);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt) * 1024);
+      }
+    };
+    issue_w(item_of(0), 0, wb[0]);
+    for (int i = 0; i < my_items; ++i) {
+      const int item = item_of(i);
+      const int next = item_of(min(i + 1, my_items - 1));
+#pragma unroll
+      for (int b = 0; b < NBAT; ++b) {
+        if (b + 1 < NBAT) issue_w(item, b + 1, wb[(b + 1) & 1]);
+        else issue_w(next, 0, wb[0]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
+#pragma unroll
+        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0);
+      }
+      finish_item(item);
+    }
+  } else {
+    // Activations stream with the weights; two batches in flight.
+    XWBatch<MT, NB, XS> fa, fb;
+    const int T_steps = my_items * nbat;
+    const int t_last = T_steps - 1;
+    auto issue = [&](int t, XWBatch<MT, NB, XS> &f) {
+      const int item = item_of(t / nbat);
+      const int b = t % nbat;
+      const int mblk = item / p.n_blocks;
+      const char *wbase = w_addr(item);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kt = min(k0 + b * U + u, kclamp);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt) * 1024);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int xp = 0; xp < XS; ++xp) f.x[u][mt][xp] = x_load(mblk * MT + mt, kt, xp);
+      }
+    };
+    auto compute = [&](int t, const XWBatch<MT, NB, XS> &f) {
+      const int b = t % nbat;
+      const int mblk = item_of(t / nbat) / p.n_blocks;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mma_tile(u, b, f.w, f.x[u], mblk);
+    };
+    issue(0, fa);
+    for (int t = 0; t < T_steps; t += 2) {
+      issue(min(t + 1, t_last), fb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t, fa);
+      if (t % nbat == nbat - 1) finish_item(item_of(t / nbat));
+      issue(min(t + 2, t_last), fa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < T_steps) {
+        compute(t + 1, fb);
+        if ((t + 1) % nbat == nbat - 1) finish_item(item_of((t + 1) / nbat));
+      }
+    }
+  }
+  if constexpr (EPI == EPI_ARGMAX) {
+    lds_barrier();
+    if (cur_mblk >= 0) flush_argmax(cur_mblk);
   }
 }
 
@@ -335,26 +464,50 @@ __global__ __launch_bounds__(64) void commit_rows_kernel(int *ctx_len, const int
   }
 }
 
-template <typename T, int EPI, int NB, int XS>
-static hipError_t launch_xs(const GemmParams &p, hipStream_t s) {
-  const dim3 grid(p.m_blocks * p.n_blocks);
-  switch (p.MT) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, NB, EPI, XS>), grid, dim3(GemmShape<1>::THREADS), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, NB, EPI, XS>), grid, dim3(GemmShape<2>::THREADS), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<T, 4, NB, EPI, XS>), grid, dim3(GemmShape<4>::THREADS), 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
+template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
+static hipError_t launch_one(const GemmParams &p, hipStream_t s) {
+  const int items = p.m_blocks * p.n_blocks;
+  const dim3 grid(items < p.grid_cap ? items : p.grid_cap);
+  hipLaunchKernelGGL((gemm_kernel<T, MT, NB, EPI, XS, XROW, KC>), grid, dim3(GEMM_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
+// Resident activations when the launch is one row block, MT * XS <= 2 and a
+// wavefront's K chunk is at most 16 tiles; the chunk register array is sized
+// 4, 8 or 16 tiles.
+template <typename T, int MT, int NB, int EPI, int XS, bool XROW>
+static hipError_t launch_kc(const GemmParams &p, hipStream_t s) {
+  const int per = (p.k_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
+  if constexpr (MT * XS <= 2) {
+    if (p.m_blocks == 1) {
+      if (per <= 4) return launch_one<T, MT, NB, EPI, XS, XROW, 4>(p, s);
+      if (per <= 8) return launch_one<T, MT, NB, EPI, XS, XROW, 8>(p, s);
+      if (per <= 16) return launch_one<T, MT, NB, EPI, XS, XROW, 16>(p, s);
+    }
+  }
+  return launch_one<T, MT, NB, EPI, XS, XROW, 0>(p, s);
+}
+
+template <typename T, int EPI, int NB, int XS, bool XROW>
+static hipError_t launch_xs(const GemmParams &p, hipStream_t s) {
+  switch (p.MT) {
+    case 1: return launch_kc<T, 1, NB, EPI, XS, XROW>(p, s);
+    case 2: return launch_kc<T, 2, NB, EPI, XS, XROW>(p, s);
+    case 4: return launch_kc<T, 4, NB, EPI, XS, XROW>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // Activation planes: fp32 storage always has one; bf16 activations that the
-// step produces itself carry two (hi + lo), external bf16 inputs one.
+// step produces itself carry two (hi + lo); external row-major inputs (target
+// features, target hidden states) one.
 template <typename T, int EPI, int NB>
 static hipError_t launch_mt(const GemmParams &p, hipStream_t s) {
+  if (p.x_ld > 0) return p.xs == 1 ? launch_xs<T, EPI, NB, 1, true>(p, s) : hipErrorInvalidValue;
   if constexpr (Ty<T>::SIZE == 2) {
-    if (p.xs == 2) return launch_xs<T, EPI, NB, 2>(p, s);
+    if (p.xs == 2) return launch_xs<T, EPI, NB, 2, false>(p, s);
   }
-  return p.xs == 1 ? launch_xs<T, EPI, NB, 1>(p, s) : hipErrorInvalidValue;
+  return p.xs == 1 ? launch_xs<T, EPI, NB, 1, false>(p, s) : hipErrorInvalidValue;
 }
 
 template <typename T>

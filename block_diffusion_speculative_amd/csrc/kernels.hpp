@@ -38,6 +38,7 @@ struct GemmParams {
   int M, m_tiles, m_blocks, MT;
   int N, n_tiles, n_blocks, NB;
   int k_tiles;
+  int grid_cap;               // persistent workgroups: at most one per compute unit
   // EPI_STORE / EPI_RESID
   float *out_f32;
   const float *resid;
@@ -48,7 +49,8 @@ struct GemmParams {
   size_t out_plane;
   // EPI_QKV / EPI_KVINJ
   int block, n_q, n_kv, head_dim;
-  float rope_theta;
+  int rope_on;
+  double rope_turns[64];      // theta^(-2i/d) / (2 pi), i < head_dim / 2
   const int *ctx_len;
   char *qbuf, *kblk, *vblk;
   size_t q_plane;
