@@ -24,7 +24,7 @@ DFLASH_ERR_HIP = -6
 DFLASH_ERR_UNSUPPORTED = -7
 DFLASH_STATUS_CAPACITY = 1
 DFLASH_STATUS_TOKEN = 2
-VIEW_FUSED, VIEW_HIDDEN, VIEW_MID, VIEW_ATTN, VIEW_FINAL = range(5)
+VIEW_FUSED, VIEW_HIDDEN, VIEW_MID, VIEW_ATTN = range(4)
 
 EXPORTED = [
     "dflash_packed_bytes", "dflash_pack_matrix", "dflash_pack_qkv", "dflash_pack_gate_up",

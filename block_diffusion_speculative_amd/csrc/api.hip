@@ -74,9 +74,10 @@ struct Bump {
 int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
 
 struct DraftLayout {
-  size_t hidden, mid, attn, final_, xa, xo, xact, qbuf, kblk, vblk, apart, end;
+  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
   int M, Mp, S, xs;
+  bool rs_inline;  // consumers reduce the RMSNorm tile sums themselves (one row block)
   GemmPlan qkv, o, gu, down, lm;
 };
 
@@ -98,7 +99,8 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.hidden = b.take(row * (d->n_layers + 1));
   L.mid = b.take(row * d->n_layers);
   L.attn = b.take(size_t(L.M) * NQD * 4 * d->n_layers);
-  L.final_ = b.take(row);
+  L.ssq = b.take(size_t(L.M) * (H / 16) * 4);
+  L.rs = b.take(size_t(L.M) * 4);
   L.xs = act_planes(d);
   L.pa = packed_bytes(d->dtype, L.Mp, H);
   L.po = packed_bytes(d->dtype, L.Mp, NQD);
@@ -111,6 +113,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.kblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
+  L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
   L.end = b.off;
   return L;
 }
@@ -128,8 +131,9 @@ VerifyLayout verify_layout(const dflash_dims *d, int batch) {
 }
 
 struct InjectLayout {
-  size_t u, fused, xc, end, pc;
+  size_t u, xc, ssq, rs, end, pc;
   int Rp, xs;
+  bool rs_inline;
   GemmPlan fc, kv;
 };
 
@@ -142,10 +146,12 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   L.Rp = L.kv.m_blocks * L.kv.MT * 16;
   Bump b;
   L.u = b.take(size_t(rows) * H * 4);
-  L.fused = b.take(size_t(rows) * H * 4);
+  L.ssq = b.take(size_t(rows) * (H / 16) * 4);
+  L.rs = b.take(size_t(rows) * 4);
   L.xs = act_planes(d);
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
+  L.rs_inline = gemm_inline_rs_ok(L.kv.m_blocks, L.kv.MT, H);
   L.end = b.off;
   return L;
 }
@@ -235,6 +241,35 @@ void fill_rope(GemmParams &p, const dflash_dims *d) {
   const int half = d->head_dim / 2;
   for (int i = 0; i < half && i < 64; ++i)
     p.rope_turns[i] = std::pow(double(d->rope_theta), -2.0 * i / d->head_dim) / (2.0 * M_PI);
+}
+
+// Producer half of an RMSNorm: the launch's fp32 output rows also go out as
+// packed (rows * gain) planes of rows_pad rows and as tile sums of squares.
+void set_norm_out(GemmParams &p, char *packed, int kt_count, int planes, size_t plane_bytes, int rows_pad,
+                  const void *gain, float *ssq) {
+  p.nx_packed = packed;
+  p.nx_kt = kt_count;
+  p.nx_planes = planes;
+  p.nx_plane = plane_bytes;
+  p.nx_rows = rows_pad;
+  p.nx_gain = static_cast<const char *>(gain);
+  p.ssq_out = ssq;
+  p.ssq_ld = p.N / 16;
+}
+
+// Consumer half: scale the output rows by 1 / rms from the producer's tile
+// sums, inline for one row block, else through rstd_kernel (one launch).
+hipError_t set_norm_in(GemmParams &p, bool inline_rs, const float *ssq, float *rs, int M, int H, float eps,
+                       hipStream_t stream) {
+  p.rs_tiles = H / 16;
+  p.rs_K = H;
+  p.rs_eps = eps;
+  if (inline_rs) {
+    p.rs_ssq = ssq;
+    return hipSuccess;
+  }
+  p.rs_direct = rs;
+  return launch_rstd(ssq, H / 16, H, eps, M, rs, stream);
 }
 
 void fill_gemm(GemmParams &p, const GemmPlan &g) {
@@ -360,7 +395,7 @@ int dflash_workspace_view(const dflash_dims *d, int32_t what, int32_t count, int
   const int H = d->hidden, NQD = d->n_q_heads * d->head_dim;
   if (what == DFLASH_VIEW_FUSED) {
     const InjectLayout L = inject_layout(d, count);
-    *offset = L.fused;
+    *offset = L.u;
     *bytes = size_t(count) * H * 4;
     return DFLASH_OK;
   }
@@ -382,10 +417,6 @@ int dflash_workspace_view(const dflash_dims *d, int32_t what, int32_t count, int
       if (layer < 0 || layer >= d->n_layers) return fail(DFLASH_ERR_SHAPE, "layer out of range");
       *offset = L.attn + size_t(L.M) * NQD * 4 * layer;
       *bytes = size_t(L.M) * NQD * 4;
-      return DFLASH_OK;
-    case DFLASH_VIEW_FINAL:
-      *offset = L.final_;
-      *bytes = row;
       return DFLASH_OK;
     default:
       return fail(DFLASH_ERR_SHAPE, "unknown view");
@@ -416,23 +447,10 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   fc.x_ld = d->n_feat_layers * H;
   fc.out_f32 = reinterpret_cast<float *>(wsb + L.u);
   fc.ld_out = H;
+  float *ssq = reinterpret_cast<float *>(wsb + L.ssq);
+  set_norm_out(fc, wsb + L.xc, H / kt, L.xs, L.pc, L.Rp, w->fc_norm, ssq);
   hipError_t e = launch_gemm(d->dtype, EPI_STORE, fc, stream);
   if (e != hipSuccess) return hip_fail(e, "inject fc");
-
-  NormParams np{};
-  np.src = reinterpret_cast<const float *>(wsb + L.u);
-  np.gain = static_cast<const char *>(w->fc_norm);
-  np.eps = d->rms_eps;
-  np.M = rows;
-  np.rows_pad = L.Rp;
-  np.H = H;
-  np.xpacked = wsb + L.xc;
-  np.x_kt = H / kt;
-  np.planes = L.xs;
-  np.x_plane = L.pc;
-  np.normed = reinterpret_cast<float *>(wsb + L.fused);
-  e = launch_norm_pack(d->dtype, np, stream);
-  if (e != hipSuccess) return hip_fail(e, "inject norm");
 
   GemmParams g{};
   fill_gemm(g, L.kv);
@@ -446,6 +464,8 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   g.x_ld = 0;
   g.xs = L.xs;
   g.x_plane = L.pc;
+  e = set_norm_in(g, L.rs_inline, ssq, reinterpret_cast<float *>(wsb + L.rs), rows, H, d->rms_eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "inject norm");
   g.n_q = d->n_q_heads;
   g.n_kv = d->n_kv_heads;
   g.head_dim = hd;
@@ -484,26 +504,31 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   float *hidden = reinterpret_cast<float *>(wsb + L.hidden);
   float *mid = reinterpret_cast<float *>(wsb + L.mid);
   const size_t region_layer = size_t(kv->max_batch) * d->n_kv_heads * size_t(kv->capacity) * hd * esize_of(d->dtype);
+  float *ssq = reinterpret_cast<float *>(wsb + L.ssq);
+  float *rs = reinterpret_cast<float *>(wsb + L.rs);
   hipError_t e;
 
-  NormParams np{};
-  np.embed = static_cast<const char *>(w->embed);
-  np.last_tok = last_tok;
-  np.block = d->block_size;
-  np.mask_id = d->mask_id;
-  np.vocab = d->vocab;
-  np.status = kv->status;
-  np.gathered = hidden;
-  np.gain = static_cast<const char *>(w->layers[0].attn_norm);
-  np.eps = d->rms_eps;
-  np.M = L.M;
-  np.rows_pad = L.Mp;
-  np.H = H;
-  np.xpacked = wsb + L.xa;
-  np.x_kt = H / kt;
-  np.planes = L.xs;
-  np.x_plane = L.pa;
-  e = launch_norm_pack(d->dtype, np, stream);
+  // Every RMSNorm is split: its producer (the embedding, o_proj, down) writes
+  // the rows * gain into xa plus tile sums of squares; its consumer (QKV,
+  // gate_up, lm_head) scales its output rows by 1 / rms.
+  EmbedParams ep{};
+  ep.embed = static_cast<const char *>(w->embed);
+  ep.last_tok = last_tok;
+  ep.block = d->block_size;
+  ep.mask_id = d->mask_id;
+  ep.vocab = d->vocab;
+  ep.status = kv->status;
+  ep.gathered = hidden;
+  ep.gain = static_cast<const char *>(w->layers[0].attn_norm);
+  ep.M = L.M;
+  ep.rows_pad = L.Mp;
+  ep.H = H;
+  ep.xpacked = wsb + L.xa;
+  ep.x_kt = H / kt;
+  ep.planes = L.xs;
+  ep.x_plane = L.pa;
+  ep.ssq = ssq;
+  e = launch_embed(d->dtype, ep, stream);
   if (e != hipSuccess) return hip_fail(e, "draft embed");
 
   for (int l = 0; l < NL; ++l) {
@@ -528,7 +553,8 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     q.qbuf = wsb + L.qbuf;
     q.kblk = wsb + L.kblk;
     q.vblk = wsb + L.vblk;
-    e = launch_gemm(d->dtype, EPI_QKV, q, stream);
+    e = set_norm_in(q, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
+    if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_QKV, q, stream);
     if (e != hipSuccess) return hip_fail(e, "draft qkv");
 
     AttnParams a{};
@@ -567,22 +593,9 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     o.out_f32 = h_mid;
     o.resid = h_in;
     o.ld_out = H;
+    set_norm_out(o, wsb + L.xa, H / kt, L.xs, L.pa, L.Mp, lw.mlp_norm, ssq);
     e = launch_gemm(d->dtype, EPI_RESID, o, stream);
     if (e != hipSuccess) return hip_fail(e, "draft o_proj");
-
-    NormParams n2{};
-    n2.src = h_mid;
-    n2.gain = static_cast<const char *>(lw.mlp_norm);
-    n2.eps = d->rms_eps;
-    n2.M = L.M;
-    n2.rows_pad = L.Mp;
-    n2.H = H;
-    n2.xpacked = wsb + L.xa;
-    n2.x_kt = H / kt;
-    n2.planes = L.xs;
-    n2.x_plane = L.pa;
-    e = launch_norm_pack(d->dtype, n2, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft mlp norm");
 
     GemmParams gu{};
     fill_gemm(gu, L.gu);
@@ -594,7 +607,8 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     gu.out_plane = L.pact;
     gu.out_packed = wsb + L.xact;
     gu.out_kt = I / kt;
-    e = launch_gemm(d->dtype, EPI_SWIGLU, gu, stream);
+    e = set_norm_in(gu, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
+    if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_SWIGLU, gu, stream);
     if (e != hipSuccess) return hip_fail(e, "draft gate_up");
 
     GemmParams dn{};
@@ -606,23 +620,10 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     dn.out_f32 = h_out;
     dn.resid = h_mid;
     dn.ld_out = H;
+    set_norm_out(dn, wsb + L.xa, H / kt, L.xs, L.pa, L.Mp, l + 1 < NL ? w->layers[l + 1].attn_norm : w->final_norm,
+                 ssq);
     e = launch_gemm(d->dtype, EPI_RESID, dn, stream);
     if (e != hipSuccess) return hip_fail(e, "draft down");
-
-    NormParams n3{};
-    n3.src = h_out;
-    n3.gain = static_cast<const char *>(l + 1 < NL ? w->layers[l + 1].attn_norm : w->final_norm);
-    n3.eps = d->rms_eps;
-    n3.M = L.M;
-    n3.rows_pad = L.Mp;
-    n3.H = H;
-    n3.xpacked = wsb + L.xa;
-    n3.x_kt = H / kt;
-    n3.planes = L.xs;
-    n3.x_plane = L.pa;
-    n3.normed = l + 1 < NL ? nullptr : reinterpret_cast<float *>(wsb + L.final_);
-    e = launch_norm_pack(d->dtype, n3, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft norm");
   }
 
   GemmParams lm{};
@@ -631,6 +632,8 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   lm.x = wsb + L.xa;
   lm.xs = L.xs;
   lm.x_plane = L.pa;
+  e = set_norm_in(lm, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "draft final norm");
   lm.vocab = d->vocab;
   lm.keys = reinterpret_cast<unsigned long long *>(wsb);
   e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);

@@ -11,7 +11,9 @@
 namespace dflash {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Storage type tags.  bf16 values are carried as raw uint16 bit patterns.
 struct bf16_t { uint16_t bits; };
@@ -33,13 +35,11 @@ __host__ __device__ inline int esize_of(int dtype) { return dtype == DFLASH_BF16
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
-__device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// Round to nearest even with the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ inline uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
+__device__ inline uint16_t f32_to_bf16(float f) { return uint16_t(f32x2_to_bf16x2(f, 0.f)); }
 
 template <typename T> __device__ inline float to_f32(T v);
 template <> __device__ inline float to_f32<float>(float v) { return v; }
@@ -67,11 +67,8 @@ template <> __device__ inline uint4 chunk_pack<float>(const float *v) {
                     __float_as_uint(v[3]));
 }
 template <> __device__ inline uint4 chunk_pack<bf16_t>(const float *v) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = uint32_t(f32_to_bf16(v[2 * i])) | (uint32_t(f32_to_bf16(v[2 * i + 1])) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]), f32x2_to_bf16x2(v[4], v[5]),
+                    f32x2_to_bf16x2(v[6], v[7]));
 }
 
 // Split x into hi + lo parts of T (hi = T(x), lo = T(x - hi)); for fp32
@@ -159,6 +156,55 @@ __host__ __device__ inline size_t vcache_offset(int pos, int dd, int head_dim) {
 __host__ __device__ inline int rot_channel(int r, int head_dim) {
   const int t = r >> 4, p = r & 15;
   return p < 8 ? 8 * t + p : head_dim / 2 + 8 * t + (p - 8);
+}
+
+// ------------------------------------------------------------- RMSNorm
+
+// The RMSNorm statistics are assembled from per-(row, 16-column tile) sums of
+// squares.  A tile's sum is the balanced binary tree over its 16 squares in
+// column order (what an xor butterfly over 16 lanes computes).  A row's total
+// takes its tiles in 8 contiguous runs of 4 * ceil(tiles / 32) (the last runs
+// may be short or empty): run q is summed in order by lane q of an 8-lane
+// group, and the runs are combined by an xor butterfly.  Every kernel that
+// forms these values uses this order, so they agree bit for bit.
+constexpr int RSTD_MAX_TILES = 512;  // hidden <= 8192
+
+__device__ inline float tile_ssq16(float v) {
+  float s = __fmul_rn(v, v);  // rounded square: never contracted into the adds
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  s += __shfl_xor(s, 8, 64);
+  return s;
+}
+
+// 1 / sqrt(mean(x^2) + eps) of one row from its tile sums (tiles a multiple
+// of 4, 16-byte aligned); called by the 8 lanes (8-aligned) of a group, lane
+// q = lane & 7; every lane gets the result.  Loads go out 8 at a time.
+__device__ inline float row_rstd8(const float *tile_ssq, int tiles, int K, float eps) {
+  constexpr int V = 8;  // 16-byte loads per pass
+  const int q = threadIdx.x & 7;
+  const int run = 4 * ((tiles + 31) / 32);
+  const int t0 = min(q * run, tiles), t1 = min(t0 + run, tiles);
+  float s = 0.f;
+  for (int base = t0; base < t0 + run; base += 4 * V) {
+    f32x4 v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = *reinterpret_cast<const f32x4 *>(tile_ssq + min(base + 4 * i, tiles - 4));
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (base + 4 * i < t1) {
+        s += v[i][0];
+        s += v[i][1];
+        s += v[i][2];
+        s += v[i][3];
+      }
+    }
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  return 1.0f / sqrtf(s / float(K) + eps);
 }
 
 // Barrier for LDS traffic only: waits for this wavefront's LDS operations,

@@ -59,10 +59,13 @@ __device__ inline int key_index(unsigned long long k) {
 // Every GEMM workgroup has 8 wavefronts (two per SIMD, so each may hold up to
 // 256 VGPRs) and splits K into the same 8 contiguous chunks whatever the
 // row-tile count.  Within a chunk, k-tiles are consumed in batches of two,
-// each tile of a batch feeding its own accumulator chain per activation plane;
-// chains and wavefronts are summed in a fixed order.  The summation order of a
-// row therefore never depends on how many other rows share the launch.
+// each tile of a batch feeding its own accumulator chain per activation plane
+// (one chain per plane when NB * XS >= 4); chains and wavefronts are summed in
+// a fixed order.  The summation order of a row therefore never depends on how
+// many other rows share the launch.
 constexpr int GEMM_WAVES = 8;
+// LDS staging of an inline RMSNorm's tile sums: rows x tiles <= 8192 floats.
+constexpr int RS_STAGE_FLOATS = 8192;
 constexpr int GEMM_THREADS = GEMM_WAVES * 64;
 constexpr int GEMM_U = 2;
 
@@ -73,20 +76,36 @@ template <int MT, int NB, int XS> struct XWBatch {
 };
 
 // Epilogue of one output tile (the reduced MT x NB fragment tile in LDS).
+// rs: per-row scales of the activations' RMSNorm (nullptr: none).
 template <typename T, int MT, int NB, int EPI>
-__device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int mblk, int nblk,
+__device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, const float *rs, int mblk, int nblk,
                                      unsigned long long *best_row) {
   constexpr int KT = Ty<T>::KT, ES = Ty<T>::SIZE;
   constexpr int R = MT * 16, CN = NB * 16, NT = GEMM_THREADS;
+  auto val = [&](int ml, int nl) { return rs ? tile_at(red, NB, ml, nl) * rs[ml] : tile_at(red, NB, ml, nl); };
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    // 16 consecutive threads hold one row of the 16-column tile, so the
+    // tile's sum of squares is one butterfly (tile_ssq16).
+    static_assert(CN == 16, "row-major epilogues take one 16-column tile");
     for (int e = threadIdx.x; e < R * CN; e += NT) {
       const int ml = e / CN, nl = e % CN;
       const int m = mblk * R + ml, n = nblk * CN + nl;
-      if (m >= p.M || n >= p.N) continue;
-      float v = tile_at(red, NB, ml, nl);
-      const size_t o = size_t(m) * p.ld_out + n;
-      if constexpr (EPI == EPI_RESID) v += p.resid[o];
-      p.out_f32[o] = v;
+      const bool ok = m < p.M && n < p.N;
+      float v = 0.f;
+      if (ok) {
+        v = val(ml, nl);
+        const size_t o = size_t(m) * p.ld_out + n;
+        if constexpr (EPI == EPI_RESID) v += p.resid[o];
+        p.out_f32[o] = v;
+      }
+      if (p.nx_packed && n < p.N && m < p.nx_rows) {
+        const float y = ok ? v * to_f32<T>(reinterpret_cast<const T *>(p.nx_gain)[n]) : 0.f;
+        store_split<T>(p.nx_packed + packed_offset<T>(m, n, p.nx_kt), p.nx_plane, p.nx_planes, y);
+      }
+      if (p.ssq_out) {
+        const float t = tile_ssq16(v);
+        if (nl == 0 && ok) p.ssq_out[size_t(m) * p.ssq_ld + nblk] = t;
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     constexpr int HALF = NB / 2;
@@ -97,8 +116,8 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int 
       const int col = (nblk * HALF + pr) * 16 + c;
       float out = 0.f;
       if (m < p.M) {
-        const float gt = tile_at(red, NB, ml, 2 * pr * 16 + c);
-        const float up = tile_at(red, NB, ml, (2 * pr + 1) * 16 + c);
+        const float gt = val(ml, 2 * pr * 16 + c);
+        const float up = val(ml, (2 * pr + 1) * 16 + c);
         out = gt / (1.0f + __expf(-gt)) * up;
       }
       store_split<T>(p.out_packed + packed_offset<T>(m, col, p.out_kt), p.out_plane, p.out_planes, out);
@@ -111,11 +130,11 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int 
       const int m = mblk * R + ml, n = nblk * CN + nl;
       if (m >= p.M) continue;
       const int s = m / p.block, j = m % p.block;
-      float v = tile_at(red, NB, ml, nl);
+      float v = val(ml, nl);
       if (n < nqd + nkd) {
         const int dd = rot_channel(n % d, d);
         const int pos = p.ctx_len[s] + j;
-        v = rope_apply(v, tile_at(red, NB, ml, nl ^ 8), dd, d, pos, p);
+        v = rope_apply(v, val(ml, nl ^ 8), dd, d, pos, p);
         if (n < nqd) {
           const int h = n / d;
           char *base = p.qbuf + (size_t(s) * p.n_q + h) * dt_count * 1024;
@@ -152,10 +171,10 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int 
       }
       const int pos = C + (m - start);
       const int layer = p.layer0 + n / segn, c = n % segn;
-      const float v = tile_at(red, NB, ml, nl);
+      const float v = val(ml, nl);
       if (c < nkd) {
         const int g = c / d, dd = rot_channel(c % d, d);
-        const float r = rope_apply(v, tile_at(red, NB, ml, nl ^ 8), dd, d, pos, p);
+        const float r = rope_apply(v, val(ml, nl ^ 8), dd, d, pos, p);
         char *base = p.kcache + ((size_t(layer) * p.max_batch + s) * p.n_kv + g) * region;
         store_elem<T>(base + kcache_offset<T>(pos, dd, d), r);
       } else {
@@ -174,7 +193,7 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int 
       const int ml = e >> 5, nl = e & 31;
       const int n = nblk * CN + nl;
       unsigned long long k = 0;
-      if (ml < R && n < p.vocab) k = argmax_key(tile_at(red, NB, ml, nl), n);
+      if (ml < R && n < p.vocab) k = argmax_key(val(ml, nl), n);
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) {
         const unsigned long long o = __shfl_xor(k, off, 64);
@@ -191,6 +210,10 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, int 
 // loaded into registers once, and only weights stream through the loop (the
 // texture-address unit, not HBM, limits a loop that also streams
 // activations).  KC == 0: activations stream with the weights.
+//
+// RMSNorm: the activations arrive as (x * gain) and the epilogue scales each
+// output row by 1 / rms(x) (the scale commutes with the product), so the norm
+// needs neither its own launch nor a pass over the activations here.
 template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) {
   constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
@@ -204,6 +227,12 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   __shared__ f32x4 red[ROUND * NF * 64];
   __shared__ f32x4 tile[NF * 64];
   __shared__ unsigned long long best_row[R];
+  // Consumers of an RMSNorm (packed activations into QKV, KV injection,
+  // gate/up, the draft head) scale their output rows; the other launches
+  // carry no row-scale code.
+  constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX);
+  __shared__ float rs_row[RS ? R : 1];
+  __shared__ f32x4 rs_stage[RS ? RS_STAGE_FLOATS / 4 : 1];  // tile sums of the block's rows
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n_items = p.m_blocks * p.n_blocks;
@@ -234,10 +263,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     }
   };
 
-  f32x4 acc[U][XS][MT][NB];
+  // Accumulator chains: one per k-tile of a batch and activation plane, or
+  // one per plane when NB * XS already gives four independent chains.
+  constexpr int UC = NB * XS >= 4 ? 1 : U;
+  f32x4 acc[UC][XS][MT][NB];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int c = 0; c < U; ++c)
+    for (int c = 0; c < UC; ++c)
 #pragma unroll
       for (int xp = 0; xp < XS; ++xp)
 #pragma unroll
@@ -249,12 +281,12 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   auto chain_sum = [&](int mt, int nb) -> f32x4 {
     f32x4 r = acc[0][0][mt][nb];
 #pragma unroll
-    for (int c = 1; c < U; ++c) r += acc[c][0][mt][nb];
+    for (int c = 1; c < UC; ++c) r += acc[c][0][mt][nb];
 #pragma unroll
     for (int xp = 1; xp < XS; ++xp) {
       f32x4 q = acc[0][xp][mt][nb];
 #pragma unroll
-      for (int c = 1; c < U; ++c) q += acc[c][xp][mt][nb];
+      for (int c = 1; c < UC; ++c) q += acc[c][xp][mt][nb];
       r += q;
     }
     return r;
@@ -272,12 +304,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
         for (int xp = 0; xp < XS; ++xp) {
           const uint4 xv = row_ok[mt] ? x[mt][xp] : make_uint4(0, 0, 0, 0);
-          acc[u][xp][mt][nb] = mma<T>(acc[u][xp][mt][nb], wv, xv);
+          acc[u % UC][xp][mt][nb] = mma<T>(acc[u % UC][xp][mt][nb], wv, xv);
         }
     }
   };
 
   int cur_mblk = -1;
+  int items_done = 0;
   auto flush_argmax = [&](int mblk) {
     if constexpr (EPI == EPI_ARGMAX) {
       if (threadIdx.x < R) {
@@ -287,6 +320,65 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
                                  best_row[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         best_row[threadIdx.x] = 0;
       }
+    }
+  };
+  // Row scales.  Inline (rs_ssq, one row block): the rows' tile sums are
+  // loaded before anything else, staged in LDS once the first weight and
+  // activation loads are out, and reduced into rs_row while those loads are
+  // in flight.  Otherwise (rs_direct) each item's scales are fetched one item
+  // ahead into a register and moved to rs_row between the barriers of
+  // finish_item, after every reader of the previous values has passed the
+  // first barrier.
+  float rs_next = 1.f;
+  bool rs_first = true;
+  f32x4 rs_ld[RS_STAGE_FLOATS / 4 / GEMM_THREADS];
+  const int rs_n4 = RS && p.rs_ssq ? min(p.M, R) * p.rs_tiles / 4 : 0;
+  auto fetch_rs = [&](int i) {
+    if constexpr (RS) {
+      if (p.rs_direct && int(threadIdx.x) < R && i < my_items) {
+        const int m = (item_of(i) / p.n_blocks) * R + threadIdx.x;
+        rs_next = m < p.M ? p.rs_direct[m] : 0.f;
+      }
+    }
+  };
+  auto rs_issue = [&]() {
+    if constexpr (RS) {
+#pragma unroll
+      for (int i = 0; i < RS_STAGE_FLOATS / 4 / GEMM_THREADS; ++i) {
+        const int c = threadIdx.x + i * GEMM_THREADS;
+        if (c < rs_n4) rs_ld[i] = reinterpret_cast<const f32x4 *>(p.rs_ssq)[c];
+      }
+      fetch_rs(0);
+    }
+  };
+  auto rs_stage_store = [&]() {
+    if constexpr (RS) {
+      if (p.rs_ssq) {
+#pragma unroll
+        for (int i = 0; i < RS_STAGE_FLOATS / 4 / GEMM_THREADS; ++i) {
+          const int c = threadIdx.x + i * GEMM_THREADS;
+          if (c < rs_n4) rs_stage[c] = rs_ld[i];
+        }
+        lds_barrier();
+        const int row = threadIdx.x >> 3;
+        if (row < R) {
+          const int m = row < p.M ? row : 0;
+          const float v = row_rstd8(reinterpret_cast<const float *>(rs_stage) + m * p.rs_tiles, p.rs_tiles,
+                                    p.rs_K, p.rs_eps);
+          if ((threadIdx.x & 7) == 0) rs_row[row] = v;
+        }
+      }
+    }
+  };
+  auto place_rs = [&]() {
+    if constexpr (RS) {
+      if (p.rs_ssq) {
+      } else if (p.rs_direct) {
+        if (int(threadIdx.x) < R) rs_row[threadIdx.x] = rs_next;
+      } else if (rs_first && int(threadIdx.x) < R) {
+        rs_row[threadIdx.x] = 1.f;
+      }
+      rs_first = false;
     }
   };
   // Fold the wavefronts' partial tiles in wavefront order and run the epilogue.
@@ -305,6 +397,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) red[(wave * NF + mt * NB + nb) * 64 + lane] = chain_sum(mt, nb);
       lds_barrier();
+      place_rs();
       if (int(threadIdx.x) < F) {
         const int f = threadIdx.x;
         float v = redf[f];
@@ -333,24 +426,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         lds_barrier();
       }
       if (e_own < NF * 64) tile[e_own] = sum;
+      place_rs();
       lds_barrier();
     }
-    gemm_epilogue<T, MT, NB, EPI>(p, tile, mblk, nblk, best_row);
+    gemm_epilogue<T, MT, NB, EPI>(p, tile, RS ? rs_row : nullptr, mblk, nblk, best_row);
     zero_acc();
+    fetch_rs(++items_done);
   };
 
   zero_acc();
   if constexpr (XRES) {
-    // Activations of this wavefront's chunk, loaded once (one row block).
-    uint4 xr[KC][MT][XS];
-#pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int kt = min(k0 + j, kclamp);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int xp = 0; xp < XS; ++xp) xr[j][mt][xp] = x_load(mt, kt, xp);
-    }
     constexpr int NBAT = KC / U;
     WBatch<NB> wb[2];
     auto issue_w = [&](int item, int b, WBatch<NB> &f) {
@@ -362,7 +447,21 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt) * 1024);
       }
     };
+    rs_issue();
+    __builtin_amdgcn_sched_barrier(0);
     issue_w(item_of(0), 0, wb[0]);
+    // Activations of this wavefront's chunk, loaded once (one row block).
+    uint4 xr[KC][MT][XS];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int kt = min(k0 + j, kclamp);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int xp = 0; xp < XS; ++xp) xr[j][mt][xp] = x_load(mt, kt, xp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    rs_stage_store();
     for (int i = 0; i < my_items; ++i) {
       const int item = item_of(i);
       const int next = item_of(min(i + 1, my_items - 1));
@@ -403,7 +502,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
       for (int u = 0; u < U; ++u) mma_tile(u, b, f.w, f.x[u], mblk);
     };
+    rs_issue();
+    __builtin_amdgcn_sched_barrier(0);
     issue(0, fa);
+    __builtin_amdgcn_sched_barrier(0);
+    rs_stage_store();
     for (int t = 0; t < T_steps; t += 2) {
       issue(min(t + 1, t_last), fb);
       __builtin_amdgcn_sched_barrier(0);
@@ -472,17 +575,16 @@ static hipError_t launch_one(const GemmParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Resident activations when the launch is one row block, MT * XS <= 2 and a
-// wavefront's K chunk is at most 16 tiles; the chunk register array is sized
-// 4, 8 or 16 tiles.
+// Resident activations when gemm_resident_ok holds; the chunk register array
+// is sized 4, 8 or 16 tiles.
 template <typename T, int MT, int NB, int EPI, int XS, bool XROW>
 static hipError_t launch_kc(const GemmParams &p, hipStream_t s) {
   const int per = (p.k_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
   if constexpr (MT * XS <= 2) {
-    if (p.m_blocks == 1) {
+    if (gemm_resident_ok(p.m_blocks, MT, XS, p.k_tiles)) {
       if (per <= 4) return launch_one<T, MT, NB, EPI, XS, XROW, 4>(p, s);
       if (per <= 8) return launch_one<T, MT, NB, EPI, XS, XROW, 8>(p, s);
-      if (per <= 16) return launch_one<T, MT, NB, EPI, XS, XROW, 16>(p, s);
+      return launch_one<T, MT, NB, EPI, XS, XROW, 16>(p, s);
     }
   }
   return launch_one<T, MT, NB, EPI, XS, XROW, 0>(p, s);

@@ -62,7 +62,35 @@ struct GemmParams {
   // EPI_ARGMAX
   int vocab;
   unsigned long long *keys;   // [rows][ARGMAX_SLOTS]
+  // RMSNorm split across two launches.  The producer (EPI_STORE / EPI_RESID)
+  // also writes its output rows y as packed (y * nx_gain) planes (rows
+  // [M, nx_rows) zeroed) and per row and 16-column tile the sum of y^2 to
+  // ssq_out[m * ssq_ld + tile].  The consumer multiplies its output rows by
+  // 1 / sqrt(mean(y^2) + eps): from the tile sums itself (rs_ssq, one row
+  // block) or from per-row values (rs_direct) made by rstd_kernel.
+  char *nx_packed;
+  const char *nx_gain;
+  int nx_kt, nx_planes, nx_rows;
+  size_t nx_plane;
+  float *ssq_out;
+  int ssq_ld;
+  const float *rs_ssq;
+  const float *rs_direct;
+  int rs_tiles, rs_K;
+  float rs_eps;
 };
+
+// Whether a consumer can reduce the RMSNorm tile sums itself: one row block
+// whose rows x tiles fit the 8192-float LDS stage.
+inline bool gemm_inline_rs_ok(int m_blocks, int MT, int hidden) {
+  return m_blocks == 1 && MT * 16 * (hidden / 16) <= 8192;
+}
+
+// Whether a launch keeps its activations resident in registers: one row
+// block, MT * planes <= 2 and a wavefront K chunk of at most 16 tiles.
+inline bool gemm_resident_ok(int m_blocks, int MT, int planes, int k_tiles) {
+  return m_blocks == 1 && MT * planes <= 2 && (k_tiles + 7) / 8 <= 16;
+}
 
 struct ArgmaxFinishParams {
   unsigned long long *keys;
@@ -88,20 +116,20 @@ struct AttnParams {
   size_t xo_plane;
 };
 
-struct NormParams {
-  const float *src;        // fp32 rows [M, H], or nullptr with embed set
-  const char *embed;       // T [V, H] gathered by token
+// Block embedding: gathers the token rows and prepares the first RMSNorm the
+// way a GEMM producer does (fp32 rows, packed rows * gain, tile sums).
+struct EmbedParams {
+  const char *embed;       // T [V, H]
   const int *last_tok;     // [batch]
   int block, mask_id, vocab;
   unsigned *status;
-  float *gathered;         // fp32 copy of the gathered rows (embed mode)
+  float *gathered;         // fp32 [M, H]
   const char *gain;        // T [H]
-  float eps;
   int M, rows_pad, H;
-  char *xpacked;           // packed T output [rows_pad, H]
+  char *xpacked;           // packed T [rows_pad, H] of gathered * gain
   int x_kt, planes;        // planes: 1, or 2 (hi, lo) x_plane bytes apart
   size_t x_plane;
-  float *normed;           // optional fp32 copy of the normed rows
+  float *ssq;              // [M, H / 16] tile sums of squares
 };
 
 // Launchers (return hipError_t of the launch).
@@ -110,7 +138,9 @@ hipError_t launch_argmax_finish(const ArgmaxFinishParams &p, int batch, hipStrea
 hipError_t launch_commit_rows(int *ctx_len, const int *cu_new, int batch, int capacity, hipStream_t s);
 hipError_t launch_attention(int dtype, const AttnParams &p, int batch, hipStream_t s);
 hipError_t launch_attn_merge(int dtype, const AttnParams &p, int batch, hipStream_t s);
-hipError_t launch_norm_pack(int dtype, const NormParams &p, hipStream_t s);
+hipError_t launch_embed(int dtype, const EmbedParams &p, hipStream_t s);
+// rs[m] = 1 / sqrt(mean(x_m^2) + eps) from tile sums ssq[m * tiles + t].
+hipError_t launch_rstd(const float *ssq, int tiles, int K, float eps, int M, float *rs, hipStream_t s);
 hipError_t launch_pack_matrix(int dtype, const void *src, int rows, int cols, void *dst,
                               int dst_tile_offset, int dst_tile_stride, int rot_head_dim,
                               int rot_rows, hipStream_t s);

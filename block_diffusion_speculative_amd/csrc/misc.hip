@@ -5,15 +5,16 @@
 
 namespace dflash {
 
-// One workgroup per row.  Embedding mode gathers the block's token row
-// (slot 0: the last accepted token, other slots: the mask token) and keeps an
-// fp32 copy; then y = x / sqrt(mean(x^2) + eps) * gain is written as packed
-// fragment tiles (and optionally as fp32).  Rows in [M, rows_pad) are zeroed.
+// Block embedding, one workgroup per row: slot 0 of a block takes the last
+// accepted token, the other slots the mask token.  Writes the fp32 rows, the
+// packed rows * gain of the first RMSNorm (rows [M, rows_pad) zeroed) and the
+// per-16-column tile sums of squares, in the order tile_ssq16 fixes: a chunk
+// of E columns is reduced as a balanced tree in column order and the 16 / E
+// chunks of a tile by an xor butterfly.
 template <typename T>
-__global__ __launch_bounds__(256) void norm_pack_kernel(const NormParams p) {
+__global__ __launch_bounds__(256) void embed_kernel(const EmbedParams p) {
   constexpr int E = Ty<T>::E, ES = Ty<T>::SIZE;
   constexpr int MAXC = 8;  // chunks per thread: H <= 256 * 8 * E
-  __shared__ float red[4];
   const int m = blockIdx.x;
   const int nch = p.H / E;
   if (m >= p.M) {
@@ -22,67 +23,50 @@ __global__ __launch_bounds__(256) void norm_pack_kernel(const NormParams p) {
         st16(p.xpacked + pl * p.x_plane + packed_offset<T>(m, c * E, p.x_kt), make_uint4(0, 0, 0, 0));
     return;
   }
-  const char *src_t = nullptr;
-  if (p.embed) {
-    const int s = m / p.block, j = m % p.block;
-    int tok = j == 0 ? p.last_tok[s] : p.mask_id;
-    if (tok < 0 || tok >= p.vocab) {
-      if (threadIdx.x == 0) atomicOr(p.status, DFLASH_STATUS_TOKEN);
-      tok = tok < 0 ? 0 : p.vocab - 1;
-    }
-    src_t = p.embed + size_t(tok) * p.H * ES;
+  const int s = m / p.block, j = m % p.block;
+  int tok = j == 0 ? p.last_tok[s] : p.mask_id;
+  if (tok < 0 || tok >= p.vocab) {
+    if (threadIdx.x == 0) atomicOr(p.status, DFLASH_STATUS_TOKEN);
+    tok = tok < 0 ? 0 : p.vocab - 1;
   }
-  float x[MAXC][E];
-  float ss = 0.f;
+  const char *src = p.embed + size_t(tok) * p.H * ES;
 #pragma unroll
   for (int k = 0; k < MAXC; ++k) {
     const int c = threadIdx.x + 256 * k;
     if (c < nch) {
-      if (src_t) {
-        const uint4 v = ld16(src_t + size_t(c) * 16);
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[k][e] = chunk_get<T>(v, e);
-      } else {
-        const float *r = p.src + size_t(m) * p.H + c * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[k][e] = r[e];
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) ss += x[k][e] * x[k][e];
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
-  const float r = 1.0f / sqrtf(tot / float(p.H) + p.eps);
-#pragma unroll
-  for (int k = 0; k < MAXC; ++k) {
-    const int c = threadIdx.x + 256 * k;
-    if (c < nch) {
+      const uint4 v = ld16(src + size_t(c) * 16);
       const uint4 gv = ld16(p.gain + size_t(c) * 16);
-      float y[E], yh[E], yl[E];
+      float x[E], sq[E], yh[E], yl[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        y[e] = x[k][e] * r * chunk_get<T>(gv, e);
-        split2<T>(y[e], yh[e], yl[e]);
+        x[e] = chunk_get<T>(v, e);
+        sq[e] = __fmul_rn(x[e], x[e]);
+        split2<T>(x[e] * chunk_get<T>(gv, e), yh[e], yl[e]);
       }
       char *dst = p.xpacked + packed_offset<T>(m, c * E, p.x_kt);
       st16(dst, chunk_pack<T>(yh));
       if (p.planes > 1) st16(dst + p.x_plane, chunk_pack<T>(yl));
-      if (p.gathered) {
-        float *gd = p.gathered + size_t(m) * p.H + c * E;
+      float *gd = p.gathered + size_t(m) * p.H + c * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) gd[e] = x[k][e];
-      }
-      if (p.normed) {
-        float *nd = p.normed + size_t(m) * p.H + c * E;
+      for (int e = 0; e < E; ++e) gd[e] = x[e];
 #pragma unroll
-        for (int e = 0; e < E; ++e) nd[e] = y[e];
-      }
+      for (int w = 1; w < E; w <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; e += 2 * w) sq[e] = sq[e] + sq[e + w];
+      float t = sq[0];
+#pragma unroll
+      for (int w = 1; w < 16 / E; w <<= 1) t += __shfl_xor(t, w, 64);
+      if ((c & (16 / E - 1)) == 0) p.ssq[size_t(m) * (p.H / 16) + c / (16 / E)] = t;
     }
   }
+}
+
+// rs[m] = 1 / sqrt(mean(x_m^2) + eps) from the tile sums (row_rstd8 order).
+__global__ __launch_bounds__(256) void rstd_kernel(const float *ssq, int tiles, int K, float eps, int M, float *rs) {
+  const int m = blockIdx.x * 32 + (threadIdx.x >> 3);
+  if (m >= M) return;  // whole 8-lane groups leave together
+  const float v = row_rstd8(ssq + size_t(m) * tiles, tiles, K, eps);
+  if ((threadIdx.x & 7) == 0) rs[m] = v;
 }
 
 // Pack a row-major [rows, cols] matrix into fragment tiles.  Destination
@@ -175,11 +159,14 @@ static int grid_for(long long work) {
   return int(g);
 }
 
-hipError_t launch_norm_pack(int dtype, const NormParams &p, hipStream_t s) {
-  if (dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(norm_pack_kernel<bf16_t>, dim3(p.rows_pad), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(norm_pack_kernel<float>, dim3(p.rows_pad), dim3(256), 0, s, p);
+hipError_t launch_embed(int dtype, const EmbedParams &p, hipStream_t s) {
+  if (dtype == DFLASH_BF16) hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(p.rows_pad), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(embed_kernel<float>, dim3(p.rows_pad), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rstd(const float *ssq, int tiles, int K, float eps, int M, float *rs, hipStream_t s) {
+  hipLaunchKernelGGL(rstd_kernel, dim3((M + 31) / 32), dim3(256), 0, s, ssq, tiles, K, eps, M, rs);
   return hipGetLastError();
 }
 

@@ -190,21 +190,20 @@ size_t dflash_workspace_bytes(const dflash_dims *dims, int32_t max_batch, int32_
 int dflash_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Where the last call of a given kind left an intermediate, for checks:
- *   DFLASH_VIEW_FUSED     fp32 [rows, H]: fused, normed injected context c
+ *   DFLASH_VIEW_FUSED     fp32 [rows, H]: fused target features W_fc f of
+ *                         the injected rows, before their RMSNorm
  *   DFLASH_VIEW_HIDDEN    fp32 [batch*B, H]: residual after layer `layer`
  *                         (layer = -1: the block embeddings)
  *   DFLASH_VIEW_MID       fp32 [batch*B, H]: residual after the attention
  *                         half of layer `layer`
  *   DFLASH_VIEW_ATTN      fp32 [batch*B, n_q*d]: attention output of layer
  *                         `layer`, before the output projection
- *   DFLASH_VIEW_FINAL     fp32 [batch*B, H]: final normed hidden
  * `count` is rows for FUSED and batch otherwise.  Offsets are from ws. */
 enum {
   DFLASH_VIEW_FUSED = 0,
   DFLASH_VIEW_HIDDEN = 1,
   DFLASH_VIEW_MID = 2,
-  DFLASH_VIEW_ATTN = 3,
-  DFLASH_VIEW_FINAL = 4
+  DFLASH_VIEW_ATTN = 3
 };
 int dflash_workspace_view(const dflash_dims *dims, int32_t what, int32_t count, int32_t layer,
                           size_t *offset, size_t *bytes);

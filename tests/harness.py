@@ -207,7 +207,6 @@ class GpuRunner:
             out["mid"].append(self.drafter.view(_lib.VIEW_MID, b, l).reshape(M, -1).cpu().numpy())
         for l in range(-1, d.n_layers):
             out["hidden"].append(self.drafter.view(_lib.VIEW_HIDDEN, b, l).reshape(M, -1).cpu().numpy())
-        out["final"] = self.drafter.view(_lib.VIEW_FINAL, b, 0).reshape(M, -1).cpu().numpy()
         return out
 
     def kv_plain(self):

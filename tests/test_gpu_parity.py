@@ -38,12 +38,13 @@ def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=Tr
     ctx_after = case.ctx + np.asarray(new_rows, dtype=np.int32)
     assert np.array_equal(gpu.ctx_len()[:case.batch], ctx_after)
     cu = np.concatenate([[0], np.cumsum(new_rows)])
+    # the fused features before their RMSNorm, normalised here in fp64 and
+    # compared with the oracle's fused context rows
     for i, s in enumerate(seqs):
         rows = slice(int(cu[s]), int(cu[s + 1]))
         if rows.stop > rows.start:
-            rep["errors"].setdefault("fused", 0.0)
-            rep["errors"]["fused"] = max(rep["errors"]["fused"],
-                                         Hn.rel_err_rows(views["fused"][rows], ref["fused"][i]))
+            c = O.rms_norm(views["fused"][rows].astype(np.float64), case.weights.fc_norm, d.rms_eps)
+            rep["errors"]["fused"] = max(rep["errors"].get("fused", 0.0), Hn.rel_err_rows(c, ref["fused"][i]))
     if check_cache:
         kg, vg = gpu.kv_plain()
         for i, s in enumerate(seqs):
@@ -62,7 +63,6 @@ def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=Tr
         rep["errors"][f"mid{l}"] = Hn.rel_err_rows(views["mid"][l][rows], dr["mid"][l])
         rep["errors"][f"hidden{l}"] = Hn.rel_err_rows(views["hidden"][l + 1][rows], dr["hidden"][l + 1])
     rep["errors"]["embed"] = Hn.rel_err_rows(views["hidden"][0][rows], dr["hidden"][0])
-    rep["errors"]["final"] = Hn.rel_err_rows(views["final"][rows], dr["final"])
     print({k: f"{v:.2e}" for k, v in rep["errors"].items()}, flush=True)
     for k, v in rep["errors"].items():
         assert v <= Hn.REL_TOL, (k, v, rep)
@@ -168,10 +168,14 @@ def test_bad_token_sets_status():
     assert g.drafter.read_status() & 2
 
 
-def test_deterministic_repeat():
-    case = Hn.build_case(SMALL_BF16, 2, [40, 90], seed=8)
+@pytest.mark.parametrize("batch", [1, 2])
+def test_deterministic_repeat(batch):
+    """Same inputs, same bits, whatever the workspace held before (batch 1:
+    the consumers reduce the norm statistics themselves; batch 2 as well, with
+    two row tiles)."""
+    case = Hn.build_case(SMALL_BF16, batch, [40, 90][:batch], seed=8)
     g = Hn.GpuRunner(case)
-    last = I.last_tokens(SMALL_BF16, 8, 0, 2)
+    last = I.last_tokens(SMALL_BF16, 8, 0, batch)
     t1 = g.draft(last)
     v1 = g.views()
     g.drafter.ws.fill_(0xFF)   # poison scratch except the counters below
@@ -182,7 +186,6 @@ def test_deterministic_repeat():
     for k in ("attn", "mid", "hidden"):
         for a, b in zip(v1[k], v2[k]):
             assert np.array_equal(a, b)
-    assert np.array_equal(v1["final"], v2["final"])
 
 
 @pytest.mark.slow
