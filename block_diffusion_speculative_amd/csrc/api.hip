@@ -55,9 +55,23 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int nb) {
   return g;
 }
 
+// Context splits of the block attention: about half a workgroup per compute
+// unit over all (sequence, KV head) pairs, at most 16 (more splits cost the
+// merge more than they save here).
 int attn_splits(const dflash_dims *d, int batch) {
   const int s = 256 / std::max(1, batch * d->n_kv_heads);
   return std::min(16, std::max(1, s));
+}
+
+// Workgroups per (sequence, KV head, split) sharing the query group: the
+// largest divisor of the group that keeps the grid within 256 workgroups.
+int attn_head_split(const dflash_dims *d, int batch, int splits) {
+  const int group = d->n_q_heads / d->n_kv_heads;
+  const int wgs = batch * d->n_kv_heads * splits;
+  int best = 1;
+  for (int hs = 1; hs <= group; ++hs)
+    if (group % hs == 0 && wgs * hs <= 256) best = hs;
+  return best;
 }
 
 struct Bump {
@@ -574,6 +588,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     a.head_dim = hd;
     a.group = d->n_q_heads / d->n_kv_heads;
     a.splits = L.S;
+    a.head_split = attn_head_split(d, batch, L.S);
     a.capacity = kv->capacity;
     a.scale_log2 = 1.4426950408889634f / sqrtf(float(hd));
     a.attn_out = reinterpret_cast<float *>(wsb + L.attn + size_t(L.M) * NQD * 4 * l);
@@ -581,8 +596,10 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     a.xo_kt = NQD / kt;
     e = launch_attention(d->dtype, a, batch, stream);
     if (e != hipSuccess) return hip_fail(e, "draft attention");
-    e = launch_attn_merge(d->dtype, a, batch, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft attention merge");
+    if (a.splits > 1) {
+      e = launch_attn_merge(d->dtype, a, batch, stream);
+      if (e != hipSuccess) return hip_fail(e, "draft attention merge");
+    }
 
     GemmParams o{};
     fill_gemm(o, L.o);

@@ -4,15 +4,23 @@
 // Research Report", "Why DFlash beats EAGLE-3" item 3; "Term: DFlash
 // speculative decoding", "DFlash: architecture and workflow").
 //
-// One workgroup per (sequence, KV head, context split); its wavefronts are the
-// query heads of that KV head's group, so each K/V step is read from HBM once
-// and staged in LDS for the whole group.  A step is KT positions (32 for
-// bf16): S^T = K Q^T on MFMA gives each lane 4 positions x 1 query per
-// 16-position tile, the online softmax runs in registers with row statistics
-// exchanged by lane shuffles, and O^T += V^T P^T consumes the probabilities
-// straight from the S^T registers (the V cache layout stores positions in
-// that register order).  Each split writes (O, running max, running sum) and
-// a merge kernel combines the splits with a log-sum-exp weighting.
+// One workgroup per (sequence, KV head, share of its query heads, context
+// split).  Its wavefronts are the workgroup's query heads times SUB
+// sub-splits (at most 16 wavefronts).  A step is KT positions (32 for bf16);
+// round r stages the SUB steps st0 + r * SUB + ss in LDS, where wavefront
+// (head, ss) takes step ss.  The K/V tiles go straight from global memory to
+// LDS (global_load_lds_dwordx4, 1 KiB per wavefront instruction), two rounds
+// in flight, so a short split (the batch-1 case) has all of its loads out at
+// once.  Per step: S^T = K Q^T on MFMA gives each lane 4 positions x 1 query
+// per 16-position tile, the online softmax runs in registers with row
+// statistics exchanged by lane shuffles, and O^T += V^T P^T consumes the
+// probabilities straight from the S^T registers (the V cache layout stores
+// positions in that register order).  q enters as hi + lo planes when XS ==
+// 2; P as one plane (its rounding error, about 0.2% of the output, averages
+// over the keys).  The sub-splits are then merged in LDS with log-sum-exp
+// weights, every wavefront taking a slice of its head's channels; a single
+// split writes the output itself, several write (O, running max, running
+// sum) records that attn_merge_kernel combines.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,22 +49,81 @@ template <> __device__ inline uint4 mask_v_chunk<bf16_t>(uint4 v, int g, int nva
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <typename T, int HD, int XS>
-__global__ __launch_bounds__(1024) void attn_kernel(const AttnParams p) {
+constexpr int ATTN_MAX_WAVES = 16;
+constexpr int ATTN_MAX_SUB = 4;
+constexpr int ATTN_MAX_SPLITS = 32;
+
+// Sub-splits per workgroup holding `heads` query heads.
+__host__ __device__ inline int attn_sub(int heads) {
+  const int s = ATTN_MAX_WAVES / heads;
+  return s < 1 ? 1 : (s > ATTN_MAX_SUB ? ATTN_MAX_SUB : s);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding (direct-to-LDS loads included); other counters untouched.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// RC: 1 KiB tiles each wavefront loads per round (a compile-time count, so the
+// wait for the older of two rounds in flight is an immediate).  NW: most
+// wavefronts per workgroup (8 leaves each 256 VGPRs, 16 leaves 128).
+template <typename T, int HD, int XS, int RC, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   constexpr int KT = Ty<T>::KT, ES = Ty<T>::SIZE;
   constexpr int DT = HD / KT, DV = HD / 16, KTT = KT / 16;
-  constexpr int KB = KTT * DT * 1024, VB = DV * 1024;
-  constexpr int REC = DV * 256 + 32;
-  __shared__ uint4 lds[(KB + VB) / 16];
+  constexpr int KB = KTT * DT * 1024, VB = DV * 1024, SB = KB + VB;
+  constexpr int TPS = SB / 1024;                    // tiles per step
+  constexpr int REC = DV * 256 + 32;                // floats of one merge record
+  constexpr int RING = 2 * ATTN_MAX_SUB * SB / 16;  // uint4 of two rounds
+  constexpr int MREC = ATTN_MAX_WAVES * REC / 4;    // uint4 of one record per wavefront
+  __shared__ uint4 lds[RING > MREC ? RING : MREC];
 
-  const int z = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int z = blockIdx.x, s = blockIdx.z;
+  const int g = blockIdx.y / p.head_split, hs = blockIdx.y % p.head_split;
+  const int gw = p.group / p.head_split;            // query heads of this workgroup
+  const int waves = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = g * p.group + wave;
+  const int SUB = attn_sub(gw);
+  const int hl = wave % gw, ss = wave / gw;
+  const int h = g * p.group + hs * gw + hl;
   const int C = min(p.ctx_len[s], p.capacity);
   const int n_ctx = (C + KT - 1) / KT;
   const int total = n_ctx + 1;
   const int per = (total + p.splits - 1) / p.splits;
   const int st0 = min(z * per, total), st1 = min(st0 + per, total);
+  const int rounds = (st1 - st0 + SUB - 1) / SUB;
+  const int round_tiles = SUB * TPS;
+
+  const size_t region = size_t(p.capacity) * HD * ES;
+  const char *kreg = p.kcache + (size_t(s) * p.n_kv + g) * region;
+  const char *vreg = p.vcache + (size_t(s) * p.n_kv + g) * region;
+  const char *kbk = p.kblk + (size_t(s) * p.n_kv + g) * KB;
+  const char *vbk = p.vblk + (size_t(s) * p.n_kv + g) * VB;
+
+  // Round r goes to ring slot r % 2.  Wavefront w loads tiles w, w + waves, ...
+  // of the round; a tile past the round or of a step past st1 reloads a valid
+  // tile into its own slot position (never read), so every wavefront issues
+  // exactly RC loads.
+  auto issue_round = [&](int r) {
+    uint4 *slot = lds + (r & 1) * (ATTN_MAX_SUB * SB / 16);
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      int j = wave + i * waves;
+      j = j < round_tiles ? j : round_tiles - 1;
+      const int st = st0 + r * SUB + j / TPS, tt = j % TPS;
+      const char *src;
+      if (st >= st1) src = kbk;
+      else if (tt < KB / 1024) src = (st == n_ctx ? kbk : kreg + size_t(st) * KB) + tt * 1024;
+      else src = (st == n_ctx ? vbk : vreg + size_t(st) * VB) + (tt - KB / 1024) * 1024;
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)(slot + j * 64), 16, 0, 0);
+    }
+  };
 
   uint4 qf[XS][DT];
   {
@@ -72,33 +139,12 @@ __global__ __launch_bounds__(1024) void attn_kernel(const AttnParams p) {
   f32x4 o[DV];
 #pragma unroll
   for (int i = 0; i < DV; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const size_t region = size_t(p.capacity) * HD * ES;
-  const char *kreg = p.kcache + (size_t(s) * p.n_kv + g) * region;
-  const char *vreg = p.vcache + (size_t(s) * p.n_kv + g) * region;
-  const char *kbk = p.kblk + (size_t(s) * p.n_kv + g) * KB;
-  const char *vbk = p.vblk + (size_t(s) * p.n_kv + g) * VB;
   const int gq = lane >> 4;
 
-  for (int st = st0; st < st1; ++st) {
+  auto compute = [&](int st, const uint4 *kl) {
     const bool blk = st == n_ctx;
-    const char *ksrc = blk ? kbk : kreg + size_t(st) * KB;
-    const char *vsrc = blk ? vbk : vreg + size_t(st) * VB;
     const int nvalid = blk ? p.block : min(KT, C - st * KT);
-    __syncthreads();
-    for (int c = threadIdx.x; c < (KB + VB) / 16; c += blockDim.x) {
-      uint4 v;
-      if (c < KB / 16) {
-        v = ld16(ksrc + size_t(c) * 16);
-      } else {
-        const int cv = c - KB / 16;
-        v = ld16(vsrc + size_t(cv) * 16);
-        if (nvalid < KT) v = mask_v_chunk<T>(v, (cv & 63) >> 4, nvalid);
-      }
-      lds[c] = v;
-    }
-    __syncthreads();
-
+    const uint4 *vl = kl + KB / 16;
     f32x4 sacc[KTT];
 #pragma unroll
     for (int t = 0; t < KTT; ++t) {
@@ -106,7 +152,7 @@ __global__ __launch_bounds__(1024) void attn_kernel(const AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int xp = 0; xp < XS; ++xp) sacc[t] = mma<T>(sacc[t], lds[(t * DT + dt) * 64 + lane], qf[xp][dt]);
+        for (int xp = 0; xp < XS; ++xp) sacc[t] = mma<T>(sacc[t], kl[(t * DT + dt) * 64 + lane], qf[xp][dt]);
     }
     float sv[KTT * 4];
     float mx = -INFINITY;
@@ -123,64 +169,126 @@ __global__ __launch_bounds__(1024) void attn_kernel(const AttnParams p) {
     mx = warp_max_xor(mx, 32);
     const float m_new = fmaxf(m_run, mx);
     const float corr = exp2f(m_run - m_new);
-    // Probabilities: with XS == 2 they enter the MFMA as hi + lo planes and
-    // the row sum uses the fp32 values; with XS == 1 both use the rounded ones.
-    float ph[KTT * 4], pl[KTT * 4];
+    // Probabilities rounded to T; the row sum uses the rounded values, so the
+    // weights of the output stay normalised.
+    float ph[KTT * 4];
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < KTT * 4; ++e) {
-      const float pr = exp2f(sv[e] - m_new);
-      if constexpr (XS == 2) {
-        split2<T>(pr, ph[e], pl[e]);
-        ps += pr;
-      } else {
-        ph[e] = round_to<T>(pr);
-        ps += ph[e];
-      }
+      ph[e] = round_to<T>(exp2f(sv[e] - m_new));
+      ps += ph[e];
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     l_run = l_run * corr + ps;
     const uint4 pf = chunk_pack<T>(ph);
-    uint4 pfl = make_uint4(0, 0, 0, 0);
-    if constexpr (XS == 2) pfl = chunk_pack<T>(pl);
 #pragma unroll
     for (int dv = 0; dv < DV; ++dv) {
       o[dv] *= corr;
-      const uint4 vf = lds[KB / 16 + dv * 64 + lane];
+      uint4 vf = vl[dv * 64 + lane];
+      // positions past nvalid hold stale data: zero them (P is 0 there, but
+      // 0 * NaN would not be)
+      if (nvalid < KT) vf = mask_v_chunk<T>(vf, gq, nvalid);
       o[dv] = mma<T>(o[dv], vf, pf);
-      if constexpr (XS == 2) o[dv] = mma<T>(o[dv], vf, pfl);
     }
     m_run = m_new;
+  };
+
+  if (rounds > 0) issue_round(0);
+  if (rounds > 1) issue_round(1);
+  for (int r = 0; r < rounds; ++r) {
+    if (r + 1 < rounds) wait_vmcnt<RC>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    const int st = st0 + r * SUB + ss;
+    if (st < st1) compute(st, lds + (r & 1) * (ATTN_MAX_SUB * SB / 16) + ss * (SB / 16));
+    lds_barrier();
+    if (r + 2 < rounds) issue_round(r + 2);
   }
 
-  float *rec = p.part + ((size_t(s) * p.n_q + h) * p.splits + z) * REC;
+  // Merge the sub-splits: every wavefront leaves its record in LDS, then
+  // wavefront (head, ss) combines channel tiles ss, ss + SUB, ... of its head
+  // over the SUB records (log-sum-exp weights) and writes them out.
+  float *recs = reinterpret_cast<float *>(lds);
+  {
+    float *mine = recs + size_t(wave) * REC;
 #pragma unroll
-  for (int dv = 0; dv < DV; ++dv) reinterpret_cast<f32x4 *>(rec)[dv * 64 + lane] = o[dv];
-  if (lane < 16) {
-    rec[DV * 256 + lane] = m_run;
-    rec[DV * 256 + 16 + lane] = l_run;
+    for (int dv = 0; dv < DV; ++dv) reinterpret_cast<f32x4 *>(mine)[dv * 64 + lane] = o[dv];
+    if (lane < 16) {
+      mine[DV * 256 + lane] = m_run;
+      mine[DV * 256 + 16 + lane] = l_run;
+    }
+  }
+  lds_barrier();
+  const int q = lane & 15;
+  float M = -1e30f;
+  for (int j = 0; j < SUB; ++j) M = fmaxf(M, recs[size_t(j * gw + hl) * REC + DV * 256 + q]);
+  float L = 0.f;
+  for (int j = 0; j < SUB; ++j) {
+    const float *r = recs + size_t(j * gw + hl) * REC;
+    L += exp2f(r[DV * 256 + q] - M) * r[DV * 256 + 16 + q];
+  }
+  const bool final_out = p.splits == 1;
+  const float inv = 1.0f / L;
+  float *rec = p.part + ((size_t(s) * p.n_q + h) * p.splits + z) * REC;
+  for (int dv = ss; dv < DV; dv += SUB) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < SUB; ++j) {
+      const float *r = recs + size_t(j * gw + hl) * REC;
+      acc += exp2f(r[DV * 256 + q] - M) * reinterpret_cast<const f32x4 *>(r)[dv * 64 + lane];
+    }
+    if (final_out) {
+      if (q < p.block) {
+        const int row = s * p.block + q;
+        const int nqd = p.n_q * HD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = h * HD + dv * 16 + 4 * (lane >> 4) + i;
+          p.attn_out[size_t(row) * nqd + col] = acc[i] * inv;
+          store_split<T>(p.xo + packed_offset<T>(row, col, p.xo_kt), p.xo_plane, p.xs, acc[i] * inv);
+        }
+      }
+    } else {
+      reinterpret_cast<f32x4 *>(rec)[dv * 64 + lane] = acc;
+    }
+  }
+  if (!final_out && ss == 0 && lane < 16) {
+    rec[DV * 256 + lane] = M;
+    rec[DV * 256 + 16 + lane] = L;
   }
 }
 
-// Combine the splits of one (sequence, query head, 16-channel tile).
-template <typename T, int HD>
+// Combine the splits of one (sequence, query head, 16-channel tile): lane
+// takes one O^T chunk of every split; all loads are issued before any is used.
+template <typename T, int HD, int ZMAX>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
   constexpr int DV = HD / 16;
   constexpr int REC = DV * 256 + 32;
   const int dv = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, q = lane & 15;
   const float *base = p.part + (size_t(s) * p.n_q + h) * p.splits * REC;
+  float mz[ZMAX], lz[ZMAX];
+  f32x4 oz[ZMAX];
+#pragma unroll
+  for (int z = 0; z < ZMAX; ++z) {
+    const float *r = base + size_t(min(z, p.splits - 1)) * REC;
+    mz[z] = r[DV * 256 + q];
+    lz[z] = r[DV * 256 + 16 + q];
+    oz[z] = reinterpret_cast<const f32x4 *>(r)[dv * 64 + lane];
+  }
   float M = -1e30f;
-  for (int z = 0; z < p.splits; ++z) M = fmaxf(M, base[size_t(z) * REC + DV * 256 + q]);
+#pragma unroll
+  for (int z = 0; z < ZMAX; ++z)
+    if (z < p.splits) M = fmaxf(M, mz[z]);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int z = 0; z < p.splits; ++z) {
-    const float *r = base + size_t(z) * REC;
-    const float w = exp2f(r[DV * 256 + q] - M);
-    L += w * r[DV * 256 + 16 + q];
-    const f32x4 ov = reinterpret_cast<const f32x4 *>(r)[dv * 64 + lane];
-    acc += w * ov;
+#pragma unroll
+  for (int z = 0; z < ZMAX; ++z) {
+    if (z < p.splits) {
+      const float w = exp2f(mz[z] - M);
+      L += w * lz[z];
+      acc += w * oz[z];
+    }
   }
   if (q >= p.block) return;
   const float inv = 1.0f / L;
@@ -195,13 +303,35 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
   }
 }
 
-template <typename T, int XS>
-static hipError_t launch_attn_xs(const AttnParams &p, int batch, hipStream_t s) {
-  const dim3 grid(p.splits, p.n_kv, batch), block(64 * p.group);
-  if (p.head_dim == 128) hipLaunchKernelGGL((attn_kernel<T, 128, XS>), grid, block, 0, s, p);
-  else if (p.head_dim == 64) hipLaunchKernelGGL((attn_kernel<T, 64, XS>), grid, block, 0, s, p);
+template <typename T, int HD, int XS, int NW>
+static hipError_t launch_attn_nw(const AttnParams &p, int batch, int rc, int threads, hipStream_t s) {
+  const dim3 grid(p.splits, p.n_kv * p.head_split, batch), block(threads);
+  if (rc <= 2) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 2, NW>), grid, block, 0, s, p);
+  else if (rc <= 4) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 4, NW>), grid, block, 0, s, p);
+  else if (rc <= 8) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 8, NW>), grid, block, 0, s, p);
+  else if (rc <= 16) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 16, NW>), grid, block, 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <typename T, int HD, int XS>
+static hipError_t launch_attn_rc(const AttnParams &p, int batch, hipStream_t s) {
+  constexpr int SB = (Ty<T>::KT / 16) * (HD / Ty<T>::KT) * 1024 + (HD / 16) * 1024;
+  const int sub = attn_sub(p.group / p.head_split);
+  const int waves = p.group / p.head_split * sub;
+  const int threads = 64 * waves;
+  const int rc = (sub * (SB / 1024) + waves - 1) / waves;  // tiles per wavefront per round
+  if (waves <= 8) return launch_attn_nw<T, HD, XS, 8>(p, batch, rc, threads, s);
+  return launch_attn_nw<T, HD, XS, 16>(p, batch, rc, threads, s);
+}
+
+template <typename T, int XS>
+static hipError_t launch_attn_xs(const AttnParams &p, int batch, hipStream_t s) {
+  if (p.group < 1 || p.group > ATTN_MAX_WAVES || p.splits < 1 || p.splits > ATTN_MAX_SPLITS) return hipErrorInvalidValue;
+  if (p.head_split < 1 || p.group % p.head_split) return hipErrorInvalidValue;
+  if (p.head_dim == 128) return launch_attn_rc<T, 128, XS>(p, batch, s);
+  if (p.head_dim == 64) return launch_attn_rc<T, 64, XS>(p, batch, s);
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
@@ -215,9 +345,16 @@ static hipError_t launch_attn_t(const AttnParams &p, int batch, hipStream_t s) {
 template <typename T>
 static hipError_t launch_merge_t(const AttnParams &p, int batch, hipStream_t s) {
   const dim3 grid(p.head_dim / 16, p.n_q, batch), block(64);
-  if (p.head_dim == 128) hipLaunchKernelGGL((attn_merge_kernel<T, 128>), grid, block, 0, s, p);
-  else if (p.head_dim == 64) hipLaunchKernelGGL((attn_merge_kernel<T, 64>), grid, block, 0, s, p);
-  else return hipErrorInvalidValue;
+  if (p.splits > ATTN_MAX_SPLITS) return hipErrorInvalidValue;
+  if (p.head_dim == 128) {
+    if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 128, 16>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, 128, ATTN_MAX_SPLITS>), grid, block, 0, s, p);
+  } else if (p.head_dim == 64) {
+    if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 64, 16>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, 64, ATTN_MAX_SPLITS>), grid, block, 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -108,6 +108,7 @@ struct AttnParams {
   const int *ctx_len;
   float *part;                      // [batch][n_q][splits] partial records
   int block, n_q, n_kv, head_dim, group, splits, capacity;
+  int head_split;                   // workgroups sharing one KV head's query group
   float scale_log2;                 // log2(e) / sqrt(head_dim)
   // merge
   float *attn_out;                  // fp32 [batch*block, n_q*d]
