@@ -28,6 +28,7 @@ VIEW_FUSED, VIEW_HIDDEN, VIEW_MID, VIEW_ATTN = range(4)
 
 EXPORTED = [
     "dflash_packed_bytes", "dflash_pack_matrix", "dflash_pack_qkv", "dflash_pack_gate_up",
+    "dflash_pack_lm_head",
     "dflash_kv_bytes", "dflash_kv_import", "dflash_kv_export",
     "dflash_workspace_bytes", "dflash_workspace_init", "dflash_workspace_view",
     "dflash_inject_kv", "dflash_draft_forward", "dflash_verify_accept",
@@ -83,6 +84,7 @@ def load() -> ctypes.CDLL:
         "dflash_pack_matrix": (c_int32, [c_int32, P, c_int32, c_int32, P, P]),
         "dflash_pack_qkv": (c_int32, [POINTER(Dims), P, P, P, P, P]),
         "dflash_pack_gate_up": (c_int32, [POINTER(Dims), P, P, P, P]),
+        "dflash_pack_lm_head": (c_int32, [c_int32, P, c_int32, c_int32, P, P]),
         "dflash_kv_bytes": (c_size_t, [POINTER(Dims), c_int32, c_int32]),
         "dflash_kv_import": (c_int32, [POINTER(Dims), POINTER(KV), P, P, P]),
         "dflash_kv_export": (c_int32, [POINTER(Dims), POINTER(KV), P, P, P]),

@@ -84,8 +84,12 @@ struct Bump {
   }
 };
 
-// bf16 activations produced inside the step travel as hi + lo planes.
+// bf16 activations produced inside the step travel as hi + lo planes, except
+// the SwiGLU output, which feeds only the down projection: one plane there
+// (its rounding adds about 0.1% to the MLP output) lets the down projection
+// keep its whole activation chunk in registers.
 int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
+constexpr int MLP_ACT_PLANES = 1;
 
 struct DraftLayout {
   size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, end;
@@ -122,7 +126,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.pq = size_t(batch) * d->n_q_heads * (hd / kt) * 1024;
   L.xa = b.take(L.pa * L.xs);
   L.xo = b.take(L.po * L.xs);
-  L.xact = b.take(L.pact * L.xs);
+  L.xact = b.take(L.pact * MLP_ACT_PLANES);
   L.qbuf = b.take(L.pq * L.xs);
   L.kblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
@@ -335,8 +339,18 @@ int dflash_pack_matrix(int32_t dtype, const void *src, int32_t rows, int32_t col
   TRY(check_ptr(src, "src"));
   TRY(check_ptr(dst, "dst"));
   if ((size_t(cols) * esize_of(dtype)) % 16) return fail(DFLASH_ERR_ALIGN, "row pitch must be a multiple of 16 bytes");
-  const hipError_t e = launch_pack_matrix(dtype, src, rows, cols, dst, 0, 1, 1, 0, stream);
+  const hipError_t e = launch_pack_matrix(dtype, src, rows, cols, dst, 0, 1, 1, 0, false, stream);
   return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_matrix");
+}
+
+int dflash_pack_lm_head(int32_t dtype, const void *src, int32_t vocab, int32_t hidden, void *dst, hipStream_t stream) {
+  if (dtype != DFLASH_BF16 && dtype != DFLASH_F32) return fail(DFLASH_ERR_DTYPE, "bad dtype");
+  if (vocab <= 0 || vocab % 32 || hidden <= 0) return fail(DFLASH_ERR_SHAPE, "vocab must be a positive multiple of 32");
+  TRY(check_ptr(src, "src"));
+  TRY(check_ptr(dst, "dst"));
+  if ((size_t(hidden) * esize_of(dtype)) % 16) return fail(DFLASH_ERR_ALIGN, "row pitch must be a multiple of 16 bytes");
+  const hipError_t e = launch_pack_matrix(dtype, src, vocab, hidden, dst, 0, 1, 1, 0, true, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_lm_head");
 }
 
 int dflash_pack_qkv(const dflash_dims *d, const void *wq, const void *wk, const void *wv, void *dst, hipStream_t stream) {
@@ -347,9 +361,9 @@ int dflash_pack_qkv(const dflash_dims *d, const void *wq, const void *wk, const 
   TRY(check_ptr(dst, "dst"));
   const int hd = d->head_dim, H = d->hidden;
   const int qr = d->n_q_heads * hd, kr = d->n_kv_heads * hd;
-  hipError_t e = launch_pack_matrix(d->dtype, wq, qr, H, dst, 0, 1, hd, qr, stream);
-  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wk, kr, H, dst, qr / 16, 1, hd, kr, stream);
-  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wv, kr, H, dst, (qr + kr) / 16, 1, hd, 0, stream);
+  hipError_t e = launch_pack_matrix(d->dtype, wq, qr, H, dst, 0, 1, hd, qr, false, stream);
+  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wk, kr, H, dst, qr / 16, 1, hd, kr, false, stream);
+  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wv, kr, H, dst, (qr + kr) / 16, 1, hd, 0, false, stream);
   return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_qkv");
 }
 
@@ -359,8 +373,8 @@ int dflash_pack_gate_up(const dflash_dims *d, const void *wg, const void *wu, vo
   TRY(check_ptr(wu, "w_up"));
   TRY(check_ptr(dst, "dst"));
   const int I = d->intermediate, H = d->hidden;
-  hipError_t e = launch_pack_matrix(d->dtype, wg, I, H, dst, 0, 2, 1, 0, stream);
-  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wu, I, H, dst, 1, 2, 1, 0, stream);
+  hipError_t e = launch_pack_matrix(d->dtype, wg, I, H, dst, 0, 2, 1, 0, true, stream);
+  if (e == hipSuccess) e = launch_pack_matrix(d->dtype, wu, I, H, dst, 1, 2, 1, 0, true, stream);
   return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack_gate_up");
 }
 
@@ -620,7 +634,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     gu.x = wsb + L.xa;
     gu.xs = L.xs;
     gu.x_plane = L.pa;
-    gu.out_planes = L.xs;
+    gu.out_planes = MLP_ACT_PLANES;
     gu.out_plane = L.pact;
     gu.out_packed = wsb + L.xact;
     gu.out_kt = I / kt;
@@ -632,7 +646,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     fill_gemm(dn, L.down);
     dn.w_seg[0] = static_cast<const char *>(lw.w_down);
     dn.x = wsb + L.xact;
-    dn.xs = L.xs;
+    dn.xs = MLP_ACT_PLANES;
     dn.x_plane = L.pact;
     dn.out_f32 = h_out;
     dn.resid = h_mid;

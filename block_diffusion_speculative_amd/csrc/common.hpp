@@ -118,6 +118,22 @@ __device__ inline uint4 ld16_stream(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer resource word 3 for gfx9-family parts (32-bit data format), and
+// a 16-byte streaming (non-temporal) load through a buffer resource: byte
+// voff (per lane) + soff (uniform) from the resource base.
+constexpr int BUF_DWORD3 = 0x00020000;
+// A pointer every lane holds the same value of, moved to scalar registers so
+// that a buffer resource built from it needs no per-lane loop.
+__device__ inline const char *uniform_ptr(const char *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v)), hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char *>((uint64_t(hi) << 32) | lo);
+}
+__device__ inline uint4 ld16_buf_stream(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2 /* nt */);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------------ layouts
 
 // Byte offset of element (row, col) in a packed matrix whose rows hold

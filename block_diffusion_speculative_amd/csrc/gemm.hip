@@ -58,21 +58,24 @@ __device__ inline int key_index(unsigned long long k) {
 
 // Every GEMM workgroup has 8 wavefronts (two per SIMD, so each may hold up to
 // 256 VGPRs) and splits K into the same 8 contiguous chunks whatever the
-// row-tile count.  Within a chunk, k-tiles are consumed in batches of two,
-// each tile of a batch feeding its own accumulator chain per activation plane
-// (one chain per plane when NB * XS >= 4); chains and wavefronts are summed in
-// a fixed order.  The summation order of a row therefore never depends on how
+// row-tile count.  Within a chunk, k-tiles are consumed in batches (of four
+// for one-tile items of one row tile, else two); even and odd k-tiles feed two accumulator
+// chains per activation plane (one chain per plane when NB * XS >= 4); chains
+// and wavefronts are summed in a fixed order.  The summation order of a row therefore never depends on how
 // many other rows share the launch.
 constexpr int GEMM_WAVES = 8;
 // LDS staging of an inline RMSNorm's tile sums: rows x tiles <= 8192 floats.
 constexpr int RS_STAGE_FLOATS = 8192;
 constexpr int GEMM_THREADS = GEMM_WAVES * 64;
-constexpr int GEMM_U = 2;
+// k-tiles per batch: 4 (a wavefront keeps 8 or 16 KiB of weights in flight
+// over its two batches) unless the streamed activations of MT = 4 row tiles
+// would not fit; then 2.
+template <int MT, int NB> constexpr int gemm_u() { return MT <= (NB == 1 ? 1 : 2) ? 4 : 2; }
 
-template <int NB> struct WBatch { uint4 w[GEMM_U][NB]; };
-template <int MT, int NB, int XS> struct XWBatch {
-  uint4 w[GEMM_U][NB];
-  uint4 x[GEMM_U][MT][XS];
+template <int U, int NB> struct WBatch { uint4 w[U][NB]; };
+template <int U, int MT, int NB, int XS> struct XWBatch {
+  uint4 w[U][NB];
+  uint4 x[U][MT][XS];
 };
 
 // Epilogue of one output tile (the reduced MT x NB fragment tile in LDS).
@@ -217,7 +220,7 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
 template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) {
   constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
-  constexpr int WAVES = GEMM_WAVES, NT = GEMM_THREADS, U = GEMM_U;
+  constexpr int WAVES = GEMM_WAVES, NT = GEMM_THREADS, U = gemm_u<MT, NB>();
   constexpr int NF = MT * NB;
   constexpr int R = MT * 16;
   constexpr bool XRES = KC > 0;
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   __shared__ float rs_row[RS ? R : 1];
   __shared__ f32x4 rs_stage[RS ? RS_STAGE_FLOATS / 4 : 1];  // tile sums of the block's rows
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_items = p.m_blocks * p.n_blocks;
   const int my_items = (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
   const int per = (p.k_tiles + WAVES - 1) / WAVES;      // k-tiles of every wavefront's chunk
@@ -249,11 +252,20 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   }
 
   auto item_of = [&](int i) { return int(blockIdx.x) + i * int(gridDim.x); };
-  auto w_addr = [&](int item) {
+  // Weight tiles of an item through a buffer resource: the item base and the
+  // k-tile offset are uniform (scalar registers); a lane adds only lane * 16.
+  // Every k-tile index is clamped into the wavefront's chunk, so all offsets
+  // stay inside the item's NB rows of tiles.  NB == 2 weights use the paired
+  // layout (the two row tiles interleave per k-tile), so a wavefront's chunk
+  // of an item is one contiguous run.
+  auto w_rsrc = [&](int item) {
     const int nt0 = (item % p.n_blocks) * NB;
     const int seg = nt0 / p.seg_ntiles;
-    return p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride + lane * 16;
+    const char *base = uniform_ptr(p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, int(NB * wstride), BUF_DWORD3);
   };
+  const int w_lane = lane * 16;
+  auto w_off = [&](int kt, int nb) { return NB == 2 ? (kt * 2 + nb) * 1024 : nb * int(wstride) + kt * 1024; };
   auto x_load = [&](int mtg, int kt, int xp) -> uint4 {
     if constexpr (XROW) {
       const int row = min(mtg * 16 + (lane & 15), p.M - 1);
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 
   // Accumulator chains: one per k-tile of a batch and activation plane, or
   // one per plane when NB * XS already gives four independent chains.
-  constexpr int UC = NB * XS >= 4 ? 1 : U;
+  constexpr int UC = NB * XS >= 4 ? 1 : 2;
   f32x4 acc[UC][XS][MT][NB];
   auto zero_acc = [&]() {
 #pragma unroll
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
         for (int xp = 0; xp < XS; ++xp) {
           const uint4 xv = row_ok[mt] ? x[mt][xp] : make_uint4(0, 0, 0, 0);
-          acc[u % UC][xp][mt][nb] = mma<T>(acc[u % UC][xp][mt][nb], wv, xv);
+          acc[u % UC][xp][mt][nb] = mma<T>(acc[u % UC][xp][mt][nb], wv, xv);  // chain = k-tile parity
         }
     }
   };
@@ -437,14 +449,14 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   zero_acc();
   if constexpr (XRES) {
     constexpr int NBAT = KC / U;
-    WBatch<NB> wb[2];
-    auto issue_w = [&](int item, int b, WBatch<NB> &f) {
-      const char *wbase = w_addr(item);
+    WBatch<U, NB> wb[2];
+    auto issue_w = [&](int item, int b, WBatch<U, NB> &f) {
+      const auto rs = w_rsrc(item);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kt = min(k0 + b * U + u, kclamp);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt) * 1024);
+        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
       }
     };
     rs_issue();
@@ -477,26 +489,26 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     }
   } else {
     // Activations stream with the weights; two batches in flight.
-    XWBatch<MT, NB, XS> fa, fb;
+    XWBatch<U, MT, NB, XS> fa, fb;
     const int T_steps = my_items * nbat;
     const int t_last = T_steps - 1;
-    auto issue = [&](int t, XWBatch<MT, NB, XS> &f) {
+    auto issue = [&](int t, XWBatch<U, MT, NB, XS> &f) {
       const int item = item_of(t / nbat);
       const int b = t % nbat;
       const int mblk = item / p.n_blocks;
-      const char *wbase = w_addr(item);
+      const auto rs = w_rsrc(item);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kt = min(k0 + b * U + u, kclamp);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_stream(wbase + nb * wstride + size_t(kt) * 1024);
+        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int xp = 0; xp < XS; ++xp) f.x[u][mt][xp] = x_load(mblk * MT + mt, kt, xp);
       }
     };
-    auto compute = [&](int t, const XWBatch<MT, NB, XS> &f) {
+    auto compute = [&](int t, const XWBatch<U, MT, NB, XS> &f) {
       const int b = t % nbat;
       const int mblk = item_of(t / nbat) / p.n_blocks;
 #pragma unroll
@@ -576,15 +588,22 @@ static hipError_t launch_one(const GemmParams &p, hipStream_t s) {
 }
 
 // Resident activations when gemm_resident_ok holds; the chunk register array
-// is sized 4, 8 or 16 tiles.
+// is sized 4 (batches of two only), 8 or 16 tiles (32 or 48 for one row tile and
+// plane, NB == 1).
 template <typename T, int MT, int NB, int EPI, int XS, bool XROW>
 static hipError_t launch_kc(const GemmParams &p, hipStream_t s) {
   const int per = (p.k_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
   if constexpr (MT * XS <= 2) {
     if (gemm_resident_ok(p.m_blocks, MT, XS, p.k_tiles)) {
-      if (per <= 4) return launch_one<T, MT, NB, EPI, XS, XROW, 4>(p, s);
+      if constexpr (gemm_u<MT, NB>() == 2) {
+        if (per <= 4) return launch_one<T, MT, NB, EPI, XS, XROW, 4>(p, s);
+      }
       if (per <= 8) return launch_one<T, MT, NB, EPI, XS, XROW, 8>(p, s);
-      return launch_one<T, MT, NB, EPI, XS, XROW, 16>(p, s);
+      if (per <= 16) return launch_one<T, MT, NB, EPI, XS, XROW, 16>(p, s);
+      if constexpr (MT * XS == 1 && NB == 1) {
+        if (per <= 32) return launch_one<T, MT, NB, EPI, XS, XROW, 32>(p, s);
+        return launch_one<T, MT, NB, EPI, XS, XROW, 48>(p, s);
+      }
     }
   }
   return launch_one<T, MT, NB, EPI, XS, XROW, 0>(p, s);

@@ -87,9 +87,11 @@ inline bool gemm_inline_rs_ok(int m_blocks, int MT, int hidden) {
 }
 
 // Whether a launch keeps its activations resident in registers: one row
-// block, MT * planes <= 2 and a wavefront K chunk of at most 16 tiles.
+// block and a wavefront K chunk of at most 16 tiles with MT * planes <= 2, or
+// of at most 48 tiles with a single row tile and plane.
 inline bool gemm_resident_ok(int m_blocks, int MT, int planes, int k_tiles) {
-  return m_blocks == 1 && MT * planes <= 2 && (k_tiles + 7) / 8 <= 16;
+  const int per = (k_tiles + 7) / 8;
+  return m_blocks == 1 && ((MT * planes <= 2 && per <= 16) || (MT * planes == 1 && per <= 48));
 }
 
 struct ArgmaxFinishParams {
@@ -144,7 +146,7 @@ hipError_t launch_embed(int dtype, const EmbedParams &p, hipStream_t s);
 hipError_t launch_rstd(const float *ssq, int tiles, int K, float eps, int M, float *rs, hipStream_t s);
 hipError_t launch_pack_matrix(int dtype, const void *src, int rows, int cols, void *dst,
                               int dst_tile_offset, int dst_tile_stride, int rot_head_dim,
-                              int rot_rows, hipStream_t s);
+                              int rot_rows, bool pairs, hipStream_t s);
 hipError_t launch_kv_convert(int dtype, bool to_packed, void *packed_k, void *packed_v,
                              void *plain_k, void *plain_v, long long regions, int capacity,
                              int head_dim, hipStream_t s);

@@ -70,13 +70,15 @@ __global__ __launch_bounds__(256) void rstd_kernel(const float *ssq, int tiles, 
 }
 
 // Pack a row-major [rows, cols] matrix into fragment tiles.  Destination
-// row tile rt goes to tile row (dst_tile_offset + rt * dst_tile_stride).  For
+// row tile rt goes to tile row d = (dst_tile_offset + rt * dst_tile_stride);
+// with pairs, row tiles 2p and 2p + 1 interleave per column tile (tile
+// (d, c) at position (p * col_tiles + c) * 2 + (d & 1)).  For
 // the first rot_rows rows, packed row r of each rot_head_dim-row head takes
 // source channel rot_channel(r) of that head (rotary pairs share a tile).
 template <typename T>
 __global__ __launch_bounds__(256) void pack_matrix_kernel(const char *src, int rows, int cols, char *dst,
                                                           int tile_off, int tile_stride, int rot_hd,
-                                                          int rot_rows) {
+                                                          int rot_rows, bool pairs) {
   constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
   const int ktc = (cols + KT - 1) / KT;
   const int rtc = (rows + 15) / 16;
@@ -107,7 +109,9 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(const char *src, int r
         v = chunk_pack<T>(tmp);
       }
     }
-    const size_t dtile = size_t(tile_off + (long long)rt * tile_stride) * ktc + ct;
+    const long long drt = tile_off + (long long)rt * tile_stride;
+    // pairs: row tiles 2p and 2p + 1 interleave per column tile
+    const size_t dtile = pairs ? size_t((drt >> 1) * ktc + ct) * 2 + (drt & 1) : size_t(drt) * ktc + ct;
     st16(dst + dtile * 1024 + lane * 16, v);
   }
 }
@@ -171,15 +175,15 @@ hipError_t launch_rstd(const float *ssq, int tiles, int K, float eps, int M, flo
 }
 
 hipError_t launch_pack_matrix(int dtype, const void *src, int rows, int cols, void *dst, int tile_off,
-                              int tile_stride, int rot_hd, int rot_rows, hipStream_t s) {
+                              int tile_stride, int rot_hd, int rot_rows, bool pairs, hipStream_t s) {
   const int kt = kt_of(dtype);
   const long long work = (long long)((rows + 15) / 16) * ((cols + kt - 1) / kt) * 64;
   if (dtype == DFLASH_BF16)
     hipLaunchKernelGGL(pack_matrix_kernel<bf16_t>, dim3(grid_for(work)), dim3(256), 0, s,
-                       (const char *)src, rows, cols, (char *)dst, tile_off, tile_stride, rot_hd, rot_rows);
+                       (const char *)src, rows, cols, (char *)dst, tile_off, tile_stride, rot_hd, rot_rows, pairs);
   else
     hipLaunchKernelGGL(pack_matrix_kernel<float>, dim3(grid_for(work)), dim3(256), 0, s,
-                       (const char *)src, rows, cols, (char *)dst, tile_off, tile_stride, rot_hd, rot_rows);
+                       (const char *)src, rows, cols, (char *)dst, tile_off, tile_stride, rot_hd, rot_rows, pairs);
   return hipGetLastError();
 }
 

@@ -74,9 +74,17 @@ class Drafter:
                       dst.data_ptr(), sp)
             return dst, (src if keep_plain else None)
 
+        def pack_lm_head(arr):
+            src = upload(arr, self.dt, self.device)
+            nb = self.lib.dflash_packed_bytes(dcode, arr.shape[0], arr.shape[1])
+            dst = torch.empty(nb, dtype=torch.uint8, device=self.device)
+            _lib.call("dflash_pack_lm_head", dcode, src.data_ptr(), arr.shape[0], arr.shape[1],
+                      dst.data_ptr(), sp)
+            return dst, (src if keep_plain else None)
+
         self.plain = {}
         self.w_fc, self.plain["w_fc"] = pack_matrix(weights.w_fc)
-        self.lm_head, self.plain["lm_head"] = pack_matrix(weights.lm_head)
+        self.lm_head, self.plain["lm_head"] = pack_lm_head(weights.lm_head)
         self.fc_norm = upload(weights.fc_norm, self.dt, self.device)
         self.final_norm = upload(weights.final_norm, self.dt, self.device)
         self.embed = upload(weights.embed, self.dt, self.device)

@@ -124,7 +124,7 @@ typedef struct {
   const void *fc_norm;     /* [H] */
   const void *embed;       /* plain row-major [V, H] (rows are gathered) */
   const void *final_norm;  /* [H] */
-  const void *lm_head;     /* dflash_pack_matrix of W_lm [V, H] */
+  const void *lm_head;     /* dflash_pack_lm_head of W_lm [V, H] */
   const dflash_layer *layers;  /* [host] array of n_layers */
 } dflash_weights;
 
@@ -161,11 +161,21 @@ int dflash_pack_matrix(int32_t dtype, const void *src, int32_t rows, int32_t col
 int dflash_pack_qkv(const dflash_dims *dims, const void *wq, const void *wk, const void *wv,
                     void *dst, hipStream_t stream);
 
-/* Pack W_gate and W_up ([I, H] each) into one matrix of 2I rows whose 16-row
- * tiles alternate gate, up, gate, up...  dst holds
+/* Pack W_gate and W_up ([I, H] each) into one matrix of 2I rows in the
+ * paired layout: row tiles alternate gate, up, gate, up..., and each pair of
+ * row tiles (2p, 2p + 1) interleaves per column tile, so tile (2p + j, c)
+ * sits at position (p * K_tiles + c) * 2 + j.  dst holds
  * dflash_packed_bytes(dtype, 2 * I, H). */
 int dflash_pack_gate_up(const dflash_dims *dims, const void *w_gate, const void *w_up,
                         void *dst, hipStream_t stream);
+
+/* Pack the shared lm_head W_lm [vocab, hidden] in the paired layout (row
+ * tiles 2p and 2p + 1 interleave per column tile, as for dflash_pack_gate_up)
+ * that the draft and verify heads read: a wavefront's K range of two row
+ * tiles is then one contiguous run.  vocab a multiple of 32; dst holds
+ * dflash_packed_bytes(dtype, vocab, hidden). */
+int dflash_pack_lm_head(int32_t dtype, const void *src, int32_t vocab, int32_t hidden, void *dst,
+                        hipStream_t stream);
 
 /* --------------------------------------------------------------- KV cache */
 
@@ -233,7 +243,7 @@ int dflash_draft_forward(const dflash_dims *dims, const dflash_weights *w, const
 
 /* Greedy verification.  target_hidden: [batch, B+1, H] row-major, storage
  * dtype: the target's final hidden states at its pass over
- * [x, d_0, ..., d_{B-1}].  lm_head: packed [V, H].  Outputs:
+ * [x, d_0, ..., d_{B-1}].  lm_head: dflash_pack_lm_head output.  Outputs:
  * target_argmax [batch, B+1] (lowest index on ties), accept_len [batch] =
  * first j < B with draft[s][j] != target_argmax[s][j], else B, and
  * bonus [batch] = target_argmax[s][accept_len[s]]. */
