@@ -290,6 +290,21 @@ hipError_t set_norm_in(GemmParams &p, bool inline_rs, const float *ssq, float *r
   return launch_rstd(ssq, H / 16, H, eps, M, rs, stream);
 }
 
+// The head GEMM with its argmax finish: inside the launch (last arriver) for
+// at most FUSED_FINISH_ROWS rows, else as a follow-up kernel per sequence.
+int launch_argmax_head(int dtype, GemmParams &lm, const ArgmaxFinishParams &fp, char *wsb, int batch,
+                       hipStream_t stream, const char *what) {
+  const bool fused = lm.M <= FUSED_FINISH_ROWS;
+  if (fused) {
+    lm.arrive = reinterpret_cast<unsigned *>(wsb + WS_ARRIVE_OFFSET);
+    lm.fin = fp;
+  }
+  hipError_t e = launch_gemm(dtype, EPI_ARGMAX, lm, stream);
+  if (e == hipSuccess && !fused) e = launch_argmax_finish(fp, batch, stream);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return DFLASH_OK;
+}
+
 void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.grid_cap = compute_units();
   p.M = g.M;
@@ -507,10 +522,10 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   g.cu_new = cu_new;
   g.batch = batch;
   g.status = kv->status;
+  g.arrive = reinterpret_cast<unsigned *>(wsb + WS_ARRIVE_OFFSET);  // the launch commits ctx_len itself
+  g.ctx_len_w = kv->ctx_len;
   e = launch_gemm(d->dtype, EPI_KVINJ, g, stream);
   if (e != hipSuccess) return hip_fail(e, "inject kv");
-  e = launch_commit_rows(kv->ctx_len, cu_new, batch, kv->capacity, stream);
-  if (e != hipSuccess) return hip_fail(e, "inject commit");
   return DFLASH_OK;
 }
 
@@ -667,17 +682,13 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   if (e != hipSuccess) return hip_fail(e, "draft final norm");
   lm.vocab = d->vocab;
   lm.keys = reinterpret_cast<unsigned long long *>(wsb);
-  e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
-  if (e != hipSuccess) return hip_fail(e, "draft lm_head");
   ArgmaxFinishParams fp{};
   fp.keys = lm.keys;
   fp.rows_per_seq = d->block_size;
   fp.block = d->block_size;
   fp.verify = 0;
   fp.tok_out = draft;
-  e = launch_argmax_finish(fp, batch, stream);
-  if (e != hipSuccess) return hip_fail(e, "draft argmax");
-  return DFLASH_OK;
+  return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "draft");
 }
 
 int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,
@@ -702,8 +713,6 @@ int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *
   lm.x_ld = d->hidden;
   lm.vocab = d->vocab;
   lm.keys = reinterpret_cast<unsigned long long *>(wsb);
-  hipError_t e = launch_gemm(d->dtype, EPI_ARGMAX, lm, stream);
-  if (e != hipSuccess) return hip_fail(e, "verify lm_head");
   ArgmaxFinishParams fp{};
   fp.keys = lm.keys;
   fp.rows_per_seq = d->block_size + 1;
@@ -713,9 +722,7 @@ int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *
   fp.draft_in = draft;
   fp.accept_len = accept_len;
   fp.bonus = bonus;
-  e = launch_argmax_finish(fp, batch, stream);
-  if (e != hipSuccess) return hip_fail(e, "verify accept");
-  return DFLASH_OK;
+  return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "verify");
 }
 
 }  // extern "C"

@@ -207,6 +207,60 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
   }
 }
 
+// Argmax finish for at most FUSED_FINISH_ROWS rows, run by one workgroup of
+// GEMM_THREADS threads after every workgroup's slot updates are performed:
+// 8 threads per row read and clear 8 slots each with atomic exchanges, fold
+// them by an 8-lane shuffle max, then one thread per sequence runs the
+// acceptance scan (verify).
+__device__ inline void fused_argmax_finish(const ArgmaxFinishParams &f, int M, int *toks) {
+  const int row = threadIdx.x >> 3, q = threadIdx.x & 7;
+  unsigned long long best = 0;
+  if (row < M) {
+    unsigned long long *k = f.keys + size_t(row) * ARGMAX_SLOTS + q * (ARGMAX_SLOTS / 8);
+#pragma unroll
+    for (int i = 0; i < ARGMAX_SLOTS / 8; ++i) {
+      const unsigned long long v = __hip_atomic_exchange(k + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      best = v > best ? v : best;
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    const unsigned long long o = __shfl_xor(best, off, 64);
+    best = o > best ? o : best;
+  }
+  if (row < M && q == 0) {
+    const int tok = key_index(best);
+    f.tok_out[row] = tok;
+    toks[row] = tok;
+  }
+  __syncthreads();
+  if (f.verify) {
+    const int R = f.rows_per_seq, B = f.block;
+    const int s = threadIdx.x;
+    if (s < M / R) {
+      int L = B;
+      for (int j = 0; j < B; ++j) {
+        if (f.draft_in[s * B + j] != toks[s * R + j]) { L = j; break; }
+      }
+      f.accept_len[s] = L;
+      f.bonus[s] = toks[s * R + L];
+    }
+  }
+}
+
+// True in every thread of the workgroup that arrives last.  Each wavefront
+// first waits for all of its vector-memory operations (so its atomics and
+// stores are performed), the workgroup synchronises, and one thread counts
+// the arrival with a device-scope atomic.
+__device__ inline bool last_arriver(unsigned *arrive, int *flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  return *flag != 0;
+}
+
 // XROW: activations are a row-major [M, x_ld] input (one plane); otherwise
 // packed fragment tiles padded to whole row blocks (so no load needs a guard).
 // KC > 0: every wavefront's K chunk (at most KC tiles) of activations is
@@ -535,6 +589,24 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   if constexpr (EPI == EPI_ARGMAX) {
     lds_barrier();
     if (cur_mblk >= 0) flush_argmax(cur_mblk);
+  }
+  if constexpr (EPI == EPI_ARGMAX || EPI == EPI_KVINJ) {
+    if (p.arrive) {
+      __shared__ int flag;
+      __shared__ int toks[FUSED_FINISH_ROWS];
+      if (last_arriver(p.arrive, &flag)) {
+        if constexpr (EPI == EPI_ARGMAX) {
+          fused_argmax_finish(p.fin, p.M, toks);
+        } else {
+          // commit: ctx_len[s] += n_s unless the injection skipped sequence s
+          for (int s = threadIdx.x; s < p.batch; s += blockDim.x) {
+            const int ns = p.cu_new[s + 1] - p.cu_new[s];
+            if (p.ctx_len_w[s] + ns <= p.capacity) p.ctx_len_w[s] += ns;
+          }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(p.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 

@@ -15,6 +15,11 @@ constexpr int MAX_KEY_ROWS = 1088;   // 64 sequences x 17 verify rows
 constexpr size_t WS_COUNTER_BYTES = size_t(1) << 20;
 static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_COUNTER_BYTES, "key slots exceed the fixed area");
 constexpr int MAX_SEGMENTS = 16;
+// Arrival counter of the last-arriver handshakes, at the end of the fixed area.
+constexpr size_t WS_ARRIVE_OFFSET = WS_COUNTER_BYTES - 256;
+// The argmax finish and the injection commit run inside the GEMM launch (by
+// its last workgroup to finish) when the launch has at most this many rows.
+constexpr int FUSED_FINISH_ROWS = 64;
 
 enum Epilogue : int {
   EPI_STORE = 0,   // out_f32[m, n] = y
@@ -23,6 +28,14 @@ enum Epilogue : int {
   EPI_QKV = 3,     // RoPE on q and k of the block; q -> qbuf, k/v -> kblk/vblk
   EPI_KVINJ = 4,   // RoPE on injected k; k/v appended to the cache
   EPI_ARGMAX = 5,  // lowest-index argmax over the vocabulary (+ acceptance)
+};
+
+struct ArgmaxFinishParams {
+  unsigned long long *keys;
+  int rows_per_seq, block, verify;
+  int *tok_out;
+  const int *draft_in;
+  int *accept_len, *bonus;
 };
 
 struct GemmParams {
@@ -78,6 +91,13 @@ struct GemmParams {
   const float *rs_direct;
   int rs_tiles, rs_K;
   float rs_eps;
+  // Last-arriver tail (arrive set): every workgroup completes its memory
+  // operations and then increments *arrive; the one that sees grid - 1 runs
+  // the argmax finish (EPI_ARGMAX, fin) or the ctx_len commit (EPI_KVINJ),
+  // and resets *arrive to 0.
+  unsigned *arrive;
+  ArgmaxFinishParams fin;
+  int *ctx_len_w;             // EPI_KVINJ commit target (the same array as ctx_len)
 };
 
 // Whether a consumer can reduce the RMSNorm tile sums itself: one row block
@@ -94,13 +114,6 @@ inline bool gemm_resident_ok(int m_blocks, int MT, int planes, int k_tiles) {
   return m_blocks == 1 && ((MT * planes <= 2 && per <= 16) || (MT * planes == 1 && per <= 48));
 }
 
-struct ArgmaxFinishParams {
-  unsigned long long *keys;
-  int rows_per_seq, block, verify;
-  int *tok_out;
-  const int *draft_in;
-  int *accept_len, *bonus;
-};
 
 struct AttnParams {
   const char *qbuf, *kblk, *vblk;   // per-step block operands
