@@ -59,17 +59,6 @@ __host__ __device__ inline int attn_sub(int heads) {
   return s < 1 ? 1 : (s > ATTN_MAX_SUB ? ATTN_MAX_SUB : s);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-// Wait until at most N of this wavefront's vector-memory operations are
-// outstanding (direct-to-LDS loads included); other counters untouched.
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // RC: 1 KiB tiles each wavefront loads per round (a compile-time count, so the
 // wait for the older of two rounds in flight is an immediate).  NW: most
 // wavefronts per workgroup (8 leaves each 256 VGPRs, 16 leaves 128).
@@ -121,7 +110,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       if (st >= st1) src = kbk;
       else if (tt < KB / 1024) src = (st == n_ctx ? kbk : kreg + size_t(st) * KB) + tt * 1024;
       else src = (st == n_ctx ? vbk : vreg + size_t(st) * VB) + (tt - KB / 1024) * 1024;
-      __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)(slot + j * 64), 16, 0, 0);
+      load_lds16(src + lane * 16, slot + j * 64);
     }
   };
 

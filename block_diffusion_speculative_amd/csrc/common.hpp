@@ -223,6 +223,24 @@ __device__ inline float row_rstd8(const float *tile_ssq, int tiles, int K, float
   return 1.0f / sqrtf(s / float(K) + eps);
 }
 
+// Direct global -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes
+// from src land at lds_base + 16 l, lds_base uniform over the wavefront (M0
+// holds its LDS byte address).  Issued as inline assembly so that the
+// compiler does not wait for every such load before each LDS read; callers
+// wait with wait_vmcnt (the loads count in vmcnt) and an LDS barrier.
+__device__ inline void load_lds16(const void *src, void *lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding (direct-to-LDS loads included); other counters untouched.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Barrier for LDS traffic only: waits for this wavefront's LDS operations,
 // not for its outstanding global loads (which __syncthreads would drain).
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

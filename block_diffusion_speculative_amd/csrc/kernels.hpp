@@ -98,7 +98,14 @@ struct GemmParams {
   unsigned *arrive;
   ArgmaxFinishParams fin;
   int *ctx_len_w;             // EPI_KVINJ commit target (the same array as ctx_len)
+  // Tiled launches (more than TILED_MIN_ROWS rows): 16-row tiles held by the
+  // packed activation buffer (loads past it are clamped), and the output tile
+  // in fragments: tile_m = 8 (128 x 256) or 4 (64 x 128).
+  int tiled, x_mtiles, tile_m;
 };
+
+// Launches with more rows than this use the tiled kernel (128 x 256 tiles).
+constexpr int TILED_MIN_ROWS = 64;
 
 // Whether a consumer can reduce the RMSNorm tile sums itself: one row block
 // whose rows x tiles fit the 8192-float LDS stage.
@@ -150,6 +157,7 @@ struct EmbedParams {
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s);
+hipError_t launch_gemm_tiled(int dtype, int epi, const GemmParams &p, hipStream_t s);
 hipError_t launch_argmax_finish(const ArgmaxFinishParams &p, int batch, hipStream_t s);
 hipError_t launch_commit_rows(int *ctx_len, const int *cu_new, int batch, int capacity, hipStream_t s);
 hipError_t launch_attention(int dtype, const AttnParams &p, int batch, hipStream_t s);

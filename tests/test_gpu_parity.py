@@ -125,6 +125,20 @@ def test_small_bf16_gains_and_no_rope():
     _compare_step(case, 0, [2])
 
 
+def test_small_bf16_batch5_tiled():
+    """80 draft rows, 85 verify rows and 85 injected rows: every GEMM of the
+    step takes the tiled (many-row) kernel, the RMSNorm scales come from
+    rstd_kernel and the argmax finish runs as its own kernel."""
+    case = Hn.build_case(SMALL_BF16, 5, [3, 70, 129, 200, 31], seed=9)
+    _compare_step(case, 0, [17, 17, 17, 17, 17])
+
+
+def test_tiny_f32_batch6_tiled():
+    d = C.TINY_DRAFT
+    case = Hn.build_case(d, 6, [0, 16, 17, 50, 96, 128], seed=10)
+    _compare_step(case, 0, [12, 1, 17, 9, 16, 15])
+
+
 @pytest.mark.parametrize("rows,split", [(12, 5), (20, 7)])
 def test_incremental_injection_matches_single(rows, split):
     """Injecting rows in two calls equals one call (positions and append
@@ -195,4 +209,17 @@ def test_qwen3_8b_b1_full_shape():
     w = C.get("qwen3-8b-b1")
     case = Hn.build_case(w.dims, 1, [2048], seed=0, kv_mode="import")
     rep = _compare_step(case, 0, [9], accept_p=I.workload_geom_p(w), check_cache=False)
+    assert rep["tokens"].compared >= 1
+
+
+@pytest.mark.slow
+def test_qwen3_8b_b32_ragged_sampled():
+    """The batch-32 ragged workload at full shape (contexts U[512, 4096],
+    injected rows U[1, 17], cache imported); the oracle follows sequences 0,
+    13 and 31, the GPU runs the whole batch."""
+    w = C.get("qwen3-8b-b32")
+    ctx = I.context_lengths(w, 0)
+    rows = I.new_row_counts(w, 0, 0)
+    case = Hn.build_case(w.dims, w.batch, ctx, seed=0, kv_mode="import")
+    rep = _compare_step(case, 0, rows, seqs=[0, 13, 31], accept_p=I.workload_geom_p(w), check_cache=False)
     assert rep["tokens"].compared >= 1
