@@ -687,7 +687,10 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   fill_gemm(lm, L.lm);
   lm.w_seg[0] = static_cast<const char *>(w->lm_head);
   lm.x = wsb + L.xa;
-  lm.xs = L.xs;
+  // The head reads the hi plane only: the normalised hidden rounded to bf16
+  // moves a logit by ~1e-3 (std), an order below the 1e-2 gap at which a
+  // drafted token is decided, and halves the head's MFMA work.
+  lm.xs = 1;
   lm.x_plane = L.pa;
   e = set_norm_in(lm, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
   if (e != hipSuccess) return hip_fail(e, "draft final norm");
