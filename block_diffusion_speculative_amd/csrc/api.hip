@@ -321,15 +321,8 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.out_planes = 1;
   // packed activation buffers hold whole row blocks of the row-tile plan
   p.x_mtiles = g.m_blocks * g.MT;
-  if (g.M > TILED_MIN_ROWS) {
-    // 128 x 256 tiles when they fill at least 3/4 of the compute units, else 64 x 128
-    p.tiled = 1;
-    const int big = ((g.M + 127) / 128) * ((g.n_tiles + 15) / 16);
-    p.tile_m = big * 4 >= 3 * p.grid_cap ? 8 : 4;
-    const int tn = p.tile_m == 8 ? 16 : 8;
-    p.m_blocks = (g.M + 16 * p.tile_m - 1) / (16 * p.tile_m);
-    p.n_blocks = (g.n_tiles + tn - 1) / tn;
-  }
+  // many-row launches go to the tiled kernel, which picks its tile shape
+  if (g.M > TILED_MIN_ROWS) p.tiled = 1;
 }
 
 }  // namespace

@@ -233,6 +233,15 @@ __device__ inline void load_lds16(const void *src, void *lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the instruction's scalar-base form): no 64-bit address per
+// lane has to stay live between loads.
+__device__ inline void load_lds16_s(const char *sbase, uint32_t voff, const void *lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wavefront's vector-memory operations are
 // outstanding (direct-to-LDS loads included); other counters untouched.
 template <int N>

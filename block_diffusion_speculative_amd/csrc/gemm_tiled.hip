@@ -7,7 +7,7 @@
 // sub-tiles, each accumulating (TM / 2) x (TN / 4) MFMA fragments over all of
 // K.  Per 32-column k-tile the tile's activation fragments (TM row tiles, one
 // or two planes) and weight fragments (TN row tiles) are copied straight from
-// global memory into an LDS ring of 4 (large tile) or 8 (small tile) stages (global_load_lds_dwordx4, one
+// global memory into an LDS ring of as many stages as fit 144 KiB (global_load_lds_dwordx4, one
 // 1 KiB fragment per wavefront instruction, the same number for every
 // wavefront so the wait before a stage is an immediate); every wavefront then
 // reads its fragments from LDS, so each fragment fetched from L2 feeds
@@ -23,17 +23,19 @@
 
 namespace dflash {
 
-constexpr int TL_WAVES = 8;
-constexpr int TL_THREADS = TL_WAVES * 64;
 constexpr int TL_XCDS = 8;   // workgroups are dispatched round-robin over 8 XCDs
 
 // S: stages of the LDS ring; S - 1 of them are in flight while one is consumed.
-template <typename T, int EPI, int XS, bool XROW, int TM, int TN, int S>
-__global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams p) {
+// WGM x WGN wavefronts; each owns (TM / WGM) x (TN / WGN) fragments.
+template <typename T, int EPI, int XS, bool XROW, int TM, int TN, int S, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmParams p) {
+  constexpr int TL_WAVES = WGM * WGN;
   constexpr int TL_STAGES = S;
   constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
   constexpr int TL_MT = TM, TL_NT = TN;
-  constexpr int TL_WM = TM / 2, TL_WN = TN / 4;   // fragments per wavefront
+  constexpr int TL_WM = TM / WGM, TL_WN = TN / WGN;   // fragments per wavefront
+  static_assert(TL_WM * WGM == TM && TL_WN * WGN == TN, "wave grid divides the tile");
+  static_assert(TM * 16 <= TL_WAVES * 64, "one thread per token row of the tile");
   // two-tile items (gate/up pairs, the heads) use the paired weight layout
   constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_ARGMAX;
   constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX);
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams
   __shared__ int flag;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int c = lane & 15, g = lane >> 4;
   const int K = p.k_tiles;
   // XCD-aware item order (the grid is a multiple of 8): XCD x takes feature
@@ -65,48 +67,57 @@ __global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams
   };
 
   // Issue side: the next stage to load (item, k-tile, ring slot), and per
-  // load of this wavefront the lane's address at k-tile 0 of the item and the
-  // bytes per k-tile (set once per item, so a stage costs only adds).
+  // load of this wavefront a wave-uniform base at k-tile 0 of the item, the
+  // lane's byte offset from it and the bytes per k-tile (set once per item,
+  // so a stage costs only scalar arithmetic).
   int is_i = 0, is_kt = 0, is_slot = 0, issued = 0;
-  const char *fb[LPW];
+  const char *sb[LPW];
+  uint32_t vo[LPW];
   int fstep[LPW];
+  const uint32_t lane16 = uint32_t(lane) * 16u;
   auto set_item = [&](int i) {
     const int item = item_of(i);
     const int nblk = item / p.m_blocks, mblk = item % p.m_blocks;
 #pragma unroll
     for (int l = 0; l < LPW; ++l) {
       const int j = wave + l * TL_WAVES;
+      const char *base;
+      vo[l] = lane16;
       if (j >= ST) {
-        fb[l] = p.w_seg[0] + lane * 16;   // padding slot: any valid fragment
+        base = p.w_seg[0];   // padding slot: any valid fragment
         fstep[l] = 0;
       } else if (j < XT) {
         const int mt = j / XS, xp = j % XS;
         if constexpr (XROW) {
-          const int row = min((mblk * TL_MT + mt) * 16 + c, p.M - 1);
-          fb[l] = p.x + (size_t(row) * p.x_ld + g * E) * ES;
+          // rows past M repeat row M - 1 (their results are never stored)
+          const int r0 = (mblk * TL_MT + mt) * 16, rb = min(r0, p.M - 1), row = min(r0 + c, p.M - 1);
+          base = p.x + size_t(rb) * p.x_ld * ES;
+          vo[l] = uint32_t(((row - rb) * p.x_ld + g * E) * ES);
           fstep[l] = KT * ES;
         } else {
           const int mg = min(mblk * TL_MT + mt, p.x_mtiles - 1);
-          fb[l] = p.x + xp * p.x_plane + size_t(mg) * K * 1024 + lane * 16;
+          base = p.x + size_t(xp) * p.x_plane + size_t(mg) * K * 1024;
           fstep[l] = 1024;
         }
       } else {
         const int nt = min(nblk * TL_NT + (j - XT), p.n_tiles - 1);
         const int seg = nt / p.seg_ntiles, loc = nt - seg * p.seg_ntiles;
         if constexpr (PAIRED) {
-          fb[l] = p.w_seg[seg] + (size_t(loc >> 1) * K * 2 + (loc & 1)) * 1024 + lane * 16;
+          base = p.w_seg[seg] + (size_t(loc >> 1) * K * 2 + (loc & 1)) * 1024;
           fstep[l] = 2048;
         } else {
-          fb[l] = p.w_seg[seg] + size_t(loc) * K * 1024 + lane * 16;
+          base = p.w_seg[seg] + size_t(loc) * K * 1024;
           fstep[l] = 1024;
         }
       }
+      sb[l] = uniform_ptr(base);
     }
   };
   auto issue_next = [&]() {
     uint4 *slot = ring + is_slot * SP * 64;
 #pragma unroll
-    for (int l = 0; l < LPW; ++l) load_lds16(fb[l] + size_t(is_kt) * fstep[l], slot + (wave + l * TL_WAVES) * 64);
+    for (int l = 0; l < LPW; ++l)
+      load_lds16_s(sb[l] + size_t(is_kt) * fstep[l], vo[l], slot + (wave + l * TL_WAVES) * 64);
     ++issued;
     is_slot = is_slot + 1 == TL_STAGES ? 0 : is_slot + 1;
     if (++is_kt == K) {
@@ -334,9 +345,9 @@ __global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams
     else wait_vmcnt<0>();
     after_epi = false;
   };
-  int rd_slot = 0, c_kt = 0, c_i = 0;
+  int rd_slot = 0, t = 0;
   Frags fa, fb2;
-  auto step = [&](int t, const Frags &cur, Frags &nxt) {
+  auto step = [&](const Frags &cur, Frags &nxt) {
     if (t + 1 < steps) {
       wait_stage(t + 1);
       lds_barrier();
@@ -345,11 +356,7 @@ __global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams
       read_frags(rd_slot, nxt);
     }
     mfma_frags(cur);
-    if (++c_kt == K) {
-      c_kt = 0;
-      epilogue(item_of(c_i++));
-      after_epi = true;
-    }
+    ++t;
   };
   if (steps > 0) {
     wait_stage(0);
@@ -357,9 +364,20 @@ __global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams
     if (issued < steps) issue_next();
     read_frags(0, fa);
   }
-  for (int t = 0; t < steps; t += 2) {
-    step(t, fa, fb2);
-    if (t + 1 < steps) step(t + 1, fb2, fa);
+  // Two k-tiles per trip so the register buffers alternate without copies;
+  // one epilogue per item, after its last k-tile.
+  for (int it = 0; it < my_items; ++it) {
+    int kt = 0;
+    for (; kt + 1 < K; kt += 2) {
+      step(fa, fb2);
+      step(fb2, fa);
+    }
+    if (kt < K) {   // odd k-tile count: the next item starts from fb2
+      step(fa, fb2);
+      fa = fb2;
+    }
+    epilogue(item_of(it));
+    after_epi = true;
   }
   if constexpr (EPI == EPI_ARGMAX) {
     if (cur_mblk >= 0) flush_argmax(cur_mblk);
@@ -375,15 +393,37 @@ __global__ __launch_bounds__(TL_THREADS) void gemm_tiled_kernel(const GemmParams
   }
 }
 
+// Stages that fit a 144 KiB ring (the LDS holds 160 KiB per workgroup).
+template <int TM, int TN, int XS, int WAVES>
+constexpr int tl_stages() {
+  constexpr int slots = (TM * XS + TN + WAVES - 1) / WAVES * WAVES;
+  return 144 / slots;
+}
+
+template <typename T, int EPI, int XS, bool XROW, int TM, int TN, int WGM, int WGN>
+static void launch_tiled_shape(const GemmParams &p, int grid, hipStream_t s) {
+  constexpr int S = tl_stages<TM, TN, XS, WGM * WGN>();
+  hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, XS, XROW, TM, TN, S, WGM, WGN>), dim3(grid), dim3(WGM * WGN * 64), 0, s, p);
+}
+
+// Tile choice: 8 x 16 fragments (128 tokens x 256 features) when those
+// items fill at least 3/4 of the compute units, else 4 x 8 (64 x 128); both
+// with 8 wavefronts in a 2 x 4 grid.
 template <typename T, int EPI, int XS, bool XROW>
-static hipError_t launch_tiled_one(const GemmParams &p, hipStream_t s) {
+static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
+  GemmParams p = p0;
+  const int cu = p.grid_cap;
+  auto blocks = [](int n, int b) { return (n + b - 1) / b; };
+  const bool big = blocks(p.M, 128) * blocks(p.n_tiles, 16) * 4 >= 3 * cu;
+  p.tile_m = big ? 8 : 4;
+  p.m_blocks = blocks(p.M, 16 * p.tile_m);
+  p.n_blocks = big ? blocks(p.n_tiles, 16) : blocks(p.n_tiles, 8);
   // grid: a multiple of the 8 XCDs, at most one workgroup per compute unit
   const int items = p.m_blocks * p.n_blocks;
-  int grid = items < p.grid_cap ? items : p.grid_cap;
+  int grid = items < cu ? items : cu;
   grid = grid < TL_XCDS ? TL_XCDS : grid - grid % TL_XCDS;
-  // 128 KiB rings: 4 stages of the large tile, 8 of the small one
-  if (p.tile_m == 8) hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, XS, XROW, 8, 16, 4>), dim3(grid), dim3(TL_THREADS), 0, s, p);
-  else hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, XS, XROW, 4, 8, 8>), dim3(grid), dim3(TL_THREADS), 0, s, p);
+  if (big) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
+  else launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
   return hipGetLastError();
 }
 

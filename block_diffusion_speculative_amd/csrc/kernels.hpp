@@ -99,8 +99,9 @@ struct GemmParams {
   ArgmaxFinishParams fin;
   int *ctx_len_w;             // EPI_KVINJ commit target (the same array as ctx_len)
   // Tiled launches (more than TILED_MIN_ROWS rows): 16-row tiles held by the
-  // packed activation buffer (loads past it are clamped), and the output tile
-  // in fragments: tile_m = 8 (128 x 256) or 4 (64 x 128).
+  // packed activation buffer (loads past it are clamped), and the output
+  // tile's token fragments (4 or 8; set by the launcher, which also
+  // sets m_blocks and n_blocks for the tile it picks).
   int tiled, x_mtiles, tile_m;
 };
 

@@ -133,6 +133,16 @@ def test_small_bf16_batch5_tiled():
     _compare_step(case, 0, [17, 17, 17, 17, 17])
 
 
+def test_large_vocab_batch16_big_tiles():
+    """A 65536-token vocabulary: the draft head (256 rows) and the verify head
+    (272 rows, a ragged last token block) run the 128 x 256 tile over many
+    items per workgroup."""
+    d = C.Dims(**{**SMALL_BF16.__dict__, "vocab": 65536})
+    ctx = [(37 * s) % 150 for s in range(16)]
+    case = Hn.build_case(d, 16, ctx, seed=12)
+    _compare_step(case, 0, [(5 * s) % 17 for s in range(16)], seqs=[0, 7, 15])
+
+
 def test_tiny_f32_batch6_tiled():
     d = C.TINY_DRAFT
     case = Hn.build_case(d, 6, [0, 16, 17, 50, 96, 128], seed=10)
