@@ -92,7 +92,7 @@ int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
 constexpr int MLP_ACT_PLANES = 1;
 
 struct DraftLayout {
-  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, end;
+  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
   int M, Mp, S, xs;
   bool rs_inline;  // consumers reduce the RMSNorm tile sums themselves (one row block)
@@ -132,6 +132,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
+  L.part = L.M > TILED_MIN_ROWS ? b.take(MAX_SPLIT_UNITS * SPLIT_TILE_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -149,7 +150,7 @@ VerifyLayout verify_layout(const dflash_dims *d, int batch) {
 }
 
 struct InjectLayout {
-  size_t u, xc, ssq, rs, end, pc;
+  size_t u, xc, ssq, rs, part, end, pc;
   int Rp, xs;
   bool rs_inline;
   GemmPlan fc, kv;
@@ -170,6 +171,7 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
   L.rs_inline = gemm_inline_rs_ok(L.kv.m_blocks, L.kv.MT, H);
+  L.part = rows > TILED_MIN_ROWS ? b.take(MAX_SPLIT_UNITS * SPLIT_TILE_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -303,6 +305,13 @@ int launch_argmax_head(int dtype, GemmParams &lm, const ArgmaxFinishParams &fp, 
   if (e == hipSuccess && !fused) e = launch_argmax_finish(fp, batch, stream);
   if (e != hipSuccess) return hip_fail(e, what);
   return DFLASH_OK;
+}
+
+// Split-K scratch of a many-row launch: partial tiles at ws + part (0: the
+// layout has none) and the per-item counts in the fixed counter area.
+void set_split(GemmParams &p, char *wsb, size_t part) {
+  p.part_ws = part ? reinterpret_cast<float *>(wsb + part) : nullptr;
+  p.part_cnt = part ? reinterpret_cast<unsigned *>(wsb + WS_SPLIT_CNT_OFFSET) : nullptr;
 }
 
 void fill_gemm(GemmParams &p, const GemmPlan &g) {
@@ -489,6 +498,7 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
 
   GemmParams fc{};
   fill_gemm(fc, L.fc);
+  set_split(fc, wsb, L.part);
   fc.w_seg[0] = static_cast<const char *>(w->w_fc);
   fc.x = static_cast<const char *>(feats);
   fc.x_ld = d->n_feat_layers * H;
@@ -501,6 +511,7 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
 
   GemmParams g{};
   fill_gemm(g, L.kv);
+  set_split(g, wsb, L.part);
   const int hd = d->head_dim;
   const size_t layer_bytes = packed_bytes(d->dtype, (long long)(d->n_q_heads + 2 * d->n_kv_heads) * hd, H);
   (void)layer_bytes;
@@ -586,6 +597,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
 
     GemmParams q{};
     fill_gemm(q, L.qkv);
+    set_split(q, wsb, L.part);
     q.w_seg[0] = static_cast<const char *>(lw.w_qkv);
     q.x = wsb + L.xa;
     q.xs = L.xs;
@@ -636,6 +648,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
 
     GemmParams o{};
     fill_gemm(o, L.o);
+    set_split(o, wsb, L.part);
     o.w_seg[0] = static_cast<const char *>(lw.w_o);
     o.x = wsb + L.xo;
     o.xs = L.xs;
@@ -649,6 +662,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
 
     GemmParams gu{};
     fill_gemm(gu, L.gu);
+    set_split(gu, wsb, L.part);
     gu.w_seg[0] = static_cast<const char *>(lw.w_gate_up);
     gu.x = wsb + L.xa;
     gu.xs = L.xs;
@@ -663,6 +677,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
 
     GemmParams dn{};
     fill_gemm(dn, L.down);
+    set_split(dn, wsb, L.part);
     dn.w_seg[0] = static_cast<const char *>(lw.w_down);
     dn.x = wsb + L.xact;
     dn.xs = MLP_ACT_PLANES;

@@ -52,19 +52,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   const int wm = wave / WGN, wn = wave % WGN;
   const int c = lane & 15, g = lane >> 4;
   const int K = p.k_tiles;
-  // XCD-aware item order (the grid is a multiple of 8): XCD x takes feature
-  // blocks x, x + 8, ...; its workgroups walk those blocks' (feature, token)
-  // items with the token block fastest.
+  // Work units: an item (feature block, token block) or, with ksplit > 1,
+  // one of ksplit parts of its k-tile range.  XCD-aware order (the grid is a
+  // multiple of 8): XCD x takes feature blocks x, x + 8, ...; its workgroups
+  // walk those blocks' units with the part fastest, then the token block.
   const int xcd = int(blockIdx.x) % TL_XCDS, r = int(blockIdx.x) / TL_XCDS;
   const int per_xcd = int(gridDim.x) / TL_XCDS;
+  const int ks = p.ksplit;
   const int nb_x = (p.n_blocks - xcd + TL_XCDS - 1) / TL_XCDS;
-  const int items_x = nb_x * p.m_blocks;
-  const int my_items = (items_x - r + per_xcd - 1) / per_xcd;
-  const int steps = my_items * K;
+  const int units_x = nb_x * p.m_blocks * ks;
+  const int my_items = (units_x - r + per_xcd - 1) / per_xcd;
+  // unit index (item * ks + part) of this workgroup's i-th unit
   auto item_of = [&](int i) {
     const int li = r + i * per_xcd;
-    return (xcd + TL_XCDS * (li / p.m_blocks)) * p.m_blocks + li % p.m_blocks;   // nblk * m_blocks + mblk
+    const int per_nb = p.m_blocks * ks;
+    return (xcd + TL_XCDS * (li / per_nb)) * per_nb + li % per_nb;
   };
+  auto k_begin = [&](int unit) { return (unit % ks) * K / ks; };
+  auto k_end = [&](int unit) { return (unit % ks + 1) * K / ks; };
+  int steps = 0;
+  for (int i = 0; i < my_items; ++i) steps += k_end(item_of(i)) - k_begin(item_of(i));
 
   // Issue side: the next stage to load (item, k-tile, ring slot), and per
   // load of this wavefront a wave-uniform base at k-tile 0 of the item, the
@@ -75,9 +82,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   uint32_t vo[LPW];
   int fstep[LPW];
   const uint32_t lane16 = uint32_t(lane) * 16u;
+  int is_kend = 0;
   auto set_item = [&](int i) {
-    const int item = item_of(i);
+    const int unit = item_of(i), item = unit / ks;
     const int nblk = item / p.m_blocks, mblk = item % p.m_blocks;
+    is_kt = k_begin(unit);
+    is_kend = k_end(unit);
 #pragma unroll
     for (int l = 0; l < LPW; ++l) {
       const int j = wave + l * TL_WAVES;
@@ -120,10 +130,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
       load_lds16_s(sb[l] + size_t(is_kt) * fstep[l], vo[l], slot + (wave + l * TL_WAVES) * 64);
     ++issued;
     is_slot = is_slot + 1 == TL_STAGES ? 0 : is_slot + 1;
-    if (++is_kt == K) {
-      is_kt = 0;
-      if (++is_i < my_items) set_item(is_i);
-    }
+    if (++is_kt == is_kend && ++is_i < my_items) set_item(is_i);
   };
 
   f32x4 acc[TL_WM][TL_WN];
@@ -364,19 +371,56 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
     if (issued < steps) issue_next();
     read_frags(0, fa);
   }
+  // The parts of a split item meet in the workspace: each stores its partial
+  // tile (agent-coherent stores, one f32x4 slot per lane and fragment),
+  // waits for them and counts itself in; the last to arrive sums the parts
+  // in part order from the workspace, so the result does not depend on
+  // which part finished last, resets the count and runs the epilogue.
+  auto split_last = [&](int unit) -> bool {
+    const int item = unit / ks;
+    auto slot = [&](int u, int a, int b) {
+      return p.part_ws + ((size_t(u) * TL_WAVES + wave) * (TL_WM * TL_WN) + a * TL_WN + b) * 256 + lane * 4;
+    };
+#pragma unroll
+    for (int a = 0; a < TL_WM; ++a)
+#pragma unroll
+      for (int b = 0; b < TL_WN; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(slot(unit, a, b) + i, acc[a][b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!last_arriver_of(p.part_cnt + item, unsigned(ks), &flag)) {
+      zero();
+      return false;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(p.part_cnt + item, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < ks; ++j) {
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a)
+#pragma unroll
+        for (int b = 0; b < TL_WN; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = __hip_atomic_load(slot(item * ks + j, a, b) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acc[a][b][i] = j == 0 ? v : acc[a][b][i] + v;
+          }
+    }
+    return true;
+  };
+
   // Two k-tiles per trip so the register buffers alternate without copies;
   // one epilogue per item, after its last k-tile.
   for (int it = 0; it < my_items; ++it) {
+    const int unit = item_of(it), nk = k_end(unit) - k_begin(unit);
     int kt = 0;
-    for (; kt + 1 < K; kt += 2) {
+    for (; kt + 1 < nk; kt += 2) {
       step(fa, fb2);
       step(fb2, fa);
     }
-    if (kt < K) {   // odd k-tile count: the next item starts from fb2
+    if (kt < nk) {   // odd k-tile count: the next unit starts from fb2
       step(fa, fb2);
       fa = fb2;
     }
-    epilogue(item_of(it));
+    if (ks == 1 || split_last(unit)) epilogue(unit / ks);
     after_epi = true;
   }
   if constexpr (EPI == EPI_ARGMAX) {
@@ -406,24 +450,55 @@ static void launch_tiled_shape(const GemmParams &p, int grid, hipStream_t s) {
   hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, XS, XROW, TM, TN, S, WGM, WGN>), dim3(grid), dim3(WGM * WGN * 64), 0, s, p);
 }
 
-// Tile choice: 8 x 16 fragments (128 tokens x 256 features) when those
-// items fill at least 3/4 of the compute units, else 4 x 8 (64 x 128); both
-// with 8 wavefronts in a 2 x 4 grid.
+// Tile choice, 8 wavefronts in a 2 x 4 grid:
+//   heads (argmax): TM x 16 fragments with TM even, at most 12: one token
+//     block covering every row when it fits (each weight byte read once),
+//     else 8 or 12, whichever pads the rows less;
+//   others: 8 x 16 (128 tokens x 256 features) when those items fill at
+//     least 3/4 of the compute units, else 4 x 8 (64 x 128), with split-K
+//     when the items still leave half the units idle.
 template <typename T, int EPI, int XS, bool XROW>
 static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   GemmParams p = p0;
   const int cu = p.grid_cap;
   auto blocks = [](int n, int b) { return (n + b - 1) / b; };
-  const bool big = blocks(p.M, 128) * blocks(p.n_tiles, 16) * 4 >= 3 * cu;
-  p.tile_m = big ? 8 : 4;
+  const int mt = blocks(p.M, 16);
+  if (EPI == EPI_ARGMAX) {
+    if (mt <= 12) p.tile_m = (mt + 1) & ~1;
+    else p.tile_m = blocks(mt, 12) * 12 < blocks(mt, 8) * 8 ? 12 : 8;
+    p.n_blocks = blocks(p.n_tiles, 16);
+  } else {
+    const bool big = blocks(p.M, 128) * blocks(p.n_tiles, 16) * 4 >= 3 * cu;
+    p.tile_m = big ? 8 : 4;
+    p.n_blocks = big ? blocks(p.n_tiles, 16) : blocks(p.n_tiles, 8);
+  }
   p.m_blocks = blocks(p.M, 16 * p.tile_m);
-  p.n_blocks = big ? blocks(p.n_tiles, 16) : blocks(p.n_tiles, 8);
-  // grid: a multiple of the 8 XCDs, at most one workgroup per compute unit
   const int items = p.m_blocks * p.n_blocks;
-  int grid = items < cu ? items : cu;
+  // Too few items for the compute units: split each item's k-tiles into
+  // parts of at least 16.
+  p.ksplit = 1;
+  if (EPI != EPI_ARGMAX && p.part_ws && p.part_cnt && 2 * items <= cu) {
+    const int cap = cu < MAX_SPLIT_UNITS ? cu : MAX_SPLIT_UNITS;
+    int ks = cap / items;
+    if (ks > p.k_tiles / 16) ks = p.k_tiles / 16;
+    p.ksplit = ks > 1 ? ks : 1;
+  }
+  // grid: a multiple of the 8 XCDs, at most one workgroup per compute unit
+  const int units = items * p.ksplit;
+  int grid = units < cu ? units : cu;
   grid = grid < TL_XCDS ? TL_XCDS : grid - grid % TL_XCDS;
-  if (big) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
-  else launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
+  if constexpr (EPI == EPI_ARGMAX && XS == 1) {
+    switch (p.tile_m) {
+      case 6: launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s); break;
+      case 8: launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s); break;
+      case 10: launch_tiled_shape<T, EPI, XS, XROW, 10, 16, 2, 4>(p, grid, s); break;
+      default: launch_tiled_shape<T, EPI, XS, XROW, 12, 16, 2, 4>(p, grid, s); break;
+    }
+  } else {
+    if (EPI == EPI_ARGMAX && p.tile_m != 8) return hipErrorInvalidValue;
+    if (p.tile_m == 8) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
+    else launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
+  }
   return hipGetLastError();
 }
 

@@ -51,4 +51,14 @@ __device__ inline bool last_arriver(unsigned *arrive, int *flag) {
   return *flag != 0;
 }
 
+// The same for a count of `total` arrivals at *counter (any workgroups).
+__device__ inline bool last_arriver_of(unsigned *counter, unsigned total, int *flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+  __syncthreads();
+  return *flag != 0;
+}
+
 }  // namespace dflash

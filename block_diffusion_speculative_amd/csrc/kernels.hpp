@@ -17,6 +17,13 @@ static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_COUNTER_BYTES, "key 
 constexpr int MAX_SEGMENTS = 16;
 // Arrival counter of the last-arriver handshakes, at the end of the fixed area.
 constexpr size_t WS_ARRIVE_OFFSET = WS_COUNTER_BYTES - 256;
+// Split-K: at most MAX_SPLIT_UNITS work units per launch, each with a partial
+// tile of at most 128 x 256 fp32 in the workspace, and one arrival count per
+// item (zero between launches) just below the arrive counter.
+constexpr int MAX_SPLIT_UNITS = 256;
+constexpr size_t SPLIT_TILE_BYTES = size_t(128) * 256 * 4;
+constexpr size_t WS_SPLIT_CNT_OFFSET = WS_ARRIVE_OFFSET - MAX_SPLIT_UNITS * 4;
+static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_SPLIT_CNT_OFFSET, "key slots overlap the split counts");
 // The argmax finish and the injection commit run inside the GEMM launch (by
 // its last workgroup to finish) when the launch has at most this many rows.
 constexpr int FUSED_FINISH_ROWS = 64;
@@ -100,9 +107,14 @@ struct GemmParams {
   int *ctx_len_w;             // EPI_KVINJ commit target (the same array as ctx_len)
   // Tiled launches (more than TILED_MIN_ROWS rows): 16-row tiles held by the
   // packed activation buffer (loads past it are clamped), and the output
-  // tile's token fragments (4 or 8; set by the launcher, which also
+  // tile's token fragments (4 to 12; set by the launcher, which also
   // sets m_blocks and n_blocks for the tile it picks).
   int tiled, x_mtiles, tile_m;
+  // Split-K (tiled launches): partial tiles and per-item arrival counts in the
+  // workspace (both null: no split); ksplit is set by the launcher.
+  float *part_ws;
+  unsigned *part_cnt;
+  int ksplit;
 };
 
 // Launches with more rows than this use the tiled kernel (128 x 256 tiles).

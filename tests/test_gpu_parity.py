@@ -18,6 +18,11 @@ pytestmark = pytest.mark.gpu
 
 SMALL_BF16 = C.Dims(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, n_layers=2,
                     intermediate=1024, vocab=4096, n_feat_layers=3, dtype="bf16")
+# Few output tiles over long k ranges: at 80-85 rows every many-row GEMM but
+# the heads splits its k-tiles over workgroups (down projection 8 parts,
+# fc 6, the rest 2).
+SPLIT_BF16 = C.Dims(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, n_layers=2,
+                    intermediate=4096, vocab=4096, n_feat_layers=3, dtype="bf16")
 
 
 def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=True):
@@ -143,6 +148,11 @@ def test_large_vocab_batch16_big_tiles():
     _compare_step(case, 0, [(5 * s) % 17 for s in range(16)], seqs=[0, 7, 15])
 
 
+def test_split_k_batch5():
+    case = Hn.build_case(SPLIT_BF16, 5, [3, 70, 129, 200, 31], seed=13)
+    _compare_step(case, 0, [17, 17, 17, 17, 17])
+
+
 def test_tiny_f32_batch6_tiled():
     d = C.TINY_DRAFT
     case = Hn.build_case(d, 6, [0, 16, 17, 50, 96, 128], seed=10)
@@ -192,14 +202,16 @@ def test_bad_token_sets_status():
     assert g.drafter.read_status() & 2
 
 
-@pytest.mark.parametrize("batch", [1, 2])
-def test_deterministic_repeat(batch):
+@pytest.mark.parametrize("dims,batch", [("small", 1), ("small", 2), ("split", 5)])
+def test_deterministic_repeat(dims, batch):
     """Same inputs, same bits, whatever the workspace held before (batch 1:
     the consumers reduce the norm statistics themselves; batch 2 as well, with
-    two row tiles)."""
-    case = Hn.build_case(SMALL_BF16, batch, [40, 90][:batch], seed=8)
+    two row tiles; batch 5 of the split configuration: split-K partial tiles
+    summed in part order whichever part finishes last)."""
+    d = {"small": SMALL_BF16, "split": SPLIT_BF16}[dims]
+    case = Hn.build_case(d, batch, [40, 90, 7, 130, 64][:batch], seed=8)
     g = Hn.GpuRunner(case)
-    last = I.last_tokens(SMALL_BF16, 8, 0, batch)
+    last = I.last_tokens(d, 8, 0, batch)
     t1 = g.draft(last)
     v1 = g.views()
     g.drafter.ws.fill_(0xFF)   # poison scratch except the counters below
