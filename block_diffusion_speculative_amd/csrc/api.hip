@@ -84,17 +84,21 @@ struct Bump {
   }
 };
 
-// bf16 activations produced inside the step travel as hi + lo planes, except
-// the SwiGLU output, which feeds only the down projection: one plane there
-// (its rounding adds about 0.1% to the MLP output) lets the down projection
-// keep its whole activation chunk in registers.
+// bf16 activations produced inside the step travel as hi + lo planes (about
+// 16 mantissa bits).  The SwiGLU output feeds only the down projection: one
+// bf16 plane there adds about 0.1% to each layer's residual, which over 8
+// layers moves logits by close to the 1e-2 gap at which drafted tokens are
+// decided, so many-row launches (MFMA to spare) carry two planes; launches of
+// at most 64 rows carry one, which lets the down projection keep its whole
+// activation chunk in registers (a second plane would double the activation
+// bytes every workgroup streams there).
 int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
-constexpr int MLP_ACT_PLANES = 1;
+int mlp_act_planes(const dflash_dims *d, int rows) { return rows > TILED_MIN_ROWS ? act_planes(d) : 1; }
 
 struct DraftLayout {
   size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
-  int M, Mp, S, xs;
+  int M, Mp, S, xs, act_xs;  // planes of the packed activations and of the SwiGLU output
   bool rs_inline;  // consumers reduce the RMSNorm tile sums themselves (one row block)
   GemmPlan qkv, o, gu, down, lm;
 };
@@ -126,13 +130,14 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.pq = size_t(batch) * d->n_q_heads * (hd / kt) * 1024;
   L.xa = b.take(L.pa * L.xs);
   L.xo = b.take(L.po * L.xs);
-  L.xact = b.take(L.pact * MLP_ACT_PLANES);
+  L.act_xs = mlp_act_planes(d, L.M);
+  L.xact = b.take(L.pact * L.act_xs);
   L.qbuf = b.take(L.pq * L.xs);
   L.kblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
-  L.part = L.M > TILED_MIN_ROWS ? b.take(MAX_SPLIT_UNITS * SPLIT_TILE_BYTES) : 0;
+  L.part = L.M > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -171,7 +176,7 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
   L.rs_inline = gemm_inline_rs_ok(L.kv.m_blocks, L.kv.MT, H);
-  L.part = rows > TILED_MIN_ROWS ? b.take(MAX_SPLIT_UNITS * SPLIT_TILE_BYTES) : 0;
+  L.part = rows > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -667,7 +672,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     gu.x = wsb + L.xa;
     gu.xs = L.xs;
     gu.x_plane = L.pa;
-    gu.out_planes = MLP_ACT_PLANES;
+    gu.out_planes = L.act_xs;
     gu.out_plane = L.pact;
     gu.out_packed = wsb + L.xact;
     gu.out_kt = I / kt;
@@ -680,7 +685,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     set_split(dn, wsb, L.part);
     dn.w_seg[0] = static_cast<const char *>(lw.w_down);
     dn.x = wsb + L.xact;
-    dn.xs = MLP_ACT_PLANES;
+    dn.xs = L.act_xs;
     dn.x_plane = L.pact;
     dn.out_f32 = h_out;
     dn.resid = h_mid;

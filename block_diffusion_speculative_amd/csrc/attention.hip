@@ -16,8 +16,9 @@
 // statistics exchanged by lane shuffles, and O^T += V^T P^T consumes the
 // probabilities straight from the S^T registers (the V cache layout stores
 // positions in that register order).  q enters as hi + lo planes when XS ==
-// 2; P as one plane (its rounding error, about 0.2% of the output, averages
-// over the keys).  The sub-splits are then merged in LDS with log-sum-exp
+// 2, and so does P for bf16 (two MFMAs per V tile: a single bf16 plane of P
+// adds about 0.1% to every layer's attention output, which compounds over
+// the layers).  The sub-splits are then merged in LDS with log-sum-exp
 // weights, every wavefront taking a slice of its head's channels; a single
 // split writes the output itself, several write (O, running max, running
 // sum) records that attn_merge_kernel combines.
@@ -25,10 +26,6 @@
 #include "kernels.hpp"
 
 namespace dflash {
-
-template <typename T> __device__ inline float round_to(float v);
-template <> __device__ inline float round_to<float>(float v) { return v; }
-template <> __device__ inline float round_to<bf16_t>(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 
 // Zero the elements of a V chunk whose positions are >= nvalid.
 template <typename T> __device__ inline uint4 mask_v_chunk(uint4 v, int g, int nvalid);
@@ -158,19 +155,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     mx = warp_max_xor(mx, 32);
     const float m_new = fmaxf(m_run, mx);
     const float corr = exp2f(m_run - m_new);
-    // Probabilities rounded to T; the row sum uses the rounded values, so the
-    // weights of the output stay normalised.
-    float ph[KTT * 4];
+    // Probabilities as hi + lo planes of T (about 16 mantissa bits for bf16;
+    // fp32 needs one); the row sum takes the fp32 values.
+    float ph[KTT * 4], pl[KTT * 4];
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < KTT * 4; ++e) {
-      ph[e] = round_to<T>(exp2f(sv[e] - m_new));
-      ps += ph[e];
+      const float pe = exp2f(sv[e] - m_new);
+      split2<T>(pe, ph[e], pl[e]);
+      ps += pe;
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     l_run = l_run * corr + ps;
     const uint4 pf = chunk_pack<T>(ph);
+    const uint4 pfl = chunk_pack<T>(pl);
 #pragma unroll
     for (int dv = 0; dv < DV; ++dv) {
       o[dv] *= corr;
@@ -179,6 +178,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       // 0 * NaN would not be)
       if (nvalid < KT) vf = mask_v_chunk<T>(vf, gq, nvalid);
       o[dv] = mma<T>(o[dv], vf, pf);
+      if constexpr (Ty<T>::SIZE == 2) o[dv] = mma<T>(o[dv], vf, pfl);
     }
     m_run = m_new;
   };

@@ -17,12 +17,15 @@ static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_COUNTER_BYTES, "key 
 constexpr int MAX_SEGMENTS = 16;
 // Arrival counter of the last-arriver handshakes, at the end of the fixed area.
 constexpr size_t WS_ARRIVE_OFFSET = WS_COUNTER_BYTES - 256;
-// Split-K: at most MAX_SPLIT_UNITS work units per launch, each with a partial
-// tile of at most 128 x 256 fp32 in the workspace, and one arrival count per
-// item (zero between launches) just below the arrive counter.
+// Split-K: partial tiles in a workspace region of SPLIT_PART_BYTES (tiled
+// launches: at most MAX_SPLIT_UNITS units of at most 128 x 256 fp32), and one
+// arrival count per item (zero between launches, at most MAX_SPLIT_ITEMS)
+// just below the arrive counter.
 constexpr int MAX_SPLIT_UNITS = 256;
 constexpr size_t SPLIT_TILE_BYTES = size_t(128) * 256 * 4;
-constexpr size_t WS_SPLIT_CNT_OFFSET = WS_ARRIVE_OFFSET - MAX_SPLIT_UNITS * 4;
+constexpr size_t SPLIT_PART_BYTES = MAX_SPLIT_UNITS * SPLIT_TILE_BYTES;
+constexpr int MAX_SPLIT_ITEMS = 8192;
+constexpr size_t WS_SPLIT_CNT_OFFSET = WS_ARRIVE_OFFSET - MAX_SPLIT_ITEMS * 4;
 static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_SPLIT_CNT_OFFSET, "key slots overlap the split counts");
 // The argmax finish and the injection commit run inside the GEMM launch (by
 // its last workgroup to finish) when the launch has at most this many rows.
@@ -129,6 +132,7 @@ inline bool gemm_inline_rs_ok(int m_blocks, int MT, int hidden) {
 // Whether a launch keeps its activations resident in registers: one row
 // block and a wavefront K chunk of at most 16 tiles with MT * planes <= 2, or
 // of at most 48 tiles with a single row tile and plane.
+// k_tiles: the k range one workgroup covers (a split part's, with split-K).
 inline bool gemm_resident_ok(int m_blocks, int MT, int planes, int k_tiles) {
   const int per = (k_tiles + 7) / 8;
   return m_blocks == 1 && ((MT * planes <= 2 && per <= 16) || (MT * planes == 1 && per <= 48));

@@ -245,3 +245,31 @@ def test_qwen3_8b_b32_ragged_sampled():
     case = Hn.build_case(w.dims, w.batch, ctx, seed=0, kv_mode="import")
     rep = _compare_step(case, 0, rows, seqs=[0, 13, 31], accept_p=I.workload_geom_p(w), check_cache=False)
     assert rep["tokens"].compared >= 1
+
+
+@pytest.mark.slow
+def test_qwen3_8b_long_context_sampled():
+    """The long-context workload at full shape: 4 sequences of 16384 cached
+    positions (imported), one injected row each; the oracle follows sequences
+    0 and 3."""
+    w = C.get("qwen3-8b-long")
+    ctx = I.context_lengths(w, 0)
+    rows = I.new_row_counts(w, 0, 0)
+    case = Hn.build_case(w.dims, w.batch, ctx, seed=0, kv_mode="import")
+    rep = _compare_step(case, 0, rows, seqs=[0, 3], accept_p=I.workload_geom_p(w), check_cache=False)
+    assert rep["tokens"].compared >= 1
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("block", [4, 8, 16])
+def test_larger_b8_block_sweep_sampled(block):
+    """The larger drafter (hidden 5120, 40/8 heads, 8 layers, intermediate
+    17408) at batch 8 over 8192 cached positions, for block sizes 4, 8 and 16;
+    the oracle follows sequences 0 and 7."""
+    w = C.get("larger-b8")
+    d = w.dims.with_block(block)
+    ctx = I.context_lengths(w, 0)
+    case = Hn.build_case(d, w.batch, ctx, seed=0, kv_mode="import")
+    rows = [1 + (3 * s) % block for s in range(w.batch)]
+    rep = _compare_step(case, 0, rows, seqs=[0, 7], accept_p=I.workload_geom_p(w), check_cache=False)
+    assert rep["tokens"].compared >= 1
