@@ -30,6 +30,30 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 EV_EVERY = 5                   # timed steps per sampled verify-head launch
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_qwen3-8b-b1.md")
+TRAFFIC_SOURCES = ["gemm.hip", "gemm_util.hpp", "common.hpp", "kernels.hpp"]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per verify-head launch from the committed FETCH_SIZE /
+    WRITE_SIZE counter summary, if it covers this workload and the GEMM
+    sources are the ones it was measured on; else None."""
+    if workload != "qwen3-8b-b1" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "block_diffusion_speculative_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "sources_sha256"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("sources_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def log(*a):
@@ -258,7 +282,8 @@ def main(argv=None):
                           "achieved_GBs": round(step_gbs, 1)},
         "roofline": {"kernel": "gemm_kernel<bf16,MT=2,NB=2,ARGMAX> (verify lm_head + argmax + accept)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
                      "bytes_per_launch": lm_bytes, "avg_launch_ms": round(verify_ms, 5)},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
