@@ -137,7 +137,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
-  L.part = L.M > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.part = L.M > TILED_WIDE_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -176,7 +176,7 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
   L.rs_inline = gemm_inline_rs_ok(L.kv.m_blocks, L.kv.MT, H);
-  L.part = rows > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.part = rows > TILED_WIDE_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -289,7 +289,7 @@ hipError_t set_norm_in(GemmParams &p, bool inline_rs, const float *ssq, float *r
   p.rs_tiles = H / 16;
   p.rs_K = H;
   p.rs_eps = eps;
-  if (inline_rs) {
+  if (inline_rs && !p.tiled) {   // the tiled kernel reads per-row scales only
     p.rs_ssq = ssq;
     return hipSuccess;
   }
@@ -297,11 +297,12 @@ hipError_t set_norm_in(GemmParams &p, bool inline_rs, const float *ssq, float *r
   return launch_rstd(ssq, H / 16, H, eps, M, rs, stream);
 }
 
-// The head GEMM with its argmax finish: inside the launch (last arriver) for
-// at most FUSED_FINISH_ROWS rows, else as a follow-up kernel per sequence.
+// The head GEMM with its argmax finish: inside the launch (last arriver of
+// the skinny kernel) for at most FUSED_FINISH_ROWS rows, else as a follow-up
+// kernel per sequence.
 int launch_argmax_head(int dtype, GemmParams &lm, const ArgmaxFinishParams &fp, char *wsb, int batch,
                        hipStream_t stream, const char *what) {
-  const bool fused = lm.M <= FUSED_FINISH_ROWS;
+  const bool fused = !lm.tiled && lm.M <= FUSED_FINISH_ROWS;
   if (fused) {
     lm.arrive = reinterpret_cast<unsigned *>(wsb + WS_ARRIVE_OFFSET);
     lm.fin = fp;
@@ -335,8 +336,9 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.out_planes = 1;
   // packed activation buffers hold whole row blocks of the row-tile plan
   p.x_mtiles = g.m_blocks * g.MT;
-  // many-row launches go to the tiled kernel, which picks its tile shape
-  if (g.M > TILED_MIN_ROWS) p.tiled = 1;
+  // many-row (and wide mid-size) launches go to the tiled kernel, which
+  // picks its tile shape
+  if (gemm_tiled(g.M, g.n_tiles)) p.tiled = 1;
 }
 
 }  // namespace

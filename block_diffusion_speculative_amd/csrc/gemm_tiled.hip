@@ -489,6 +489,7 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   grid = grid < TL_XCDS ? TL_XCDS : grid - grid % TL_XCDS;
   if constexpr (EPI == EPI_ARGMAX && XS == 1) {
     switch (p.tile_m) {
+      case 4: launch_tiled_shape<T, EPI, XS, XROW, 4, 16, 2, 4>(p, grid, s); break;
       case 6: launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s); break;
       case 8: launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s); break;
       case 10: launch_tiled_shape<T, EPI, XS, XROW, 10, 16, 2, 4>(p, grid, s); break;

@@ -108,7 +108,7 @@ struct GemmParams {
   unsigned *arrive;
   ArgmaxFinishParams fin;
   int *ctx_len_w;             // EPI_KVINJ commit target (the same array as ctx_len)
-  // Tiled launches (more than TILED_MIN_ROWS rows): 16-row tiles held by the
+  // Tiled launches (gemm_tiled holds): 16-row tiles held by the
   // packed activation buffer (loads past it are clamped), and the output
   // tile's token fragments (4 to 12; set by the launcher, which also
   // sets m_blocks and n_blocks for the tile it picks).
@@ -120,8 +120,16 @@ struct GemmParams {
   int ksplit;
 };
 
-// Launches with more rows than this use the tiled kernel (128 x 256 tiles).
+// Launches with more rows than TILED_MIN_ROWS use the tiled kernel; so do
+// wide ones (at least TILED_WIDE_NTILES output tiles: the heads, gate/up) with
+// more than TILED_WIDE_MIN_ROWS rows, where the skinny kernel's activation
+// stream per item outweighs the tiled kernel's LDS traffic.
 constexpr int TILED_MIN_ROWS = 64;
+constexpr int TILED_WIDE_MIN_ROWS = 48;
+constexpr int TILED_WIDE_NTILES = 1024;
+inline bool gemm_tiled(int rows, int n_tiles) {
+  return rows > TILED_MIN_ROWS || (rows > TILED_WIDE_MIN_ROWS && n_tiles >= TILED_WIDE_NTILES);
+}
 
 // Whether a consumer can reduce the RMSNorm tile sums itself: one row block
 // whose rows x tiles fit the 8192-float LDS stage.
