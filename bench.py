@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
-EV_EVERY = 5                   # timed steps per sampled verify-head launch
+EV_EVERY = 20                  # timed steps per sampled verify-head launch
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_qwen3-8b-b1.md")
 TRAFFIC_SOURCES = ["gemm.hip", "gemm_util.hpp", "common.hpp", "kernels.hpp"]
 

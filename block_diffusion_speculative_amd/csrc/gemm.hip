@@ -600,15 +600,6 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const ArgmaxFinishPa
   }
 }
 
-// Commit the injected rows: ctx_len[s] += n_s unless that exceeds capacity
-// (the injection skipped such a sequence and flagged it).
-__global__ __launch_bounds__(64) void commit_rows_kernel(int *ctx_len, const int *cu_new, int batch, int capacity) {
-  for (int s = threadIdx.x; s < batch; s += blockDim.x) {
-    const int ns = cu_new[s + 1] - cu_new[s];
-    if (ctx_len[s] + ns <= capacity) ctx_len[s] += ns;
-  }
-}
-
 template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
 static hipError_t launch_one(const GemmParams &p, hipStream_t s) {
   const int items = p.m_blocks * p.n_blocks;
@@ -681,11 +672,6 @@ hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s) {
 
 hipError_t launch_argmax_finish(const ArgmaxFinishParams &p, int batch, hipStream_t s) {
   hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_commit_rows(int *ctx_len, const int *cu_new, int batch, int capacity, hipStream_t s) {
-  hipLaunchKernelGGL(commit_rows_kernel, dim3(1), dim3(64), 0, s, ctx_len, cu_new, batch, capacity);
   return hipGetLastError();
 }
 

@@ -184,7 +184,6 @@ struct EmbedParams {
 hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s);
 hipError_t launch_gemm_tiled(int dtype, int epi, const GemmParams &p, hipStream_t s);
 hipError_t launch_argmax_finish(const ArgmaxFinishParams &p, int batch, hipStream_t s);
-hipError_t launch_commit_rows(int *ctx_len, const int *cu_new, int batch, int capacity, hipStream_t s);
 hipError_t launch_attention(int dtype, const AttnParams &p, int batch, hipStream_t s);
 hipError_t launch_attn_merge(int dtype, const AttnParams &p, int batch, hipStream_t s);
 hipError_t launch_embed(int dtype, const EmbedParams &p, hipStream_t s);
