@@ -34,6 +34,38 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_qwen3-8b-
 TRAFFIC_SOURCES = ["gemm.hip", "gemm_util.hpp", "common.hpp", "kernels.hpp"]
 
 
+def time_graph(args, torch, b: int, rewind, run, outs):
+    """The same step captured once in a HIP graph and replayed: warmup
+    replays, then `steps` timed replays.  The replays' outputs must equal the
+    eager step's (the step is deterministic)."""
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rewind()
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rewind()
+        run()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    ms = g0.elapsed_time(g1) / args.steps
+    match = all(bool(torch.equal(o, r)) for o, r in zip(outs, ref))
+    return {"ms_per_step": round(ms, 4), "value": round(b * 1000.0 / ms, 2), "outputs_match": match}
+
+
 def measured_traffic(workload: str):
     """HBM bytes per verify-head launch from the committed FETCH_SIZE /
     WRITE_SIZE counter summary, if it covers this workload and the GEMM
@@ -101,6 +133,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="qwen3-8b-b1")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (reported under 'graph')")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (reference dispatch for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -202,11 +236,14 @@ def main(argv=None):
     ev_v0 = {i: torch.cuda.Event(enable_timing=True) for i in ev_idx}
     ev_v1 = {i: torch.cuda.Event(enable_timing=True) for i in ev_idx}
 
-    def step(i=None):
+    def rewind():
         if ctx_uniform is not None:
             dr_gpu.ctx_len[:b].fill_(ctx_uniform)
         else:
-            dr_gpu.ctx_len[:b].copy_(ctx0)
+            torch.add(ctx0, 0, out=dr_gpu.ctx_len[:b])
+
+    def step(i=None):
+        rewind()
         dr_gpu.inject(feats_t, cu, b, R)
         dr_gpu.draft(last_t, draft_out, b)
         timed = i is not None and i in ev_v0
@@ -238,6 +275,12 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = e0.elapsed_time(e1)
+    graph_res = None
+    if args.graph:
+        graph_res = time_graph(args, torch, b, rewind, lambda: (dr_gpu.inject(feats_t, cu, b, R),
+                                                               dr_gpu.draft(last_t, draft_out, b),
+                                                               dr_gpu.verify(th, draft_out, tgt, acc, bonus, b)),
+                               [draft_out, tgt, acc, bonus])
     ms_step = ms_total / args.steps
     verify_ms = float(np.mean([ev_v0[i].elapsed_time(ev_v1[i]) for i in ev_idx]))
     status = dr_gpu.read_status()
@@ -286,6 +329,7 @@ def main(argv=None):
                      "traffic": measured_traffic(args.workload),
                      "bytes_per_launch": lm_bytes, "avg_launch_ms": round(verify_ms, 5)},
         "cpu_baseline": cpu,
+        "graph": graph_res,
         "wall_s_timed": round(wall, 4),
         "accept": {"mean_len": float(np.mean(got_acc)), "planted_mean": float(np.mean(L_plant))},
         "draft_matches_oracle": match,

@@ -273,3 +273,61 @@ def test_larger_b8_block_sweep_sampled(block):
     rows = [1 + (3 * s) % block for s in range(w.batch)]
     rep = _compare_step(case, 0, rows, seqs=[0, 7], accept_p=I.workload_geom_p(w), check_cache=False)
     assert rep["tokens"].compared >= 1
+
+
+@pytest.mark.parametrize("batch", [2, 5])
+def test_graph_replay_matches_eager(batch):
+    """One inject + draft + verify step captured in a HIP graph and replayed
+    three times, with eager steps and synchronisations between the replays:
+    every replay's drafted tokens, target argmax, accept lengths, fallback
+    tokens and ctx_len equal the eager step's (batch 2: skinny GEMMs with the
+    fused argmax and commit tails; batch 5: tiled GEMMs, split-K, rstd and
+    the argmax finish kernel)."""
+    import torch
+    d = SPLIT_BF16 if batch == 5 else SMALL_BF16
+    case = Hn.build_case(d, batch, [40, 90, 7, 130, 64][:batch], seed=14)
+    g = Hn.GpuRunner(case)
+    dr, dev = g.drafter, g.drafter.device
+    B, H = d.block_size, d.hidden
+    rows = [17] * batch
+    ft = g.upload(np.concatenate([I.features(d, 14, 0, s, 17) for s in range(batch)]), dr.dt, dev)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)).to(dev)
+    last = torch.as_tensor(I.last_tokens(d, 14, 0, batch).astype(np.int32)).to(dev)
+    hid = I.stream(14, 99, 1).standard_normal((batch * (B + 1), H)).astype(np.float32)
+    th = g.upload(hid, dr.dt, dev).reshape(batch, B + 1, H)
+    ctx0 = torch.as_tensor(np.asarray(case.ctx, dtype=np.int32)).to(dev)
+    out = torch.empty((batch, B), dtype=torch.int32, device=dev)
+    ta = torch.empty((batch, B + 1), dtype=torch.int32, device=dev)
+    al = torch.empty(batch, dtype=torch.int32, device=dev)
+    bo = torch.empty(batch, dtype=torch.int32, device=dev)
+
+    def step():
+        torch.add(ctx0, 0, out=dr.ctx_len[:batch])   # a kernel, not a copy node
+        dr.inject(ft, cu, batch, int(np.sum(rows)))
+        dr.draft(last, out, batch)
+        dr.verify(th, out, ta, al, bo, batch)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (out, ta, al, bo, dr.ctx_len[:batch])]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for x in (out, ta, al, bo):
+            x.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((out, ta, al, bo, dr.ctx_len[:batch]), ref):
+            assert torch.equal(got, want)
+        step()
+        torch.cuda.synchronize()
+        for got, want in zip((out, ta, al, bo), ref[:4]):
+            assert torch.equal(got, want)
