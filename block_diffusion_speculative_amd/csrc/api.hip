@@ -88,12 +88,15 @@ struct Bump {
 // 16 mantissa bits).  The SwiGLU output feeds only the down projection: one
 // bf16 plane there adds about 0.1% to each layer's residual, which over 8
 // layers moves logits by close to the 1e-2 gap at which drafted tokens are
-// decided, so many-row launches (MFMA to spare) carry two planes; launches of
-// at most 64 rows carry one, which lets the down projection keep its whole
-// activation chunk in registers (a second plane would double the activation
-// bytes every workgroup streams there).
+// decided, so launches of more than one 16-row tile carry two planes; a
+// single row tile (one sequence of a 16-slot block) carries one, which lets
+// the down projection keep its whole activation chunk in registers (a second
+// plane would double the activation bytes every workgroup streams there).
+// At 64 rows over 16384 cached positions a single plane left a drafted token
+// with a 0.0108 logit gap on the wrong side.
+constexpr int MLP_ONE_PLANE_ROWS = 16;
 int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
-int mlp_act_planes(const dflash_dims *d, int rows) { return rows > TILED_MIN_ROWS ? act_planes(d) : 1; }
+int mlp_act_planes(const dflash_dims *d, int rows) { return rows > MLP_ONE_PLANE_ROWS ? act_planes(d) : 1; }
 
 struct DraftLayout {
   size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, end;
