@@ -30,6 +30,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 EV_EVERY = 20                  # timed steps per sampled verify-head launch
+# Cost model of the speedup ("Term: DFlash speculative decoding", section
+# "Mathematical view of acceptance and speedup": S ~ C_AR * E[L] / C_DF).
+# The target itself is not built here: its pass is modeled as streaming the
+# bf16 weights of an 8-billion-parameter model (the pages' Qwen3-8B) once at
+# the HBM rate the verify head measures in the same run.
+TARGET_PARAMS = 8.0e9
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_qwen3-8b-b1.md")
 TRAFFIC_SOURCES = ["gemm.hip", "gemm_util.hpp", "common.hpp", "kernels.hpp"]
 
@@ -325,6 +331,20 @@ def main(argv=None):
     t_mfma = model["flops"] / (BF16_PEAK_TFLOPS * 1e12)
     t_roof = max(t_hbm, t_mfma)
     value = b * 1000.0 / ms_step
+    # S = C_AR * E / C_DF: C_AR is one autoregressive target step, C_DF one
+    # draft-and-verify step (this step plus the target's verify pass over the
+    # block), E the tokens a step commits on average: E[L] of the planted
+    # acceptance, and E[L] + 1 with the fallback token.
+    t_target_ms = TARGET_PARAMS * 2 / (lm_bytes / (verify_ms * 1e-3)) * 1e3
+    e_l = I.geometric_mean_accept(p_acc, B)
+    c_df = ms_step + t_target_ms
+    cost = {"source": "S = C_AR * E / C_DF with C_AR = t_target, C_DF = t_step + t_target",
+            "t_step_ms": round(ms_step, 4),
+            "t_target_ms_modeled": round(t_target_ms, 4),
+            "target": f"{TARGET_PARAMS:.0e} bf16 parameters streamed at the verify head's measured rate",
+            "E_L_planted": round(e_l, 4),
+            "S_with_E_L": round(t_target_ms * e_l / c_df, 3),
+            "S_with_E_L_plus_bonus": round(t_target_ms * (e_l + 1) / c_df, 3)}
     out = {
         "metric": "draft+verify block-steps/s (B=16)",
         "value": round(value, 2),
@@ -350,6 +370,7 @@ def main(argv=None):
                           "achieved_GBs": round(step_gbs, 1)},
         "roofline": lm_roof,
         "cpu_baseline": cpu,
+        "cost_model": cost,
         "graph": graph_res,
         "wall_s_timed": round(wall, 4),
         # Targets are planted against the oracle's drafted tokens; without the
