@@ -36,7 +36,10 @@ EV_EVERY = 20                  # timed steps per sampled verify-head launch
 # bf16 weights of an 8-billion-parameter model (the pages' Qwen3-8B) once at
 # the HBM rate the verify head measures in the same run.
 TARGET_PARAMS = 8.0e9
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_qwen3-8b-b1.md")
+# Calibrated HBM bytes of the verify head per workload, with the kernel
+# sources they were measured on (files that name no sources were taken on
+# the skinny GEMM's).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_{}.md")
 TRAFFIC_SOURCES = ["gemm.hip", "gemm_util.hpp", "common.hpp", "kernels.hpp"]
 
 
@@ -74,21 +77,22 @@ def time_graph(args, torch, b: int, rewind, run, outs):
 
 def measured_traffic(workload: str):
     """HBM bytes per verify-head launch from the committed FETCH_SIZE /
-    WRITE_SIZE counter summary, if it covers this workload and the GEMM
-    sources are the ones it was measured on; else None."""
-    if workload != "qwen3-8b-b1" or not os.path.exists(TRAFFIC_FILE):
+    WRITE_SIZE counter summary of this workload, if there is one and the
+    kernel sources it lists are the ones it was measured on; else None."""
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
     import hashlib
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "block_diffusion_speculative_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
     vals = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
-            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "sources_sha256"):
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "sources", "sources_sha256"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in vals.get("sources", " ".join(TRAFFIC_SOURCES)).split():
+        with open(os.path.join(ROOT, "block_diffusion_speculative_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
     if vals.get("sources_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
         return None
     return int(vals["traffic_bytes_per_launch"])
