@@ -235,8 +235,13 @@ def main(argv=None):
     tgt = torch.empty((b, B + 1), dtype=torch.int32, device=dev)
     acc = torch.empty(b, dtype=torch.int32, device=dev)
     bonus = torch.empty(b, dtype=torch.int32, device=dev)
-    # Every timed step rolls the context back to its starting length, so the
-    # workload stays fixed; a uniform length is one fill, a ragged one a copy.
+    # Every step must start from the configured context lengths, so the
+    # workload stays fixed.  Each timed step gets its own copy of the lengths,
+    # made before the timed region (the injection appends at the same
+    # positions every step, and only the lengths it commits differ), so the
+    # timed region holds the step's launches only.  Warm-up steps and graph
+    # replays roll the drafter's own lengths back instead (a uniform length is
+    # one fill, a ragged one a copy).
     ctx_uniform = int(ctx[0]) if bool(np.all(ctx == ctx[0])) else None
     # The verify head is bracketed by a pair of events on every EV_EVERY-th
     # timed step: an event record is a barrier packet on the stream (about
@@ -252,8 +257,14 @@ def main(argv=None):
         else:
             torch.add(ctx0, 0, out=dr_gpu.ctx_len[:b])
 
+    ctx_fresh = torch.zeros((args.steps, dr_gpu.ckv.max_batch), dtype=torch.int32, device=dev)
+    ctx_fresh[:, :b] = ctx0.to(torch.int32)
+
     def step(i=None):
-        rewind()
+        if i is None:
+            rewind()
+        else:
+            dr_gpu.bind_ctx_len(ctx_fresh[i])
         dr_gpu.inject(feats_t, cu, b, R)
         dr_gpu.draft(last_t, draft_out, b)
         timed = i is not None and i in ev_v0
@@ -284,6 +295,7 @@ def main(argv=None):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    dr_gpu.bind_ctx_len(None)
     ms_total = e0.elapsed_time(e1)
     graph_res = None
     if args.graph:

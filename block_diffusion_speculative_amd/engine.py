@@ -175,6 +175,16 @@ class Drafter:
                   v.data_ptr(), _stream_ptr(stream))
         return k, v
 
+    def bind_ctx_len(self, ctx_len: Optional[torch.Tensor] = None):
+        """Point the cache's per-sequence context lengths at another int32
+        device array of max_batch entries (None: back to the drafter's own).
+        The K/V rows stay shared; only where lengths are read and committed
+        changes."""
+        t = self.ctx_len if ctx_len is None else ctx_len
+        assert t.dtype == torch.int32 and t.device == self.device and t.numel() >= self.ckv.max_batch
+        self.ckv.ctx_len = t.data_ptr()
+        self._bound_ctx = t   # keep the array alive while bound
+
     def set_ctx_len(self, lens: Sequence[int]):
         t = torch.as_tensor(np.asarray(lens, dtype=np.int32))
         self.ctx_len[:len(t)].copy_(t)
