@@ -153,6 +153,23 @@ def test_split_k_batch5():
     _compare_step(case, 0, [17, 17, 17, 17, 17])
 
 
+def test_max_batch64():
+    """The largest batch the library takes (64 sequences: 1024 draft rows and
+    1088 verify rows, every argmax key slot row in use), ragged contexts and
+    injections; the oracle follows three sequences."""
+    ctx = [(7 * s) % 100 for s in range(64)]
+    case = Hn.build_case(SMALL_BF16, 64, ctx, seed=23)
+    rep = _compare_step(case, 0, [1 + s % 17 for s in range(64)], seqs=[0, 33, 63])
+    assert rep["tokens"].compared >= 1
+
+
+def test_inject_exactly_to_capacity():
+    """An injection that fills the cache to its last position is accepted
+    (no status bit) and the draft reads every cached position."""
+    case = Hn.build_case(SMALL_BF16, 1, [20], seed=24, capacity=32)
+    _compare_step(case, 0, [12])
+
+
 def test_tiny_f32_batch6_tiled():
     d = C.TINY_DRAFT
     case = Hn.build_case(d, 6, [0, 16, 17, 50, 96, 128], seed=10)
