@@ -176,6 +176,51 @@ def test_tiny_f32_batch6_tiled():
     _compare_step(case, 0, [12, 1, 17, 9, 16, 15])
 
 
+@pytest.mark.parametrize("dims", ["small", "tiny"])
+def test_decode_loop_four_steps(dims):
+    """Four draft-and-verify steps in a row, as a decoder runs them: each
+    step injects the L + 1 rows the previous one committed (the first step
+    one row), drafts from the previous fallback token at the grown context,
+    and verifies targets planted on the oracle's drafted tokens.  Context
+    lengths follow the oracle exactly, accept lengths and fallback tokens
+    wherever the positions deciding them are above the 1e-2 gap, drafted
+    tokens wherever the oracle's gap exceeds 1e-2."""
+    d = {"small": SMALL_BF16, "tiny": C.TINY_DRAFT}[dims]
+    b, B, seed, p_acc = 2, d.block_size, 30, 0.12
+    ctx0 = [40, 70]
+    case = Hn.build_case(d, b, ctx0, seed=seed, capacity=C.kv_capacity(max(ctx0) + 4 * 17))
+    gpu = Hn.GpuRunner(case)
+    cache = Hn.oracle_prefill(case, list(range(b)))
+    rows = np.ones(b, dtype=np.int64)
+    last = I.last_tokens(d, seed, 0, b)
+    tr = Hn.TokenReport()
+    for step in range(4):
+        feats = [I.features(d, seed, step + 1, s, int(rows[s])) for s in range(b)]
+        gpu.inject(feats)
+        O.inject(d, case.weights, cache, feats)
+        assert np.array_equal(gpu.ctx_len()[:b], cache.length), (step, gpu.ctx_len()[:b], cache.length)
+        got = gpu.draft(last)
+        ref = O.draft_forward(d, case.weights, cache, last)
+        tr.add(got, ref["tokens"], ref["gaps"], f"draft{step}")
+        L_plant = I.planted_accept(seed, step, b, p_acc, B)
+        _, hid = I.planted_targets(d, seed, step, case.weights.lm_head, ref["tokens"], L_plant)
+        ta, al, bo = gpu.verify(hid, ref["tokens"].astype(np.int32))
+        g_ref, vgaps = O.verify(d, case.weights.lm_head, hid)
+        L_ref, bonus_ref = O.accept(ref["tokens"], g_ref)
+        tr.add(ta, g_ref, vgaps, f"verify{step}")
+        assert np.array_equal(L_ref, L_plant)
+        for s_ in range(b):
+            if np.all(vgaps[s_, :min(int(L_ref[s_]), B) + 1] > Hn.GAP):   # decided above the gap
+                assert al[s_] == L_ref[s_] and bo[s_] == bonus_ref[s_], (step, s_, al, L_ref, bo, bonus_ref)
+        # both sides go on from the oracle's commit
+        rows = L_ref + 1
+        last = bonus_ref.astype(np.int32)
+    assert gpu.drafter.read_status() == 0
+    assert not tr.mismatched, tr.mismatched
+    assert tr.compared > 0
+    print("compared", tr.compared, "below_gap", tr.below_gap, "ctx", cache.length)
+
+
 @pytest.mark.parametrize("rows,split", [(12, 5), (20, 7)])
 def test_incremental_injection_matches_single(rows, split):
     """Injecting rows in two calls equals one call (positions and append
