@@ -378,8 +378,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   // which part finished last, resets the count and runs the epilogue.
   auto split_last = [&](int unit) -> bool {
     const int item = unit / ks;
+    // Fragment (a, b) of a wavefront is 256 floats; element i of every lane
+    // is a run of 64 consecutive floats, so each coherent store and load
+    // instruction moves one contiguous 256-byte run.
     auto slot = [&](int u, int a, int b) {
-      return p.part_ws + ((size_t(u) * TL_WAVES + wave) * (TL_WM * TL_WN) + a * TL_WN + b) * 256 + lane * 4;
+      return p.part_ws + ((size_t(u) * TL_WAVES + wave) * (TL_WM * TL_WN) + a * TL_WN + b) * 256 + lane;
     };
 #pragma unroll
     for (int a = 0; a < TL_WM; ++a)
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
       for (int b = 0; b < TL_WN; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(slot(unit, a, b) + i, acc[a][b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(slot(unit, a, b) + i * 64, acc[a][b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!last_arriver_of(p.part_cnt + item, unsigned(ks), &flag)) {
       zero();
       return false;
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
         for (int b = 0; b < TL_WN; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = __hip_atomic_load(slot(item * ks + j, a, b) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float v = __hip_atomic_load(slot(item * ks + j, a, b) + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             acc[a][b][i] = j == 0 ? v : acc[a][b][i] + v;
           }
     }
