@@ -474,19 +474,51 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     rs_issue();
     __builtin_amdgcn_sched_barrier(0);
     issue_w(item_of(0), 0, wb[0]);
-    // Activations of this wavefront's chunk, loaded once (one row block).
+    // Activations of this wavefront's chunk, loaded once (one row block) and
+    // kept for every item: up to 16 tiles, the first batch's now and each
+    // further batch beside the first item's weight batch before it, so the
+    // chunk arrives with the first item's weight stream instead of ahead of
+    // it.
     uint4 xr[KC][MT][XS];
+    auto load_x = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int kt = min(k0 + j, kclamp);
+      for (int u = 0; u < U; ++u) {
+        const int kt = min(k0 + b * U + u, kclamp);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int xp = 0; xp < XS; ++xp) xr[j][mt][xp] = x_load(mt, kt, xp);
+          for (int xp = 0; xp < XS; ++xp) xr[b * U + u][mt][xp] = x_load(mt, kt, xp);
+      }
+    };
+    // (A 48-tile chunk leaves no registers for the peeled first item: it is
+    // loaded whole, up front.)
+    constexpr bool PROGRESSIVE = KC <= 16;
+    if constexpr (PROGRESSIVE) {
+      load_x(0);
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBAT; ++b) load_x(b);
     }
     __builtin_amdgcn_sched_barrier(0);
     rs_stage_store();
-    for (int i = 0; i < my_items; ++i) {
+    if (PROGRESSIVE && my_items > 0) {
+      const int item = item_of(0);
+      const int next = item_of(min(1, my_items - 1));
+#pragma unroll
+      for (int b = 0; b < NBAT; ++b) {
+        if (b + 1 < NBAT) {
+          issue_w(item, b + 1, wb[(b + 1) & 1]);
+          load_x(b + 1);
+        } else {
+          issue_w(next, 0, wb[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
+#pragma unroll
+        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0);
+      }
+      finish_item(item);
+    }
+    for (int i = PROGRESSIVE ? 1 : 0; i < my_items; ++i) {
       const int item = item_of(i);
       const int next = item_of(min(i + 1, my_items - 1));
 #pragma unroll
