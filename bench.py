@@ -146,6 +146,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3-8b-b1")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--block-size", type=int, default=0, metavar="B",
+                    help="block size B of the step (one of the workload's sweep sizes; default its largest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (reported under 'graph')")
@@ -158,16 +160,22 @@ def main(argv=None):
               "no exchange; see the design notes).  Run with --gpus 1.", file=sys.stderr)
         return 2
 
-    import torch
     from block_diffusion_speculative_amd import configs as C
+    w = C.get(args.workload)
+    d = w.dims
+    if args.block_size:
+        if args.block_size not in w.block_sizes:
+            log(f"block size {args.block_size} is not swept on {args.workload} (sizes {w.block_sizes})")
+            return 2
+        d = d.with_block(args.block_size)
+
+    import torch
     from block_diffusion_speculative_amd import inputs as I
     from block_diffusion_speculative_amd.engine import Drafter, upload
 
     if not torch.cuda.is_available():
         log("no GPU visible")
         return 1
-    w = C.get(args.workload)
-    d = w.dims
     B = d.block_size
     b = w.batch
     seed = args.seed
@@ -178,7 +186,8 @@ def main(argv=None):
     if w.new_rows is not None:
         rows = I.new_row_counts(w, seed, 0)
     else:
-        rows = np.full(b, int(round(w.mean_accept)) + 1, dtype=np.int32)
+        # a step commits at most B + 1 rows (B accepted drafts and the fallback token)
+        rows = np.full(b, min(int(round(w.mean_accept)) + 1, B + 1), dtype=np.int32)
     cap = C.kv_capacity(int(ctx.max()))
     p_acc = I.workload_geom_p(w)
 
@@ -376,7 +385,7 @@ def main(argv=None):
             "S_with_E_L": round(t_target_ms * e_l / c_df, 3),
             "S_with_E_L_plus_bonus": round(t_target_ms * (e_l + 1) / c_df, 3)}
     out = {
-        "metric": "draft+verify block-steps/s (B=16)",
+        "metric": f"draft+verify block-steps/s (B={B})",
         "value": round(value, 2),
         "unit": "block-steps/s",
         "n_gpus": 1,

@@ -84,3 +84,10 @@ def test_traffic_lookup_follows_the_sources(tmp_path, monkeypatch):
             h2.update(fh.read())
     _write_summary(tmp_path / "traffic_default.md", 42, None, h2.hexdigest())
     assert bench.measured_traffic("default") == 42
+
+
+def test_block_size_outside_the_sweep_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "qwen3-8b-b1",
+                        "--block-size", "4"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "not swept" in r.stderr and r.stdout == ""
