@@ -140,7 +140,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
-  L.part = L.M > TILED_WIDE_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.part = L.M > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -179,7 +179,7 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
   L.rs_inline = gemm_inline_rs_ok(L.kv.m_blocks, L.kv.MT, H);
-  L.part = rows > TILED_WIDE_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.part = rows > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -339,9 +339,9 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.out_planes = 1;
   // packed activation buffers hold whole row blocks of the row-tile plan
   p.x_mtiles = g.m_blocks * g.MT;
-  // many-row (and wide mid-size) launches go to the tiled kernel, which
+  // launches of more than 48 rows go to the tiled kernel, which
   // picks its tile shape
-  if (gemm_tiled(g.M, g.n_tiles)) p.tiled = 1;
+  if (gemm_tiled(g.M)) p.tiled = 1;
 }
 
 }  // namespace

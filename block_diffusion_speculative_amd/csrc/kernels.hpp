@@ -120,16 +120,12 @@ struct GemmParams {
   int ksplit;
 };
 
-// Launches with more rows than TILED_MIN_ROWS use the tiled kernel; so do
-// wide ones (at least TILED_WIDE_NTILES output tiles: the heads, gate/up) with
-// more than TILED_WIDE_MIN_ROWS rows, where the skinny kernel's activation
-// stream per item outweighs the tiled kernel's LDS traffic.
-constexpr int TILED_MIN_ROWS = 64;
-constexpr int TILED_WIDE_MIN_ROWS = 48;
-constexpr int TILED_WIDE_NTILES = 1024;
-inline bool gemm_tiled(int rows, int n_tiles) {
-  return rows > TILED_MIN_ROWS || (rows > TILED_WIDE_MIN_ROWS && n_tiles >= TILED_WIDE_NTILES);
-}
+// Launches with more than TILED_MIN_ROWS rows use the tiled kernel: from four
+// row tiles on, the skinny kernel's activation stream per item (every row
+// tile and plane through each workgroup) outweighs the tiled kernel's LDS
+// traffic and, for the narrow GEMMs, its split-K partial tiles.
+constexpr int TILED_MIN_ROWS = 48;
+inline bool gemm_tiled(int rows) { return rows > TILED_MIN_ROWS; }
 
 // Whether a consumer can reduce the RMSNorm tile sums itself: one row block
 // whose rows x tiles fit the 8192-float LDS stage.
