@@ -32,6 +32,16 @@ size_t packed_bytes(int dtype, long long rows, long long cols) {
 
 constexpr int MAX_BATCH = 64;
 
+// Launches with more than TILED_MIN_ROWS rows use the tiled kernel: from
+// three row tiles on, the skinny kernel's activation stream per item (every
+// row tile and plane through each workgroup) outweighs the tiled kernel's LDS
+// traffic and split-K partial tiles.  Launches of up to 32 rows stay on the
+// skinny kernel, whose summation order is the same for every row count up to
+// 32, so an injection split over two such calls writes the same cache bits
+// as one call.
+constexpr int TILED_MIN_ROWS = 32;
+static bool gemm_tiled(int rows) { return rows > TILED_MIN_ROWS; }
+
 struct GemmPlan {
   int M, N, K;
   int MT, NB, m_tiles, m_blocks, n_tiles, n_blocks, k_tiles;
@@ -339,7 +349,7 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.out_planes = 1;
   // packed activation buffers hold whole row blocks of the row-tile plan
   p.x_mtiles = g.m_blocks * g.MT;
-  // launches of more than 48 rows go to the tiled kernel, which
+  // launches of more than 32 rows go to the tiled kernel, which
   // picks its tile shape
   if (gemm_tiled(g.M)) p.tiled = 1;
 }

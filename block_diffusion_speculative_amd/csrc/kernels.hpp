@@ -120,13 +120,6 @@ struct GemmParams {
   int ksplit;
 };
 
-// Launches with more than TILED_MIN_ROWS rows use the tiled kernel: from four
-// row tiles on, the skinny kernel's activation stream per item (every row
-// tile and plane through each workgroup) outweighs the tiled kernel's LDS
-// traffic and, for the narrow GEMMs, its split-K partial tiles.
-constexpr int TILED_MIN_ROWS = 48;
-inline bool gemm_tiled(int rows) { return rows > TILED_MIN_ROWS; }
-
 // Whether a consumer can reduce the RMSNorm tile sums itself: one row block
 // whose rows x tiles fit the 8192-float LDS stage.
 inline bool gemm_inline_rs_ok(int m_blocks, int MT, int hidden) {
