@@ -32,25 +32,29 @@ size_t packed_bytes(int dtype, long long rows, long long cols) {
 
 constexpr int MAX_BATCH = 64;
 
-// Launches with more than TILED_MIN_ROWS rows use the tiled kernel: from
-// three row tiles on, the skinny kernel's activation stream per item (every
-// row tile and plane through each workgroup) outweighs the tiled kernel's LDS
-// traffic and split-K partial tiles.  Launches of up to 32 rows stay on the
-// skinny kernel, whose summation order is the same for every row count up to
-// 32, so an injection split over two such calls writes the same cache bits
-// as one call.
-constexpr int TILED_MIN_ROWS = 32;
-static bool gemm_tiled(int rows) { return rows > TILED_MIN_ROWS; }
+// Launches of more rows than these use the tiled kernel: from two row tiles
+// on, the skinny kernel's activation stream per item (every row tile and
+// plane through each workgroup) outweighs the tiled kernel's LDS traffic and
+// split-K partial tiles.  The draft and verify GEMMs switch above 17 rows
+// (one sequence's 16 draft and 17 verify rows stay skinny).  The injection
+// GEMMs stay skinny up to 32 rows: there the skinny kernel's summation order
+// is the same for every row count, so an injection split over two such calls
+// writes the same cache bits as one call.
+constexpr int STEP_TILED_MIN_ROWS = 17;
+constexpr int INJECT_TILED_MIN_ROWS = 32;
 
 struct GemmPlan {
   int M, N, K;
   int MT, NB, m_tiles, m_blocks, n_tiles, n_blocks, k_tiles;
+  bool tiled;
 };
 
 // nb: weight tiles per workgroup (2 for the gate/up pairs and the argmax,
-// 1 otherwise); the workgroup's wavefronts split K.
-GemmPlan plan_gemm(int dtype, int M, int N, int K, int nb) {
+// 1 otherwise); the workgroup's wavefronts split K.  Launches of more than
+// tiled_above rows take the tiled kernel.
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int nb, int tiled_above) {
   GemmPlan g{};
+  g.tiled = M > tiled_above;
   g.M = M;
   g.N = N;
   g.K = K;
@@ -122,11 +126,11 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   const int H = d->hidden, NQD = d->n_q_heads * d->head_dim, I = d->intermediate, hd = d->head_dim;
   L.M = batch * d->block_size;
   L.S = attn_splits(d, batch);
-  L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1);
-  L.o = plan_gemm(d->dtype, L.M, H, NQD, 1);
-  L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2);
-  L.down = plan_gemm(d->dtype, L.M, H, I, 1);
-  L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, 2);
+  L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1, STEP_TILED_MIN_ROWS);
+  L.o = plan_gemm(d->dtype, L.M, H, NQD, 1, STEP_TILED_MIN_ROWS);
+  L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2, STEP_TILED_MIN_ROWS);
+  L.down = plan_gemm(d->dtype, L.M, H, I, 1, STEP_TILED_MIN_ROWS);
+  L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, 2, STEP_TILED_MIN_ROWS);
   // packed activations hold whole row blocks (the GEMMs load them unguarded)
   L.Mp = L.qkv.m_blocks * L.qkv.MT * 16;
   Bump b;
@@ -150,7 +154,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
-  L.part = L.M > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.part = L.M > STEP_TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -162,7 +166,7 @@ struct VerifyLayout {
 
 VerifyLayout verify_layout(const dflash_dims *d, int batch) {
   VerifyLayout L{};
-  L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, 2);
+  L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, 2, STEP_TILED_MIN_ROWS);
   L.end = WS_COUNTER_BYTES;
   return L;
 }
@@ -178,8 +182,8 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   InjectLayout L{};
   const int H = d->hidden;
 
-  L.fc = plan_gemm(d->dtype, rows, H, d->n_feat_layers * H, 1);
-  L.kv = plan_gemm(d->dtype, rows, d->n_layers * 2 * d->n_kv_heads * d->head_dim, H, 1);
+  L.fc = plan_gemm(d->dtype, rows, H, d->n_feat_layers * H, 1, INJECT_TILED_MIN_ROWS);
+  L.kv = plan_gemm(d->dtype, rows, d->n_layers * 2 * d->n_kv_heads * d->head_dim, H, 1, INJECT_TILED_MIN_ROWS);
   L.Rp = L.kv.m_blocks * L.kv.MT * 16;
   Bump b;
   L.u = b.take(size_t(rows) * H * 4);
@@ -189,7 +193,7 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   L.pc = packed_bytes(d->dtype, L.Rp, H);
   L.xc = b.take(L.pc * L.xs);
   L.rs_inline = gemm_inline_rs_ok(L.kv.m_blocks, L.kv.MT, H);
-  L.part = rows > TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.part = rows > INJECT_TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.end = b.off;
   return L;
 }
@@ -349,9 +353,8 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   p.out_planes = 1;
   // packed activation buffers hold whole row blocks of the row-tile plan
   p.x_mtiles = g.m_blocks * g.MT;
-  // launches of more than 32 rows go to the tiled kernel, which
-  // picks its tile shape
-  if (gemm_tiled(g.M)) p.tiled = 1;
+  // the tiled kernel picks its tile shape
+  if (g.tiled) p.tiled = 1;
 }
 
 }  // namespace

@@ -337,12 +337,12 @@ def test_larger_b8_block_sweep_sampled(block):
     assert rep["tokens"].compared >= 1
 
 
-@pytest.mark.parametrize("batch", [2, 5])
+@pytest.mark.parametrize("batch", [1, 5])
 def test_graph_replay_matches_eager(batch):
     """One inject + draft + verify step captured in a HIP graph and replayed
     three times, with eager steps and synchronisations between the replays:
     every replay's drafted tokens, target argmax, accept lengths, fallback
-    tokens and ctx_len equal the eager step's (batch 2: skinny GEMMs with the
+    tokens and ctx_len equal the eager step's (batch 1: skinny GEMMs with the
     fused argmax and commit tails; batch 5: tiled GEMMs, split-K, rstd and
     the argmax finish kernel)."""
     import torch
