@@ -124,6 +124,16 @@ def test_small_bf16_step():
     _compare_step(case, 0, [5, 17])
 
 
+@pytest.mark.parametrize("rows", [[15, 17], [16, 17]])
+def test_routing_boundaries(rows):
+    """Launch sizes on both sides of the skinny/tiled switch: injections of
+    32 rows (the largest on the skinny kernel) and 33 rows (tiled), at batch 2
+    with 32 draft and 34 verify rows (tiled) beside the batch-1 step's 16 and
+    17 (skinny) in the other tests."""
+    case = Hn.build_case(SMALL_BF16, 2, [40, 9], seed=25)
+    _compare_step(case, 0, rows)
+
+
 def test_small_bf16_gains_and_no_rope():
     d = C.Dims(**{**SMALL_BF16.__dict__, "rope_theta": 0.0})
     case = Hn.build_case(d, 1, [64], seed=4, gain_std=0.05)
