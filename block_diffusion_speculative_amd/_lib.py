@@ -32,7 +32,7 @@ EXPORTED = [
     "dflash_kv_bytes", "dflash_kv_import", "dflash_kv_export",
     "dflash_workspace_bytes", "dflash_workspace_init", "dflash_workspace_view",
     "dflash_inject_kv", "dflash_draft_forward", "dflash_verify_accept",
-    "dflash_status_str", "dflash_last_error", "dflash_abi_version",
+    "dflash_status_str", "dflash_last_error", "dflash_abi_version", "dflash_build_id",
 ]
 
 
@@ -101,6 +101,7 @@ def load() -> ctypes.CDLL:
         "dflash_status_str": (c_char_p, [c_int32]),
         "dflash_last_error": (c_char_p, []),
         "dflash_abi_version": (c_int32, []),
+        "dflash_build_id": (c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -108,6 +109,26 @@ def load() -> ctypes.CDLL:
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def build_id() -> str:
+    """Digest of the sources the loaded library was built from."""
+    return load().dflash_build_id().decode()
+
+
+def is_fresh() -> bool:
+    """Whether the loaded library was built from the sources now in the tree."""
+    from .csrc.build import source_digest
+    return build_id() == source_digest()
+
+
+def file_is_fresh(path: str = LIB_PATH) -> bool:
+    """The same question answered from the library file's bytes (the digest
+    is compiled in as a string), without loading it: usable before the GPU
+    runtime is initialised."""
+    from .csrc.build import source_digest
+    with open(path, "rb") as fh:
+        return source_digest().encode() in fh.read()
 
 
 def last_error() -> str:

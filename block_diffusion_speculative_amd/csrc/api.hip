@@ -201,17 +201,22 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
 int check_dims(const dflash_dims *d) {
   if (!d) return fail(DFLASH_ERR_NULL, "dims is NULL");
   if (d->dtype != DFLASH_BF16 && d->dtype != DFLASH_F32) return fail(DFLASH_ERR_DTYPE, "dtype must be DFLASH_BF16 or DFLASH_F32");
-  if (d->hidden <= 0 || d->hidden % 64 || d->hidden > 8192) return fail(DFLASH_ERR_SHAPE, "hidden must be a positive multiple of 64, at most 8192");
-  if (d->head_dim != 64 && d->head_dim != 128) return fail(DFLASH_ERR_SHAPE, "head_dim must be 64 or 128");
+  // Malformed dimensions: DFLASH_ERR_SHAPE.
+  if (d->hidden <= 0 || d->hidden % 32) return fail(DFLASH_ERR_SHAPE, "hidden must be a positive multiple of 32");
+  if (d->head_dim <= 0 || d->head_dim % 32) return fail(DFLASH_ERR_SHAPE, "head_dim must be a positive multiple of 32");
   if (d->n_kv_heads <= 0 || d->n_q_heads <= 0 || d->n_q_heads % d->n_kv_heads) return fail(DFLASH_ERR_SHAPE, "n_q_heads must be a positive multiple of n_kv_heads");
-  if (d->n_q_heads / d->n_kv_heads > 16) return fail(DFLASH_ERR_SHAPE, "at most 16 query heads per KV head");
-  if (d->n_layers < 1 || d->n_layers > MAX_SEGMENTS) return fail(DFLASH_ERR_SHAPE, "n_layers must be in [1, 16]");
+  if (d->n_layers < 1) return fail(DFLASH_ERR_SHAPE, "n_layers must be >= 1");
   if (d->intermediate <= 0 || d->intermediate % 32) return fail(DFLASH_ERR_SHAPE, "intermediate must be a positive multiple of 32");
   if (d->n_feat_layers < 1) return fail(DFLASH_ERR_SHAPE, "n_feat_layers must be >= 1");
   if (d->vocab < 32 || d->vocab % 32) return fail(DFLASH_ERR_SHAPE, "vocab must be a positive multiple of 32");
   if (d->mask_id < 0 || d->mask_id >= d->vocab) return fail(DFLASH_ERR_SHAPE, "mask_id must be in [0, vocab)");
   if (d->block_size < 1 || d->block_size > 16) return fail(DFLASH_ERR_SHAPE, "block_size must be in [1, 16]");
   if (!(d->rms_eps >= 0.f) || !(d->rope_theta >= 0.f)) return fail(DFLASH_ERR_SHAPE, "rms_eps and rope_theta must be >= 0");
+  // Well-formed but outside what the kernels are built for: DFLASH_ERR_UNSUPPORTED.
+  if (d->hidden % 64 || d->hidden > 8192) return fail(DFLASH_ERR_UNSUPPORTED, "hidden must be a multiple of 64, at most 8192");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->n_q_heads / d->n_kv_heads > 16) return fail(DFLASH_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (d->n_layers > MAX_SEGMENTS) return fail(DFLASH_ERR_UNSUPPORTED, "at most 16 layers");
   return DFLASH_OK;
 }
 
@@ -359,9 +364,54 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
 
 }  // namespace
 
+namespace dflash {
+
+int set_error(int code, const char *msg) { return fail(code, msg); }
+
+int set_hip_error(hipError_t e, const char *what) { return hip_fail(e, what); }
+
+int verify_with_ws(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,
+                int32_t batch, int32_t *target_argmax, int32_t *accept_len, int32_t *bonus, char *wsb,
+                size_t ws_bytes, hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_ptr(lm_head, "lm_head"));
+  TRY(check_ptr(target_hidden, "target_hidden"));
+  TRY(check_ptr(draft, "draft", false));
+  TRY(check_ptr(target_argmax, "target_argmax", false));
+  TRY(check_ptr(accept_len, "accept_len", false));
+  TRY(check_ptr(bonus, "bonus", false));
+  if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
+  const VerifyLayout L = verify_layout(d, batch);
+  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
+  GemmParams lm{};
+  fill_gemm(lm, L.lm);
+  lm.w_seg[0] = static_cast<const char *>(lm_head);
+  lm.x = static_cast<const char *>(target_hidden);
+  lm.x_ld = d->hidden;
+  lm.vocab = d->vocab;
+  lm.keys = reinterpret_cast<unsigned long long *>(wsb);
+  ArgmaxFinishParams fp{};
+  fp.keys = lm.keys;
+  fp.rows_per_seq = d->block_size + 1;
+  fp.block = d->block_size;
+  fp.verify = 1;
+  fp.tok_out = target_argmax;
+  fp.draft_in = draft;
+  fp.accept_len = accept_len;
+  fp.bonus = bonus;
+  return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "verify");
+}
+
+}  // namespace dflash
+
 extern "C" {
 
 int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+#ifndef DFLASH_SOURCE_DIGEST
+#define DFLASH_SOURCE_DIGEST "unknown"
+#endif
+const char *dflash_build_id(void) { return DFLASH_SOURCE_DIGEST; }
 
 const char *dflash_last_error(void) { return g_err.c_str(); }
 
@@ -739,35 +789,9 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
 int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,
                          int32_t batch, int32_t *target_argmax, int32_t *accept_len, int32_t *bonus, void *ws,
                          size_t ws_bytes, hipStream_t stream) {
-  TRY(check_dims(d));
-  TRY(check_ptr(lm_head, "lm_head"));
-  TRY(check_ptr(target_hidden, "target_hidden"));
-  TRY(check_ptr(draft, "draft", false));
-  TRY(check_ptr(target_argmax, "target_argmax", false));
-  TRY(check_ptr(accept_len, "accept_len", false));
-  TRY(check_ptr(bonus, "bonus", false));
   TRY(check_ptr(ws, "ws"));
-  if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
-  const VerifyLayout L = verify_layout(d, batch);
-  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
-  char *wsb = static_cast<char *>(ws);
-  GemmParams lm{};
-  fill_gemm(lm, L.lm);
-  lm.w_seg[0] = static_cast<const char *>(lm_head);
-  lm.x = static_cast<const char *>(target_hidden);
-  lm.x_ld = d->hidden;
-  lm.vocab = d->vocab;
-  lm.keys = reinterpret_cast<unsigned long long *>(wsb);
-  ArgmaxFinishParams fp{};
-  fp.keys = lm.keys;
-  fp.rows_per_seq = d->block_size + 1;
-  fp.block = d->block_size;
-  fp.verify = 1;
-  fp.tok_out = target_argmax;
-  fp.draft_in = draft;
-  fp.accept_len = accept_len;
-  fp.bonus = bonus;
-  return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "verify");
+  return verify_with_ws(d, lm_head, target_hidden, draft, batch, target_argmax, accept_len, bonus,
+                        static_cast<char *>(ws), ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -35,9 +35,31 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str, obj_dir: str) -> str:
+def source_files():
+    """Every file the library is built from: the HIP sources and headers of
+    this folder and the public header."""
+    names = sorted(f for f in os.listdir(HERE) if f.endswith((".hip", ".hpp")))
+    return [os.path.join(HERE, f) for f in names] + [os.path.join(ROOT, "include", "dflash.h")]
+
+
+def source_digest() -> str:
+    """sha256 over the build flags and the name and bytes of every source
+    file; the library reports the digest it was built from
+    (dflash_build_id), so a stale build is detected before it is used."""
+    import hashlib
+    # flags without absolute paths (the tree may move between build and use)
+    flags = [os.path.relpath(f, ROOT) if f.startswith(ROOT) else f for f in COMMON]
+    h = hashlib.sha256(" ".join(flags).encode())
+    for path in source_files():
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _compile(src: str, obj_dir: str, digest: str) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(HERE, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, f'-DDFLASH_SOURCE_DIGEST="{digest}"', "-c", os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -47,8 +69,9 @@ def _compile(src: str, obj_dir: str) -> str:
 def build(jobs: int = 4, verbose: bool = False) -> str:
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
+    digest = source_digest()
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, digest), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

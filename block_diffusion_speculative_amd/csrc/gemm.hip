@@ -667,8 +667,7 @@ static hipError_t launch_xs(const GemmParams &p, hipStream_t s) {
   switch (p.MT) {
     case 1: return launch_kc<T, 1, NB, EPI, XS, XROW>(p, s);
     case 2: return launch_kc<T, 2, NB, EPI, XS, XROW>(p, s);
-    case 4: return launch_kc<T, 4, NB, EPI, XS, XROW>(p, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;   // more than 32 rows run tiled
   }
 }
 

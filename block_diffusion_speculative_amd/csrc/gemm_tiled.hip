@@ -1,5 +1,6 @@
-// Y = X W^T on MFMA for launches with many rows (more than 64 tokens: the
-// batched draft step and its heads, large injections).
+// Y = X W^T on MFMA for launches with many rows (draft and verify GEMMs of
+// more than 17 rows, injections of more than 32: the batched draft step and
+// its heads, large injections).
 //
 // A workgroup owns a TM x TN tile of 16 x 16 output fragments (128 tokens x
 // 256 features, or 64 x 128 when the large tiles would leave compute units
@@ -467,7 +468,9 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   auto blocks = [](int n, int b) { return (n + b - 1) / b; };
   const int mt = blocks(p.M, 16);
   if (EPI == EPI_ARGMAX) {
-    if (mt <= 12) p.tile_m = (mt + 1) & ~1;
+    // at least 4 fragments: 2 (17-32 rows) would leave half the wave grid
+    // without a row tile
+    if (mt <= 12) p.tile_m = mt <= 4 ? 4 : (mt + 1) & ~1;
     else p.tile_m = blocks(mt, 12) * 12 < blocks(mt, 8) * 8 ? 12 : 8;
     p.n_blocks = blocks(p.n_tiles, 16);
   } else {
@@ -496,7 +499,8 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
       case 6: launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s); break;
       case 8: launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s); break;
       case 10: launch_tiled_shape<T, EPI, XS, XROW, 10, 16, 2, 4>(p, grid, s); break;
-      default: launch_tiled_shape<T, EPI, XS, XROW, 12, 16, 2, 4>(p, grid, s); break;
+      case 12: launch_tiled_shape<T, EPI, XS, XROW, 12, 16, 2, 4>(p, grid, s); break;
+      default: return hipErrorInvalidValue;
     }
   } else {
     if (EPI == EPI_ARGMAX && p.tile_m != 8) return hipErrorInvalidValue;

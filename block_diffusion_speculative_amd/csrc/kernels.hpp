@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/dflash.h"
+
 namespace dflash {
 
 // The first bytes of every workspace hold the argmax key slots: zeroed once
@@ -28,8 +30,10 @@ constexpr int MAX_SPLIT_ITEMS = 8192;
 constexpr size_t WS_SPLIT_CNT_OFFSET = WS_ARRIVE_OFFSET - MAX_SPLIT_ITEMS * 4;
 static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_SPLIT_CNT_OFFSET, "key slots overlap the split counts");
 // The argmax finish and the injection commit run inside the GEMM launch (by
-// its last workgroup to finish) when the launch has at most this many rows.
-constexpr int FUSED_FINISH_ROWS = 64;
+// its last workgroup to finish) when the launch runs on the skinny kernel,
+// which takes at most this many rows (17 for draft and verify heads, 32 for
+// injections); tiled launches finish in argmax_finish_kernel.
+constexpr int FUSED_FINISH_ROWS = 32;
 
 enum Epilogue : int {
   EPI_STORE = 0,   // out_f32[m, n] = y
@@ -168,6 +172,17 @@ struct EmbedParams {
   size_t x_plane;
   float *ssq;              // [M, H / 16] tile sums of squares
 };
+
+// Greedy verification with its scratch (argmax key slots and the arrival
+// counter, at least WS_COUNTER_BYTES, zero on entry) at wsb: the body of
+// dflash_verify_accept after its workspace check.  Returns a dflash_status.
+int verify_with_ws(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,
+                   int32_t batch, int32_t *target_argmax, int32_t *accept_len, int32_t *bonus, char *wsb,
+                   size_t ws_bytes, hipStream_t stream);
+// Record an error for dflash_last_error() and return `code` (DFLASH_ERR_HIP
+// with the HIP error string for set_hip_error).
+int set_error(int code, const char *msg);
+int set_hip_error(hipError_t e, const char *what);
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_gemm(int dtype, int epi, const GemmParams &p, hipStream_t s);

@@ -79,19 +79,22 @@ typedef enum {
   DFLASH_ERR_WORKSPACE = -4,   /* workspace too small */
   DFLASH_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
   DFLASH_ERR_HIP = -6,         /* a HIP call or kernel launch failed */
-  DFLASH_ERR_UNSUPPORTED = -7  /* a valid but unsupported configuration */
+  DFLASH_ERR_UNSUPPORTED = -7  /* well-formed dims outside the kernels' limits */
 } dflash_status;
 
 /* Sticky bits OR-ed into *kv->status by device code. */
 #define DFLASH_STATUS_CAPACITY 1u  /* an injection would exceed kv->capacity */
 #define DFLASH_STATUS_TOKEN 2u     /* a token id outside [0, vocab) was clamped */
 
-/* Drafter dimensions [host].  Limits checked by every call:
- * hidden, intermediate, n_feat_layers*hidden and n_q_heads*head_dim are
- * multiples of 32; head_dim is 64 or 128; n_q_heads % n_kv_heads == 0 with
- * n_q_heads / n_kv_heads <= 16; 1 <= block_size <= 16; 1 <= n_layers <= 16;
- * vocab is a multiple of 32; 0 <= mask_id < vocab; rope_theta == 0 turns
- * rotary embedding off. */
+/* Drafter dimensions [host].  Every call that takes dims checks them first.
+ * DFLASH_ERR_SHAPE (malformed): hidden, head_dim, intermediate and vocab
+ * must be positive multiples of 32; n_q_heads % n_kv_heads == 0 with both
+ * positive; n_layers >= 1; n_feat_layers >= 1; 1 <= block_size <= 16;
+ * 0 <= mask_id < vocab; rms_eps >= 0 and rope_theta >= 0.
+ * DFLASH_ERR_UNSUPPORTED (well-formed, but outside what the kernels are
+ * built for): hidden must be a multiple of 64 and at most 8192; head_dim 64
+ * or 128; n_q_heads / n_kv_heads <= 16; n_layers <= 16.
+ * rope_theta == 0 turns rotary embedding off. */
 typedef struct {
   int32_t hidden;
   int32_t n_q_heads;
@@ -256,6 +259,9 @@ int dflash_verify_accept(const dflash_dims *dims, const void *lm_head, const voi
 const char *dflash_status_str(int status);
 const char *dflash_last_error(void);
 int dflash_abi_version(void);
+/* sha256 (hex) of the sources and build flags this library was built from,
+ * or "unknown"; lets a caller detect a stale build. */
+const char *dflash_build_id(void);
 
 #ifdef __cplusplus
 }

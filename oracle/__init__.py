@@ -29,6 +29,5 @@ from .dflash_oracle import (  # noqa: F401
     rope,
     silu,
     speedup,
-    step,
     verify,
 )

@@ -279,11 +279,3 @@ def verify(dims, lm_head: np.ndarray, target_hidden: np.ndarray):
     logits = linear(th, lm_head)
     return argmax_lowest(logits)
 
-
-def step(dims, weights, cache: OracleCache, feats, last_tok, target_hidden):
-    """inject + draft + verify + accept, in that order."""
-    inject(dims, weights, cache, feats)
-    dr = draft_forward(dims, weights, cache, last_tok)
-    g, vgaps = verify(dims, _get(weights, "lm_head"), target_hidden)
-    L, bonus = accept(dr["tokens"], g)
-    return {"draft": dr, "target_argmax": g, "verify_gaps": vgaps, "accept_len": L, "bonus": bonus}

@@ -16,6 +16,17 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
 
 
+def pytest_sessionstart(session):
+    # A library built from other sources than the ones in the tree would test
+    # the wrong code: refuse to run against it.  (Checked on the file: the
+    # library is loaded only after torch has initialised the GPU runtime.)
+    from block_diffusion_speculative_amd import _lib
+    if os.path.exists(_lib.LIB_PATH) and not _lib.file_is_fresh():
+        raise pytest.UsageError(
+            f"{_lib.LIB_PATH} was built from other sources than the ones in the tree "
+            "(dflash_build_id differs from the source digest): rebuild with __graft_entry__.build()")
+
+
 def pytest_collection_modifyitems(config, items):
     # GPU tests need the device; when run without one they are skipped with a reason
     # rather than silently passing.

@@ -30,6 +30,25 @@ def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(num / den))
 
 
+HEAD = 128            # channels per attention head: the per-head error segment
+
+
+def rel_err_heads(got: np.ndarray, ref: np.ndarray, seg: int = HEAD) -> float:
+    """max over rows and over each row's ``seg``-channel segments of
+    ||got - ref|| / ||ref||: localises an error confined to one head or one
+    rotary pair that a whole-row norm would dilute.  Rows narrower than
+    ``seg`` are taken whole."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    w = g.shape[-1]
+    s = seg if w % seg == 0 else w
+    g = g.reshape(-1, s)
+    r = r.reshape(-1, s)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.maximum(np.linalg.norm(r, axis=1), 1e-30)
+    return float(np.max(num / den))
+
+
 @dataclass
 class TokenReport:
     compared: int = 0
@@ -212,6 +231,16 @@ class GpuRunner:
     def kv_plain(self):
         k, v = self.drafter.kv_export()
         return k.float().cpu().numpy(), v.float().cpu().numpy()
+
+    def kv_rows(self, seq: int, lo: int, hi: int):
+        """Cache positions [lo, hi) of one sequence, every layer and head:
+        K and V as [n_layers, n_kv, hi - lo, head_dim] (sliced on the device,
+        so a full-size cache never crosses to the host)."""
+        k, v = self.drafter.kv_export()
+        ks = k[:, seq, :, lo:hi].float().cpu().numpy()
+        vs = v[:, seq, :, lo:hi].float().cpu().numpy()
+        del k, v
+        return ks, vs
 
     def ctx_len(self):
         return self.drafter.ctx_len.cpu().numpy()

@@ -38,6 +38,7 @@ def test_exports_every_declared_symbol(lib):
 def test_abi_version(lib):
     assert lib.dflash_abi_version() == 1
     assert lib.dflash_status_str(-4) == b"workspace too small"
+    assert lib.dflash_status_str(-7) == b"unsupported"
 
 
 def test_sizes(lib):
@@ -75,9 +76,14 @@ def _bad_dims(**kw):
 @pytest.mark.parametrize("field,value,code", [
     ("dtype", 7, _lib.DFLASH_ERR_DTYPE),
     ("hidden", 100, _lib.DFLASH_ERR_SHAPE),
-    ("head_dim", 96, _lib.DFLASH_ERR_SHAPE),
+    ("hidden", 96, _lib.DFLASH_ERR_UNSUPPORTED),
+    ("hidden", 8256, _lib.DFLASH_ERR_UNSUPPORTED),
+    ("head_dim", 80, _lib.DFLASH_ERR_SHAPE),
+    ("head_dim", 96, _lib.DFLASH_ERR_UNSUPPORTED),
     ("n_q_heads", 30, _lib.DFLASH_ERR_SHAPE),
-    ("n_layers", 17, _lib.DFLASH_ERR_SHAPE),
+    ("n_q_heads", 136, _lib.DFLASH_ERR_UNSUPPORTED),
+    ("n_layers", 0, _lib.DFLASH_ERR_SHAPE),
+    ("n_layers", 17, _lib.DFLASH_ERR_UNSUPPORTED),
     ("block_size", 17, _lib.DFLASH_ERR_SHAPE),
     ("block_size", 0, _lib.DFLASH_ERR_SHAPE),
     ("mask_id", 151936, _lib.DFLASH_ERR_SHAPE),

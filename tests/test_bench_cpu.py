@@ -91,3 +91,22 @@ def test_block_size_outside_the_sweep_is_refused():
                         "--block-size", "4"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "not swept" in r.stderr and r.stdout == ""
+
+
+def test_head_label_follows_the_routing_rule():
+    """The verify head runs skinny up to 17 rows (one sequence at B = 16) and
+    tiled above: 40 rows (hidden-5120 drafter, batch 8, B = 4) is tiled."""
+    assert bench.STEP_TILED_MIN_ROWS == 17
+    assert bench.head_kernel_label(17).startswith("gemm_kernel<")
+    assert bench.head_kernel_label(18).startswith("gemm_tiled_kernel<")
+    assert bench.head_kernel_label(40).startswith("gemm_tiled_kernel<")
+    api = open(os.path.join(ROOT, "block_diffusion_speculative_amd", "csrc", "api.hip")).read()
+    assert "constexpr int STEP_TILED_MIN_ROWS = 17;" in api
+
+
+def test_extras_default_list_covers_the_measured_workloads():
+    names = {(n, b) for n, b in bench.EXTRAS}
+    assert ("qwen3-8b-b32", 16) in names and ("qwen3-8b-long", 16) in names
+    assert {("larger-b8", b) for b in (4, 8, 16)} <= names
+    for n, b in names:
+        assert b in C.get(n).block_sizes

@@ -27,7 +27,9 @@ SPLIT_BF16 = C.Dims(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, n_laye
 
 def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=True):
     """Run inject + draft + verify on both sides and assert parity.  Returns a
-    report dict."""
+    report dict.  check_cache: True compares every cached position of the
+    followed sequences, "new" only the rows this step injected (full-size
+    caches)."""
     d = case.dims
     seqs = list(range(case.batch)) if seqs is None else list(seqs)
     gpu = Hn.GpuRunner(case)
@@ -50,7 +52,20 @@ def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=Tr
         if rows.stop > rows.start:
             c = O.rms_norm(views["fused"][rows].astype(np.float64), case.weights.fc_norm, d.rms_eps)
             rep["errors"]["fused"] = max(rep["errors"].get("fused", 0.0), Hn.rel_err_rows(c, ref["fused"][i]))
-    if check_cache:
+            rep["errors"]["fused_head"] = max(rep["errors"].get("fused_head", 0.0),
+                                              Hn.rel_err_heads(c, ref["fused"][i]))
+    if check_cache == "new":
+        # the rows this step appended, [ctx, ctx + n), of every layer and head
+        # (cache rows are one head's head_dim channels each)
+        for i, s in enumerate(seqs):
+            lo, hi = int(case.ctx[s]), int(ctx_after[s])
+            if hi == lo:
+                continue
+            kg, vg = gpu.kv_rows(s, lo, hi)
+            ek = Hn.rel_err_rows(kg, ref["cache"].k[:, i, :, lo:hi])
+            ev = Hn.rel_err_rows(vg, ref["cache"].v[:, i, :, lo:hi])
+            rep["errors"]["cache_new"] = max(rep["errors"].get("cache_new", 0.0), ek, ev)
+    elif check_cache:
         kg, vg = gpu.kv_plain()
         for i, s in enumerate(seqs):
             n = int(ctx_after[s])
@@ -64,9 +79,13 @@ def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=Tr
     rows = np.concatenate([np.arange(s * B, (s + 1) * B) for s in seqs])
     dr = ref["draft"]
     for l in range(d.n_layers):
-        rep["errors"][f"attn{l}"] = Hn.rel_err_rows(views["attn"][l][rows], dr["attn_out"][l])
-        rep["errors"][f"mid{l}"] = Hn.rel_err_rows(views["mid"][l][rows], dr["mid"][l])
-        rep["errors"][f"hidden{l}"] = Hn.rel_err_rows(views["hidden"][l + 1][rows], dr["hidden"][l + 1])
+        pairs = {f"attn{l}": (views["attn"][l][rows], dr["attn_out"][l]),
+                 f"mid{l}": (views["mid"][l][rows], dr["mid"][l]),
+                 f"hidden{l}": (views["hidden"][l + 1][rows], dr["hidden"][l + 1])}
+        for k, (g_, r_) in pairs.items():
+            rep["errors"][k] = Hn.rel_err_rows(g_, r_)
+            # per 128-channel segment (one head of the attention output)
+            rep["errors"][k + "_head"] = Hn.rel_err_heads(g_, r_)
     rep["errors"]["embed"] = Hn.rel_err_rows(views["hidden"][0][rows], dr["hidden"][0])
     print({k: f"{v:.2e}" for k, v in rep["errors"].items()}, flush=True)
     for k, v in rep["errors"].items():
@@ -96,7 +115,9 @@ def _compare_step(case, step, new_rows, seqs=None, accept_p=0.12, check_cache=Tr
     rep["tokens"] = tr
     rep["status"] = gpu.drafter.read_status()
     assert rep["status"] == 0
-    print({k: f"{v:.2e}" for k, v in rep["errors"].items()}, "compared", tr.compared, "below_gap", tr.below_gap)
+    print({k: f"{v:.2e}" for k, v in rep["errors"].items() if not k.endswith("_head")},
+          "worst per-head", f"{max(v for k, v in rep['errors'].items() if k.endswith('_head')):.2e}",
+          "compared", tr.compared, "below_gap", tr.below_gap)
     return rep
 
 
@@ -277,9 +298,10 @@ def test_bad_token_sets_status():
 @pytest.mark.parametrize("dims,batch", [("small", 1), ("small", 2), ("split", 5)])
 def test_deterministic_repeat(dims, batch):
     """Same inputs, same bits, whatever the workspace held before (batch 1:
-    the consumers reduce the norm statistics themselves; batch 2 as well, with
-    two row tiles; batch 5 of the split configuration: split-K partial tiles
-    summed in part order whichever part finishes last)."""
+    skinny GEMMs whose consumers reduce the norm statistics themselves;
+    batch 2: 32 draft rows on the tiled kernel with rstd_kernel's per-row
+    scales; batch 5 of the split configuration: split-K partial tiles summed
+    in part order whichever part finishes last)."""
     d = {"small": SMALL_BF16, "split": SPLIT_BF16}[dims]
     case = Hn.build_case(d, batch, [40, 90, 7, 130, 64][:batch], seed=8)
     g = Hn.GpuRunner(case)
@@ -302,7 +324,7 @@ def test_qwen3_8b_b1_full_shape():
     one step of 9 injected rows."""
     w = C.get("qwen3-8b-b1")
     case = Hn.build_case(w.dims, 1, [2048], seed=0, kv_mode="import")
-    rep = _compare_step(case, 0, [9], accept_p=I.workload_geom_p(w), check_cache=False)
+    rep = _compare_step(case, 0, [9], accept_p=I.workload_geom_p(w), check_cache="new")
     assert rep["tokens"].compared >= 1
 
 
@@ -315,7 +337,7 @@ def test_qwen3_8b_b32_ragged_sampled():
     ctx = I.context_lengths(w, 0)
     rows = I.new_row_counts(w, 0, 0)
     case = Hn.build_case(w.dims, w.batch, ctx, seed=0, kv_mode="import")
-    rep = _compare_step(case, 0, rows, seqs=[0, 13, 31], accept_p=I.workload_geom_p(w), check_cache=False)
+    rep = _compare_step(case, 0, rows, seqs=[0, 13, 31], accept_p=I.workload_geom_p(w), check_cache="new")
     assert rep["tokens"].compared >= 1
 
 
@@ -328,7 +350,7 @@ def test_qwen3_8b_long_context_sampled():
     ctx = I.context_lengths(w, 0)
     rows = I.new_row_counts(w, 0, 0)
     case = Hn.build_case(w.dims, w.batch, ctx, seed=0, kv_mode="import")
-    rep = _compare_step(case, 0, rows, seqs=[0, 3], accept_p=I.workload_geom_p(w), check_cache=False)
+    rep = _compare_step(case, 0, rows, seqs=[0, 3], accept_p=I.workload_geom_p(w), check_cache="new")
     assert rep["tokens"].compared >= 1
 
 
@@ -343,7 +365,7 @@ def test_larger_b8_block_sweep_sampled(block):
     ctx = I.context_lengths(w, 0)
     case = Hn.build_case(d, w.batch, ctx, seed=0, kv_mode="import")
     rows = [1 + (3 * s) % block for s in range(w.batch)]
-    rep = _compare_step(case, 0, rows, seqs=[0, 7], accept_p=I.workload_geom_p(w), check_cache=False)
+    rep = _compare_step(case, 0, rows, seqs=[0, 7], accept_p=I.workload_geom_p(w), check_cache="new")
     assert rep["tokens"].compared >= 1
 
 
@@ -403,3 +425,131 @@ def test_graph_replay_matches_eager(batch):
         torch.cuda.synchronize()
         for got, want in zip((out, ta, al, bo), ref[:4]):
             assert torch.equal(got, want)
+
+
+TIE_DIMS = C.Dims(**{**SMALL_BF16.__dict__, "vocab": 65536})
+
+
+def _far_index(tok: int, lower: bool, vocab: int, avoid) -> int:
+    """An index far from ``tok`` (another workgroup and argmax slot of the
+    head): about half way down to 0 when ``lower`` (and tok >= 64), else half
+    way up to the last real token; never the mask id or a member of
+    ``avoid``."""
+    if lower and tok >= 64:
+        t = tok // 2
+        while t in avoid:
+            t -= 1
+        return t
+    t = tok + (vocab - 1 - tok) // 2
+    while t in avoid or t >= vocab - 1:
+        t = t + 1 if t + 1 < vocab - 1 else tok + 1
+    return t
+
+
+@pytest.mark.parametrize("batch", [1, 5])
+def test_argmax_exact_ties_lowest_index(batch):
+    """Exact ties inside both heads' top-1, built by duplicating lm_head rows
+    ("Term: DFlash speculative decoding", "DFlash: architecture and
+    workflow": the drafted token and the target's token are each an argmax;
+    ties go to the lowest index).  A duplicated row gives bit-identical
+    logits on both sides, so the tied positions are compared bit-exactly with
+    no gap exemption.  Batch 1 runs the skinny heads (fused finish), batch 5
+    the tiled heads and argmax_finish_kernel; the 65536-token vocabulary puts
+    the two rows of a pair in different workgroups and argmax slots, with the
+    lower index first in some pairs and second in others."""
+    d = TIE_DIMS
+    seed = 40 + batch
+    ctx = [31 + 29 * s for s in range(batch)]
+    case = Hn.build_case(d, batch, ctx, seed=seed)
+    W = case.weights
+    feats, last = Hn.step_inputs(case, 0, [1] * batch)
+    cache0 = Hn.oracle_prefill(case, list(range(batch)))
+    O.inject(d, W, cache0, feats)
+    toks0 = O.draft_forward(d, W, cache0, last)["tokens"]
+    # draft ties: duplicate the rows of distinct drafted tokens, half of them
+    # to a lower index (the argmax moves there) and half to a higher one
+    lm = W.lm_head.copy()
+    avoid = set(int(t) for t in toks0.reshape(-1)) | {d.mask_id}
+    draft_pairs = {}
+    vals, counts = np.unique(toks0.reshape(-1), return_counts=True)
+    by_count = [int(v) for v in vals[np.argsort(-counts, kind="stable")] if int(v) != d.mask_id]
+    for i, tok in enumerate(by_count[:6]):
+        t2 = _far_index(tok, i % 2 == 0, d.vocab, avoid)
+        lm[t2] = lm[tok]
+        draft_pairs[tok] = t2
+        avoid.add(t2)
+    W.lm_head = lm
+    cache1 = Hn.oracle_prefill(case, list(range(batch)))
+    O.inject(d, W, cache1, feats)
+    dr = O.draft_forward(d, W, cache1, last)
+    # every constructed pair that is some slot's top-1 is an exact tie there
+    tied_draft = np.zeros_like(dr["tokens"], dtype=bool)
+    for tok, t2 in draft_pairs.items():
+        hit = (toks0 == tok)
+        assert np.all(dr["tokens"][hit] == min(tok, t2))
+        assert np.all(dr["gaps"][hit] == 0.0)
+        tied_draft |= hit
+    assert tied_draft.sum() >= 2 and any(t2 < tok for tok, t2 in draft_pairs.items()
+                                         if np.any(toks0 == tok))
+    # verify ties: planted targets on the oracle's tokens; the rows of a few
+    # targets past the accepted prefix get a duplicate too
+    L_plant = I.planted_accept(seed, 0, batch, 0.15, d.block_size)
+    t, _ = I.planted_targets(d, seed, 0, W.lm_head, dr["tokens"], L_plant)
+    verify_pairs = {}
+    for s in range(batch):
+        for j in range(int(L_plant[s]) + 1, d.block_size + 1, 3):
+            tok = int(t[s, j])
+            if tok in avoid or tok in verify_pairs:
+                continue
+            t3 = _far_index(tok, (s + j) % 2 == 0, d.vocab, avoid | {tok})
+            lm[t3] = lm[tok]
+            verify_pairs[tok] = t3
+            avoid |= {tok, t3}
+    W.lm_head = lm
+    # the draft does not see the new pairs (neither row is any slot's top-1)
+    assert np.array_equal(O.draft_forward(d, W, cache1, last)["tokens"], dr["tokens"])
+    t, hid = I.planted_targets(d, seed, 0, W.lm_head, dr["tokens"], L_plant)
+    g_ref, vgaps = O.verify(d, W.lm_head, hid)
+    L_ref, bonus_ref = O.accept(dr["tokens"], g_ref)
+    tied_verify = np.isin(t, list(draft_pairs) + list(draft_pairs.values())
+                          + list(verify_pairs) + list(verify_pairs.values()))
+    assert np.all(vgaps[tied_verify] == 0.0) and tied_verify.sum() >= 2
+    # GPU on the same (modified) weights
+    gpu = Hn.GpuRunner(case)
+    gpu.inject(feats)
+    got = gpu.draft(last)
+    ta, al, bo = gpu.verify(hid, dr["tokens"].astype(np.int32))
+    assert np.array_equal(got[tied_draft], dr["tokens"][tied_draft]), (got, dr["tokens"])
+    assert np.array_equal(ta[tied_verify], g_ref[tied_verify]), (ta, g_ref)
+    tr = Hn.TokenReport()
+    tr.add(got, dr["tokens"], dr["gaps"], "draft")
+    tr.add(ta, g_ref, vgaps, "verify")
+    assert not tr.mismatched, tr.mismatched
+    # accept length and fallback token: decided by positions that are above
+    # the gap or constructed ties
+    for s in range(batch):
+        upto = min(int(L_ref[s]), d.block_size)
+        ok = (vgaps[s, :upto + 1] > Hn.GAP) | tied_verify[s, :upto + 1]
+        if np.all(ok):
+            assert al[s] == L_ref[s] and bo[s] == bonus_ref[s], (s, al, L_ref, bo, bonus_ref)
+    print("tied draft slots", int(tied_draft.sum()), "tied verify rows", int(tied_verify.sum()),
+          "compared", tr.compared, "below_gap", tr.below_gap)
+
+
+def test_deterministic_injection_two_row_tiles():
+    """A 24-row injection (two row tiles on the skinny kernel, whose
+    consumer reduces the RMSNorm tile sums itself) writes the same cache bits
+    again after the workspace outside its counter area is poisoned."""
+    d = SMALL_BF16
+    case = Hn.build_case(d, 2, [0, 0], seed=26, capacity=64)
+    F = [I.features(d, 26, 0, s, 12) for s in range(2)]
+    g = Hn.GpuRunner(case, max_rows=24)
+    g.inject(F)
+    k1, v1 = g.kv_plain()
+    g.drafter.set_ctx_len([0, 0])
+    g.drafter.ws.fill_(0xFF)
+    g.drafter.ws[: 1 << 20].zero_()
+    g.inject(F)
+    k2, v2 = g.kv_plain()
+    assert np.array_equal(g.ctx_len()[:2], [12, 12])
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
