@@ -31,7 +31,7 @@ EXPORTED = [
     "dflash_pack_lm_head",
     "dflash_kv_bytes", "dflash_kv_import", "dflash_kv_export",
     "dflash_workspace_bytes", "dflash_workspace_init", "dflash_workspace_view",
-    "dflash_inject_kv", "dflash_draft_forward", "dflash_verify_accept",
+    "dflash_inject_kv", "dflash_draft_forward", "dflash_verify_accept", "dflash_verify_accept_noalloc",
     "dflash_status_str", "dflash_last_error", "dflash_abi_version", "dflash_build_id",
 ]
 
@@ -98,6 +98,7 @@ def load() -> ctypes.CDLL:
                                            c_int32, P, P, c_size_t, P]),
         "dflash_verify_accept": (c_int32, [POINTER(Dims), P, P, P, c_int32, P, P, P, P,
                                            c_size_t, P]),
+        "dflash_verify_accept_noalloc": (c_int32, [POINTER(Dims), P, P, P, c_int32, P, P, P, P]),
         "dflash_status_str": (c_char_p, [c_int32]),
         "dflash_last_error": (c_char_p, []),
         "dflash_abi_version": (c_int32, []),

@@ -255,6 +255,21 @@ int dflash_verify_accept(const dflash_dims *dims, const void *lm_head, const voi
                          int32_t *accept_len, int32_t *bonus, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* Greedy verification for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and outputs as dflash_verify_accept, with no
+ * workspace argument.  Its scratch (the argmax key slots and an arrival
+ * counter, 1 MiB) is a static device array of the library, one per GPU,
+ * looked up and zero-filled by the first call on each device (on `stream`,
+ * with that device current) and held until the process ends; the call
+ * itself allocates nothing.  batch must be in [1, 64] (DFLASH_ERR_SHAPE
+ * otherwise).  Every call on one GPU shares that scratch: two calls that
+ * overlap on one GPU (different streams, or different threads without
+ * ordering) race.  Pointers and outputs as for dflash_verify_accept. */
+int dflash_verify_accept_noalloc(const dflash_dims *dims, const void *lm_head, const void *target_hidden,
+                                 const int32_t *draft, int32_t batch, int32_t *target_argmax,
+                                 int32_t *accept_len, int32_t *bonus, hipStream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 const char *dflash_status_str(int status);
 const char *dflash_last_error(void);
