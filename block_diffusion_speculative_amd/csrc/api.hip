@@ -676,6 +676,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     q.xs = L.xs;
     q.x_plane = L.pa;
     q.q_plane = L.pq;
+    q.q_planes = L.xs;   // q itself goes to the attention as hi + lo
     q.block = d->block_size;
     q.n_q = d->n_q_heads;
     q.n_kv = d->n_kv_heads;

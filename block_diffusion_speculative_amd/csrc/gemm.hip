@@ -112,7 +112,7 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
         if (n < nqd) {
           const int h = n / d;
           char *base = p.qbuf + (size_t(s) * p.n_q + h) * dt_count * 1024;
-          store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.xs, v);
+          store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.q_planes, v);
         } else {
           const int g = (n - nqd) / d;
           char *base = p.kblk + (size_t(s) * p.n_kv + g) * size_t(KT) * d * ES;

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
                 x = rope_apply(x, partner, dd, d, p.ctx_len[sq] + j, p);
                 if (n < nqd) {
                   char *base = p.qbuf + (size_t(sq) * p.n_q + n / d) * dt_count * 1024;
-                  store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.xs, x);
+                  store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.q_planes, x);
                 } else {
                   char *base = p.kblk + (size_t(sq) * p.n_kv + (n - nqd) / d) * size_t(KT) * d * ES;
                   store_elem<T>(base + kcache_offset<T>(j, dd, d), x);

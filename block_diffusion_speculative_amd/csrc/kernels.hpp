@@ -81,6 +81,7 @@ struct GemmParams {
   const int *ctx_len;
   char *qbuf, *kblk, *vblk;
   size_t q_plane;
+  int q_planes;               // planes of q written for the attention (1, or 2 = hi + lo)
   char *kcache, *vcache;
   int layer0, capacity, max_batch;
   const int *cu_new;
