@@ -9,7 +9,8 @@ Parity status per function (what pins it is listed in the tests that check
 it; see ``tests/test_oracle_*.py``):
 
 * ``rms_norm``, ``rope``, ``silu``, ``linear``, ``attention``,
-  ``argmax_lowest``, ``accept``, ``inject``, ``draft_forward``, ``verify``,
+  ``argmax_lowest``, ``accept``, ``inject``, ``draft_forward``,
+  ``draft_anchors``, ``verify``,
   ``speedup``: pinned by brute force, closed forms and invariants.
 * End-to-end drafted token values on random weights have no external
   reference value; they are pinned only through the invariants above
@@ -21,6 +22,7 @@ from .dflash_oracle import (  # noqa: F401
     accept,
     argmax_lowest,
     attention,
+    draft_anchors,
     draft_block,
     draft_forward,
     inject,

@@ -226,6 +226,36 @@ def draft_forward(dims, weights, cache: OracleCache, last_tok: np.ndarray,
     return draft_block(dims, weights, cache, toks, keep_logits, pos_offset)
 
 
+def draft_anchors(dims, weights, cache: OracleCache, anchor_seq, anchor_pos, anchor_tok,
+                  keep_logits: bool = False) -> Dict[str, np.ndarray]:
+    """Drafting passes over blocks with explicit anchors ([Term/WF] stage
+    one: anchor positions at the decoding frontier and at additional points
+    when several blocks are drafted concurrently).
+
+    Block a belongs to cached sequence anchor_seq[a]; its anchor position
+    p = anchor_pos[a] is the number of that sequence's cached positions it
+    sees, so slot 0 holds anchor_tok[a] at position p, the mask slots follow
+    at p + 1 .. p + B - 1, and attention covers cached positions [0, p) and
+    the block's own slots.  A block anchored at the frontier (p equal to the
+    cached length) is the ordinary drafting pass.  Blocks are independent of
+    one another; several may share a sequence.  Returns the draft_forward
+    outputs stacked over blocks."""
+    outs = []
+    for a in range(len(anchor_tok)):
+        s, p = int(anchor_seq[a]), int(anchor_pos[a])
+        if not 0 <= p <= int(cache.length[s]):
+            raise ValueError("an anchor lies beyond its sequence's cached positions")
+        view = OracleCache(cache.k[:, s:s + 1], cache.v[:, s:s + 1], np.array([p], dtype=np.int64))
+        outs.append(draft_forward(dims, weights, view, np.array([anchor_tok[a]]), keep_logits))
+    res: Dict[str, np.ndarray] = {}
+    for key in outs[0]:
+        if isinstance(outs[0][key], list):
+            res[key] = [np.concatenate([o[key][l] for o in outs], axis=0) for l in range(len(outs[0][key]))]
+        else:
+            res[key] = np.concatenate([o[key] for o in outs], axis=0)
+    return res
+
+
 def draft_block(dims, weights, cache: OracleCache, toks: np.ndarray,
                 keep_logits: bool = False, pos_offset: int = 0) -> Dict[str, np.ndarray]:
     """The drafting pass over an arbitrary block of token ids [b, B]

@@ -398,6 +398,76 @@ def check_draft_closed_form():
         assert np.allclose(out["logits"][0, 0], w.embed @ z, atol=1e-12)
 
 
+def check_anchor_frontier_is_the_draft():
+    """A block anchored at its sequence's frontier (anchor position = cached
+    length, anchor token = last accepted token) is the ordinary drafting pass."""
+    dims = SMALL
+    w = small_weights(dims)
+    cache, _ = _prefill(dims, w, 2, 9)
+    last = np.array([5, 40])
+    a = O.draft_forward(dims, w, cache, last, keep_logits=True)
+    b = O.draft_anchors(dims, w, cache, [0, 1], [9, 9], last, keep_logits=True)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-13)
+    for l in range(dims.n_layers):
+        assert np.allclose(a["attn_out"][l], b["attn_out"][l], atol=1e-13)
+
+
+def check_anchor_sees_only_its_prefix():
+    """A block anchored at p < C reads cached positions [0, p) only: it
+    equals drafting over the first p injected rows alone, cache rows at p and
+    beyond do not reach it, and it differs from the frontier block."""
+    dims = SMALL
+    w = small_weights(dims)
+    cache, feats = _prefill(dims, w, 1, 12)
+    p = 7
+    short = O.OracleCache.empty(dims, 1, 16)
+    O.inject(dims, w, short, [feats[0][:p]])
+    a = O.draft_anchors(dims, w, cache, [0], [p], [3], keep_logits=True)
+    b = O.draft_forward(dims, w, short, np.array([3]), keep_logits=True)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-12)
+    c2 = O.OracleCache(cache.k.copy(), cache.v.copy(), cache.length.copy())
+    c2.k[:, 0, :, p:, :] = 1e3
+    c2.v[:, 0, :, p:, :] = -1e3
+    c = O.draft_anchors(dims, w, c2, [0], [p], [3], keep_logits=True)
+    assert np.allclose(a["logits"], c["logits"], atol=1e-13)
+    f = O.draft_anchors(dims, w, cache, [0], [12], [3], keep_logits=True)
+    assert not np.allclose(a["logits"], f["logits"])
+
+
+def check_anchor_blocks_independent():
+    """Blocks do not see each other: permuting the anchors permutes the
+    outputs, and several blocks may share one sequence."""
+    dims = SMALL
+    w = small_weights(dims)
+    cache, _ = _prefill(dims, w, 2, 10)
+    seq, pos, tok = [0, 1, 1, 0], [10, 4, 10, 6], [2, 9, 9, 30]
+    a = O.draft_anchors(dims, w, cache, seq, pos, tok, keep_logits=True)
+    perm = [2, 0, 3, 1]
+    b = O.draft_anchors(dims, w, cache, [seq[i] for i in perm], [pos[i] for i in perm],
+                        [tok[i] for i in perm], keep_logits=True)
+    assert np.allclose(a["logits"][perm], b["logits"], atol=1e-13)
+    assert not np.allclose(a["logits"][1], a["logits"][2])   # same sequence and token, other anchor
+
+
+def check_anchor_closed_form():
+    """The identity drafter over two injected rows: a block anchored at
+    position 1 sees row e0 only and is the one-row closed form (block query
+    at angle 1 + pi/2), anchored at 2 the two-row one."""
+    dims, w = _identity_drafter()
+    r2 = math.sqrt(2.0)
+    cache = O.OracleCache.empty(dims, 1, 8)
+    O.inject(dims, w, cache, [np.array([[1.0, 0.0], [0.0, 1.0]])])
+    out = O.draft_anchors(dims, w, cache, [0, 0], [1, 2], [1, 1], keep_logits=True)
+    for a, C in enumerate((1, 2)):
+        q_ang = C + math.pi / 2
+        ctx_ang = [0.0, 1.0 + math.pi / 2][:C]
+        scores = [2.0 * math.cos(q_ang - x) / r2 for x in ctx_ang] + [2.0 / r2]
+        vals = [np.array([r2, 0.0]), np.array([0.0, r2])][:C] + [np.array([0.0, r2])]
+        e = [math.exp(x) for x in scores]
+        o = sum(ei * v for ei, v in zip(e, vals)) / sum(e)
+        assert np.allclose(out["attn_out"][0][a, 0], o, atol=1e-12), (C, out["attn_out"][0][a, 0], o)
+
+
 def check_planted_recovery():
     """Verify on planted target states recovers the planted accept length
     and fallback token exactly (the self-logit margin is large)."""
@@ -438,5 +508,7 @@ ALL_CHECKS = [
     check_inject_layer_major_features, check_permutation_equivariance,
     check_position_shift_invariance, check_context_matters, check_draft_layer_structure,
     check_draft_closed_form,
+    check_anchor_frontier_is_the_draft, check_anchor_sees_only_its_prefix,
+    check_anchor_blocks_independent, check_anchor_closed_form,
     check_planted_recovery, check_cost_model_simulation,
 ]

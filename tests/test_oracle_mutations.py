@@ -37,6 +37,9 @@ MUTATIONS = {
     "draft mlp gate/up swapped": ("act = silu(linear(a, lw[\"w_gate\"])) * linear(a, lw[\"w_up\"])",
                                   "act = silu(linear(a, lw[\"w_up\"])) * linear(a, lw[\"w_gate\"])"),
     "draft no final norm": ("z = rms_norm(h, _get(weights, \"final_norm\"), dims.rms_eps)", "z = h"),
+    "anchor sees the whole context": ("np.array([p], dtype=np.int64))", "cache.length[s:s + 1].copy())"),
+    "anchor one position late": ("view = OracleCache(cache.k[:, s:s + 1], cache.v[:, s:s + 1], np.array([p], dtype=np.int64))",
+                                 "view = OracleCache(cache.k[:, s:s + 1], cache.v[:, s:s + 1], np.array([p + 1], dtype=np.int64))"),
     "inject wrong slot": ("cache.k[l, s, :, start:start + n, :] = k.transpose(1, 0, 2)",
                           "cache.k[l, s, :, start + 1:start + n + 1, :] = k.transpose(1, 0, 2)"),
 }
