@@ -24,6 +24,7 @@ DFLASH_ERR_HIP = -6
 DFLASH_ERR_UNSUPPORTED = -7
 DFLASH_STATUS_CAPACITY = 1
 DFLASH_STATUS_TOKEN = 2
+DFLASH_STATUS_ANCHOR = 4
 VIEW_FUSED, VIEW_HIDDEN, VIEW_MID, VIEW_ATTN = range(4)
 
 EXPORTED = [
@@ -31,7 +32,7 @@ EXPORTED = [
     "dflash_pack_lm_head",
     "dflash_kv_bytes", "dflash_kv_import", "dflash_kv_export",
     "dflash_workspace_bytes", "dflash_workspace_init", "dflash_workspace_view",
-    "dflash_inject_kv", "dflash_draft_forward", "dflash_verify_accept", "dflash_verify_accept_noalloc",
+    "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_anchors", "dflash_verify_accept", "dflash_verify_accept_noalloc",
     "dflash_status_str", "dflash_last_error", "dflash_abi_version", "dflash_build_id",
 ]
 
@@ -95,6 +96,8 @@ def load() -> ctypes.CDLL:
         "dflash_inject_kv": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, P,
                                        c_int32, c_int32, P, c_size_t, P]),
         "dflash_draft_forward": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P,
+                                           c_int32, P, P, c_size_t, P]),
+        "dflash_draft_anchors": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, P, P,
                                            c_int32, P, P, c_size_t, P]),
         "dflash_verify_accept": (c_int32, [POINTER(Dims), P, P, P, c_int32, P, P, P, P,
                                            c_size_t, P]),

@@ -113,7 +113,7 @@ int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
 int mlp_act_planes(const dflash_dims *d, int rows) { return rows > MLP_ONE_PLANE_ROWS ? act_planes(d) : 1; }
 
 struct DraftLayout {
-  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, end;
+  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, anc, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
   int M, Mp, S, xs, act_xs;  // planes of the packed activations and of the SwiGLU output
   bool rs_inline;  // consumers reduce the RMSNorm tile sums themselves (one row block)
@@ -155,6 +155,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
   L.part = L.M > STEP_TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
+  L.anc = b.take(size_t(2) * MAX_BATCH * 4);   // anchored blocks: checked context lengths, cache regions
   L.end = b.off;
   return L;
 }
@@ -617,15 +618,27 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
   return DFLASH_OK;
 }
 
-int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
-                         int32_t batch, int32_t *draft, void *ws, size_t ws_bytes, hipStream_t stream) {
+// The drafting pass over `batch` blocks: block s holds last_tok[s], then
+// mask slots.  Plain form (anchor_pos null): block s is sequence s at its
+// frontier.  Anchored form: block s reads cached sequence anchor_seq[s] up to
+// position anchor_pos[s] (checked and clamped on the device by the embedding
+// launch, which writes the per-block lengths and regions the later launches
+// read).
+static int draft_impl(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
+                      const int32_t *anchor_seq, const int32_t *anchor_pos, int32_t batch, int32_t *draft, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
   TRY(check_dims(d));
   TRY(check_weights(d, w, false, true));
   TRY(check_kv(d, kv));
-  TRY(check_ptr(last_tok, "last_tok", false));
+  TRY(check_ptr(last_tok, anchor_pos ? "anchor_tok" : "last_tok", false));
   TRY(check_ptr(draft, "draft", false));
   TRY(check_ptr(ws, "ws"));
-  if (batch < 1 || batch > kv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  if (anchor_pos) {
+    TRY(check_ptr(anchor_seq, "anchor_seq", false));
+    if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "nblocks must be in [1, 64]");
+  } else if (batch < 1 || batch > kv->max_batch) {
+    return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  }
   const DraftLayout L = draft_layout(d, batch);
   if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
   char *wsb = static_cast<char *>(ws);
@@ -659,6 +672,18 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   ep.planes = L.xs;
   ep.x_plane = L.pa;
   ep.ssq = ssq;
+  int *blk_ctx = reinterpret_cast<int *>(wsb + L.anc), *blk_region = blk_ctx + MAX_BATCH;
+  if (anchor_pos) {
+    ep.anchor_seq = anchor_seq;
+    ep.anchor_pos = anchor_pos;
+    ep.ctx_len = kv->ctx_len;
+    ep.max_batch = kv->max_batch;
+    ep.capacity = kv->capacity;
+    ep.blk_ctx = blk_ctx;
+    ep.blk_region = blk_region;
+  }
+  // the context each block attends to (and its rotary base position)
+  const int *ctx_of = anchor_pos ? blk_ctx : kv->ctx_len;
   e = launch_embed(d->dtype, ep, stream);
   if (e != hipSuccess) return hip_fail(e, "draft embed");
 
@@ -682,7 +707,7 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     q.n_kv = d->n_kv_heads;
     q.head_dim = hd;
     fill_rope(q, d);
-    q.ctx_len = kv->ctx_len;
+    q.ctx_len = ctx_of;
     q.qbuf = wsb + L.qbuf;
     q.kblk = wsb + L.kblk;
     q.vblk = wsb + L.vblk;
@@ -699,7 +724,8 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
     a.vblk = wsb + L.vblk;
     a.kcache = static_cast<const char *>(kv->k) + region_layer * l;
     a.vcache = static_cast<const char *>(kv->v) + region_layer * l;
-    a.ctx_len = kv->ctx_len;
+    a.ctx_len = ctx_of;
+    a.region_of = anchor_pos ? blk_region : nullptr;
     a.part = reinterpret_cast<float *>(wsb + L.apart);
     a.block = d->block_size;
     a.n_q = d->n_q_heads;
@@ -785,6 +811,18 @@ int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const df
   fp.verify = 0;
   fp.tok_out = draft;
   return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "draft");
+}
+
+int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
+                         int32_t batch, int32_t *draft, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return draft_impl(d, w, kv, last_tok, nullptr, nullptr, batch, draft, ws, ws_bytes, stream);
+}
+
+int dflash_draft_anchors(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *anchor_seq,
+                         const int32_t *anchor_pos, const int32_t *anchor_tok, int32_t nblocks, int32_t *draft,
+                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  TRY(check_ptr(anchor_pos, "anchor_pos", false));
+  return draft_impl(d, w, kv, anchor_tok, anchor_seq, anchor_pos, nblocks, draft, ws, ws_bytes, stream);
 }
 
 int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,

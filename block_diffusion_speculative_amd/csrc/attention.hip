@@ -87,8 +87,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   const int round_tiles = SUB * TPS;
 
   const size_t region = size_t(p.capacity) * HD * ES;
-  const char *kreg = p.kcache + (size_t(s) * p.n_kv + g) * region;
-  const char *vreg = p.vcache + (size_t(s) * p.n_kv + g) * region;
+  const int cs = p.region_of ? p.region_of[s] : s;   // the cached sequence this block reads
+  const char *kreg = p.kcache + (size_t(cs) * p.n_kv + g) * region;
+  const char *vreg = p.vcache + (size_t(cs) * p.n_kv + g) * region;
   const char *kbk = p.kblk + (size_t(s) * p.n_kv + g) * KB;
   const char *vbk = p.vblk + (size_t(s) * p.n_kv + g) * VB;
 

@@ -146,7 +146,8 @@ struct AttnParams {
   size_t q_plane;                   // bytes between the q hi and lo planes
   int xs;                           // 2: q and P carried as hi + lo bf16 planes
   const char *kcache, *vcache;      // this layer's cache (sequence-major regions)
-  const int *ctx_len;
+  const int *ctx_len;               // per block: cached positions it attends to
+  const int *region_of;             // per block: its sequence's cache region (null: the block's own)
   float *part;                      // [batch][n_q][splits] partial records
   int block, n_q, n_kv, head_dim, group, splits, capacity;
   int head_split;                   // workgroups sharing one KV head's query group
@@ -172,6 +173,14 @@ struct EmbedParams {
   int x_kt, planes;        // planes: 1, or 2 (hi, lo) x_plane bytes apart
   size_t x_plane;
   float *ssq;              // [M, H / 16] tile sums of squares
+  // Anchored blocks (anchor_pos set): block s drafts for cached sequence
+  // anchor_seq[s] from position anchor_pos[s]; the first row's thread 0
+  // checks both against the cache (DFLASH_STATUS_ANCHOR when outside it,
+  // then clamped) and writes them to blk_region / blk_ctx, which the QKV
+  // epilogue and the attention read.
+  const int *anchor_seq, *anchor_pos, *ctx_len;
+  int max_batch, capacity;
+  int *blk_ctx, *blk_region;
 };
 
 // Greedy verification with its scratch (argmax key slots and the arrival

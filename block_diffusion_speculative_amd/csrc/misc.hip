@@ -24,6 +24,17 @@ __global__ __launch_bounds__(256) void embed_kernel(const EmbedParams p) {
     return;
   }
   const int s = m / p.block, j = m % p.block;
+  if (p.anchor_pos && j == 0 && threadIdx.x == 0) {
+    int seq = p.anchor_seq[s], pos = p.anchor_pos[s];
+    bool bad = seq < 0 || seq >= p.max_batch;
+    seq = seq < 0 ? 0 : (seq >= p.max_batch ? p.max_batch - 1 : seq);
+    const int have = max(0, min(p.ctx_len[seq], p.capacity));
+    bad = bad || pos < 0 || pos > have;
+    pos = pos < 0 ? 0 : (pos > have ? have : pos);
+    if (bad) atomicOr(p.status, DFLASH_STATUS_ANCHOR);
+    p.blk_region[s] = seq;
+    p.blk_ctx[s] = pos;
+  }
   int tok = j == 0 ? p.last_tok[s] : p.mask_id;
   if (tok < 0 || tok >= p.vocab) {
     if (threadIdx.x == 0) atomicOr(p.status, DFLASH_STATUS_TOKEN);

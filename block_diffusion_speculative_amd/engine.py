@@ -53,7 +53,7 @@ class Drafter:
     """Packed drafter weights + draft KV cache + workspace on one GPU."""
 
     def __init__(self, dims: Dims, weights: Weights, max_batch: int, capacity: int,
-                 max_rows: int, device="cuda:0", keep_plain: bool = False):
+                 max_rows: int, device="cuda:0", keep_plain: bool = False, max_blocks: int = 0):
         self.lib = _lib.load()
         self.dims = dims
         self.cd = cdims(dims)
@@ -129,7 +129,10 @@ class Drafter:
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         self.ckv = _lib.KV(self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.ctx_len.data_ptr(),
                            self.status.data_ptr(), capacity, max_batch)
-        self.ws_bytes = self.lib.dflash_workspace_bytes(ctypes.byref(self.cd), max_batch, max_rows)
+        # the workspace holds the largest draft call: max_batch sequences, or
+        # max_blocks anchored blocks
+        self.max_blocks = max(max_batch, max_blocks)
+        self.ws_bytes = self.lib.dflash_workspace_bytes(ctypes.byref(self.cd), self.max_blocks, max_rows)
         if self.ws_bytes == 0:
             raise ValueError("invalid workspace request")
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
@@ -141,20 +144,41 @@ class Drafter:
                   _ptr(feats), _ptr(cu_new), batch, rows, self.ws.data_ptr(), self.ws_bytes,
                   _stream_ptr(stream))
 
-    def draft(self, last_tok: torch.Tensor, out: torch.Tensor, batch: int, stream=None):
-        _lib.call("dflash_draft_forward", ctypes.byref(self.cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
+    def dims_for(self, block_size: Optional[int] = None) -> _lib.Dims:
+        """The drafter's dims, with another block size for this call (any
+        B <= the drafter's: its workspace is sized for that)."""
+        if block_size is None or block_size == self.dims.block_size:
+            return self.cd
+        if not 1 <= block_size <= self.dims.block_size:
+            raise ValueError(f"block size {block_size} outside [1, {self.dims.block_size}]")
+        cd = cdims(self.dims.with_block(block_size))
+        return cd
+
+    def draft(self, last_tok: torch.Tensor, out: torch.Tensor, batch: int, stream=None,
+              block_size: Optional[int] = None):
+        cd = self.dims_for(block_size)
+        _lib.call("dflash_draft_forward", ctypes.byref(cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
                   _ptr(last_tok), batch, _ptr(out), self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
 
+    def draft_anchors(self, anchor_seq: torch.Tensor, anchor_pos: torch.Tensor, anchor_tok: torch.Tensor,
+                      out: torch.Tensor, nblocks: int, stream=None, block_size: Optional[int] = None):
+        cd = self.dims_for(block_size)
+        _lib.call("dflash_draft_anchors", ctypes.byref(cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
+                  _ptr(anchor_seq), _ptr(anchor_pos), _ptr(anchor_tok), nblocks, _ptr(out),
+                  self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
+
     def verify(self, target_hidden: torch.Tensor, draft: torch.Tensor, target_argmax: torch.Tensor,
-               accept_len: torch.Tensor, bonus: torch.Tensor, batch: int, stream=None):
-        _lib.call("dflash_verify_accept", ctypes.byref(self.cd), self.lm_head.data_ptr(),
+               accept_len: torch.Tensor, bonus: torch.Tensor, batch: int, stream=None,
+               block_size: Optional[int] = None):
+        cd = self.dims_for(block_size)
+        _lib.call("dflash_verify_accept", ctypes.byref(cd), self.lm_head.data_ptr(),
                   _ptr(target_hidden), _ptr(draft), batch, _ptr(target_argmax), _ptr(accept_len),
                   _ptr(bonus), self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
 
     # ------------------------------------------------------------ helpers
-    def view(self, what: int, count: int, layer: int = 0) -> torch.Tensor:
+    def view(self, what: int, count: int, layer: int = 0, block_size: Optional[int] = None) -> torch.Tensor:
         off, nb = ctypes.c_size_t(), ctypes.c_size_t()
-        _lib.call("dflash_workspace_view", ctypes.byref(self.cd), what, count, layer,
+        _lib.call("dflash_workspace_view", ctypes.byref(self.dims_for(block_size)), what, count, layer,
                   ctypes.byref(off), ctypes.byref(nb))
         return self.ws[off.value:off.value + nb.value].view(torch.float32)
 

@@ -85,6 +85,7 @@ typedef enum {
 /* Sticky bits OR-ed into *kv->status by device code. */
 #define DFLASH_STATUS_CAPACITY 1u  /* an injection would exceed kv->capacity */
 #define DFLASH_STATUS_TOKEN 2u     /* a token id outside [0, vocab) was clamped */
+#define DFLASH_STATUS_ANCHOR 4u    /* an anchor outside its sequence's cache was clamped */
 
 /* Drafter dimensions [host].  Every call that takes dims checks them first.
  * DFLASH_ERR_SHAPE (malformed): hidden, head_dim, intermediate and vocab
@@ -243,6 +244,24 @@ int dflash_inject_kv(const dflash_dims *dims, const dflash_weights *w, const dfl
 int dflash_draft_forward(const dflash_dims *dims, const dflash_weights *w, const dflash_kv *kv,
                          const int32_t *last_tok, int32_t batch, int32_t *draft,
                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Drafting passes over blocks with explicit anchors ("Term: DFlash
+ * speculative decoding", "DFlash: architecture and workflow", stage one: the
+ * engine picks anchor positions at the decoding frontier and at additional
+ * points when several blocks are drafted concurrently).  Block a drafts for
+ * cached sequence anchor_seq[a] in [0, kv->max_batch): slot 0 holds
+ * anchor_tok[a] at rotary position p = anchor_pos[a], slot j > 0 holds
+ * dims->mask_id at p + j, and the block attends to that sequence's cached
+ * positions [0, p) and to its own slots.  0 <= p <= ctx_len[anchor_seq[a]]
+ * (p = ctx_len is the frontier, the dflash_draft_forward case); several
+ * blocks may share a sequence and do not see each other.  An anchor outside
+ * the cache sets DFLASH_STATUS_ANCHOR and is clamped into it.  anchor_seq,
+ * anchor_pos, anchor_tok: [nblocks] device arrays; 1 <= nblocks <= 64; the
+ * workspace must hold dflash_workspace_bytes(dims, nblocks, .).  draft:
+ * [nblocks, B] out.  The cache is read, never written. */
+int dflash_draft_anchors(const dflash_dims *dims, const dflash_weights *w, const dflash_kv *kv,
+                         const int32_t *anchor_seq, const int32_t *anchor_pos, const int32_t *anchor_tok,
+                         int32_t nblocks, int32_t *draft, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Greedy verification.  target_hidden: [batch, B+1, H] row-major, storage
  * dtype: the target's final hidden states at its pass over

@@ -553,3 +553,144 @@ def test_deterministic_injection_two_row_tiles():
     k2, v2 = g.kv_plain()
     assert np.array_equal(g.ctx_len()[:2], [12, 12])
     assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def _compare_anchors(case, gpu, anchors, seed, check_views=True):
+    """Anchored drafting (dflash_draft_anchors) against the oracle's
+    draft_anchors on the case's cache: tokens under the gap rule, and the
+    per-layer attention outputs and residuals of every block."""
+    import torch
+    d = case.dims
+    seq = np.array([a[0] for a in anchors], dtype=np.int32)
+    pos = np.array([a[1] for a in anchors], dtype=np.int32)
+    tok = np.array([a[2] for a in anchors], dtype=np.int32)
+    n = len(anchors)
+    cache = Hn.oracle_prefill(case, list(range(case.batch)))
+    ref = O.draft_anchors(d, case.weights, cache, seq, pos, tok)
+    dev = gpu.drafter.device
+    out = torch.full((n, d.block_size), -1, dtype=torch.int32, device=dev)
+    t = lambda a: torch.as_tensor(a).to(dev)
+    gpu.drafter.draft_anchors(t(seq), t(pos), t(tok), out, n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    tr = Hn.TokenReport()
+    tr.add(got, ref["tokens"], ref["gaps"], "anchors")
+    assert not tr.mismatched, tr.mismatched
+    errs = {}
+    if check_views:
+        from block_diffusion_speculative_amd import _lib
+        M = n * d.block_size
+        for l in range(d.n_layers):
+            ga = gpu.drafter.view(_lib.VIEW_ATTN, n, l).reshape(M, -1).cpu().numpy()
+            gh = gpu.drafter.view(_lib.VIEW_HIDDEN, n, l).reshape(M, -1).cpu().numpy()
+            ra = ref["attn_out"][l].reshape(M, -1)
+            rh = ref["hidden"][l + 1].reshape(M, -1)
+            errs[f"attn{l}"] = max(Hn.rel_err_rows(ga, ra), Hn.rel_err_heads(ga, ra))
+            errs[f"hidden{l}"] = max(Hn.rel_err_rows(gh, rh), Hn.rel_err_heads(gh, rh))
+        for k, v in errs.items():
+            assert v <= Hn.REL_TOL, (k, v, errs)
+    assert gpu.drafter.read_status() == 0
+    print({k: f"{v:.2e}" for k, v in errs.items()}, "compared", tr.compared, "below_gap", tr.below_gap)
+    return tr
+
+
+def test_anchored_blocks_small():
+    """Blocks with explicit anchors: the frontier of each sequence, two
+    candidate anchor tokens at one frontier, earlier anchors (position 0,
+    inside a key step, on a step boundary) and a block over an empty prefix;
+    7 blocks over 2 cached sequences (112 draft rows: the tiled path)."""
+    d = SMALL_BF16
+    case = Hn.build_case(d, 2, [100, 301], seed=33)
+    gpu = Hn.GpuRunner(case, max_blocks=7)
+    anchors = [(0, 100, 17), (1, 301, 500), (1, 301, 2048), (1, 150, 9), (1, 64, 9), (0, 0, 77), (0, 37, 3000)]
+    _compare_anchors(case, gpu, anchors, 33)
+
+
+def test_anchored_single_block_skinny():
+    """One anchored block (16 rows: the skinny path) at an earlier position
+    equals the oracle's drafting over that prefix."""
+    d = SMALL_BF16
+    case = Hn.build_case(d, 1, [200], seed=34)
+    gpu = Hn.GpuRunner(case)
+    _compare_anchors(case, gpu, [(0, 123, 42)], 34)
+
+
+def test_anchor_outside_cache_sets_status():
+    import torch
+    d = C.TINY_DRAFT
+    case = Hn.build_case(d, 1, [20], seed=35)
+    g = Hn.GpuRunner(case)
+    dev = g.drafter.device
+    out = torch.empty((1, d.block_size), dtype=torch.int32, device=dev)
+    t = lambda a: torch.as_tensor(np.array(a, dtype=np.int32)).to(dev)
+    g.drafter.draft_anchors(t([0]), t([25]), t([3]), out, 1)      # beyond the 20 cached positions
+    torch.cuda.synchronize()
+    assert g.drafter.read_status() & 4
+    g.drafter.clear_status()
+    g.drafter.draft_anchors(t([5]), t([10]), t([3]), out, 1)      # no such sequence
+    torch.cuda.synchronize()
+    assert g.drafter.read_status() & 4
+
+
+@pytest.mark.slow
+def test_anchored_blocks_qwen3_8b_full_shape():
+    """The Qwen3-8B-shaped drafter over one 2048-position cache (imported):
+    four blocks (64 rows) anchored at the frontier with two tokens, at 1000
+    and at 2047."""
+    w = C.get("qwen3-8b-b1")
+    case = Hn.build_case(w.dims, 1, [2048], seed=36, kv_mode="import")
+    gpu = Hn.GpuRunner(case, max_blocks=4)
+    tr = _compare_anchors(case, gpu, [(0, 2048, 11), (0, 2048, 70000), (0, 1000, 11), (0, 2047, 5)], 36)
+    assert tr.compared >= 16
+
+
+def test_decode_loop_block_size_per_step():
+    """Adaptive block size: a decode loop whose block size changes every
+    step (16, 4, 8, 16, 1) on one drafter, cache and workspace, each step
+    compared with the oracle at that step's block size (drafted tokens under
+    the gap rule, accept lengths, fallback tokens and context lengths)."""
+    d0 = SMALL_BF16
+    b, seed = 2, 37
+    ctx0 = [30, 61]
+    case = Hn.build_case(d0, b, ctx0, seed=seed, capacity=C.kv_capacity(max(ctx0) + 5 * 17))
+    gpu = Hn.GpuRunner(case)
+    cache = Hn.oracle_prefill(case, list(range(b)))
+    rows = np.ones(b, dtype=np.int64)
+    last = I.last_tokens(d0, seed, 0, b)
+    tr = Hn.TokenReport()
+    for step, B in enumerate((16, 4, 8, 16, 1)):
+        d = d0.with_block(B)
+        feats = [I.features(d, seed, step + 1, s, int(rows[s])) for s in range(b)]
+        gpu.inject(feats)
+        O.inject(d, case.weights, cache, feats)
+        assert np.array_equal(gpu.ctx_len()[:b], cache.length)
+        import torch
+        dev = gpu.drafter.device
+        out = torch.full((b, B), -1, dtype=torch.int32, device=dev)
+        gpu.drafter.draft(torch.as_tensor(last).to(dev), out, b, block_size=B)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = O.draft_forward(d, case.weights, cache, last)
+        tr.add(got, ref["tokens"], ref["gaps"], f"draft{step}")
+        L_plant = I.planted_accept(seed, step, b, 0.2, B)
+        _, hid = I.planted_targets(d, seed, step, case.weights.lm_head, ref["tokens"], L_plant)
+        th = gpu.upload(hid.reshape(b * (B + 1), d.hidden), gpu.drafter.dt, dev).reshape(b, B + 1, d.hidden)
+        ta = torch.full((b, B + 1), -1, dtype=torch.int32, device=dev)
+        al = torch.full((b,), -1, dtype=torch.int32, device=dev)
+        bo = torch.full((b,), -1, dtype=torch.int32, device=dev)
+        gpu.drafter.verify(th, torch.as_tensor(ref["tokens"].astype(np.int32)).to(dev), ta, al, bo, b,
+                           block_size=B)
+        torch.cuda.synchronize()
+        g_ref, vgaps = O.verify(d, case.weights.lm_head, hid)
+        L_ref, bonus_ref = O.accept(ref["tokens"], g_ref)
+        assert np.array_equal(L_ref, L_plant)
+        tr.add(ta.cpu().numpy(), g_ref, vgaps, f"verify{step}")
+        al, bo = al.cpu().numpy(), bo.cpu().numpy()
+        for s_ in range(b):
+            if np.all(vgaps[s_, :min(int(L_ref[s_]), B) + 1] > Hn.GAP):   # decided above the gap
+                assert al[s_] == L_ref[s_] and bo[s_] == bonus_ref[s_], (step, s_, al, L_ref, bo, bonus_ref)
+        rows = L_ref + 1
+        last = bonus_ref.astype(np.int32)
+    assert gpu.drafter.read_status() == 0
+    assert not tr.mismatched, tr.mismatched
+    print("compared", tr.compared, "below_gap", tr.below_gap, "ctx", cache.length)
