@@ -10,7 +10,10 @@ it; see ``tests/test_oracle_*.py``):
 
 * ``rms_norm``, ``rope``, ``silu``, ``linear``, ``attention``,
   ``argmax_lowest``, ``accept``, ``inject``, ``draft_forward``,
-  ``draft_anchors``, ``verify``,
+  ``draft_anchors``, ``verify``, ``gumbel``, ``sample_categorical``,
+  ``draft_sample``, ``speculative_verify`` (the last four by closed-form
+  distribution tests: chi-square against softmax and against the target's
+  distribution at every emitted position),
   ``speedup``: pinned by brute force, closed forms and invariants.
 * End-to-end drafted token values on random weights have no external
   reference value; they are pinned only through the invariants above
@@ -25,11 +28,15 @@ from .dflash_oracle import (  # noqa: F401
     draft_anchors,
     draft_block,
     draft_forward,
+    draft_sample,
+    gumbel,
     inject,
     linear,
     rms_norm,
     rope,
     silu,
+    sample_categorical,
+    speculative_verify,
     speedup,
     verify,
 )

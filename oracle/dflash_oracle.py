@@ -309,3 +309,83 @@ def verify(dims, lm_head: np.ndarray, target_hidden: np.ndarray):
     logits = linear(th, lm_head)
     return argmax_lowest(logits)
 
+
+
+# ------------------------------------------------------- temperature sampling
+
+def gumbel(u: np.ndarray) -> np.ndarray:
+    """Gumbel noise -log(-log u) of uniforms u in (0, 1)."""
+    u = np.asarray(u, dtype=np.float64)
+    return -np.log(-np.log(u))
+
+
+def sample_categorical(log_weights: np.ndarray, u: np.ndarray):
+    """A draw from the distribution proportional to exp(log_weights) along
+    the last axis, by the Gumbel-max property: the lowest-index argmax of
+    log_weights + gumbel(u).  Entries with weight 0 carry -inf.  Returns the
+    index and the top-1/top-2 gap of the perturbed values."""
+    return argmax_lowest(np.asarray(log_weights, dtype=np.float64) + gumbel(u))
+
+
+def log_softmax(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max(axis=-1, keepdims=True)
+    return x - m - np.log(np.exp(x - m).sum(axis=-1, keepdims=True))
+
+
+def draft_sample(dims, weights, cache: OracleCache, last_tok, temperature: float, u):
+    """The drafting pass with each slot's token drawn from the drafter's
+    distribution q_j = softmax(l_j / T) ([Term/WF] stage two: the masked
+    positions are filled with sampled tokens).  u: uniforms [b, B, V].
+    Returns the draft_forward outputs plus "tokens" / "gaps" of the sampled
+    draw and the logits."""
+    dr = draft_forward(dims, weights, cache, last_tok, keep_logits=True)
+    tok, gaps = sample_categorical(dr["logits"] / float(temperature), u)
+    dr["tokens"], dr["gaps"] = tok, gaps
+    return dr
+
+
+def speculative_verify(draft, q_logits, p_logits, temperature: float, u_accept, u_resid):
+    """Speculative-sampling verification ([Term/WF] stage three: each
+    drafted token is checked against the target by an acceptance criterion,
+    the accepted prefix is emitted and the target supplies the next token).
+
+    Reading of the criterion: the standard speculative-sampling rule.  With
+    q_j = softmax(q_logits_j / T) (drafter) and p_j = softmax(p_logits_j / T)
+    (target), drafted token d_j is accepted when u_accept_j <= p_j(d_j) /
+    q_j(d_j), slot by slot; at the first rejected slot j the next token is
+    drawn from max(0, p_j - q_j) (normalised), and after B accepted slots
+    from p_B.  Draws use sample_categorical with u_resid.
+
+    draft [b, B], q_logits [b, B, V], p_logits [b, B+1, V], u_accept [b, B],
+    u_resid [b, V].  Returns (accept_len [b], next_tok [b], margins [b]: the
+    smallest |log(p/q) - log u| over the decisions taken, and gaps [b]: the
+    top-1/top-2 gap of the final draw)."""
+    draft = np.asarray(draft)
+    b, B = draft.shape
+    L = np.zeros(b, dtype=np.int64)
+    nxt = np.zeros(b, dtype=np.int64)
+    margins = np.full(b, np.inf)
+    gaps = np.zeros(b)
+    T = float(temperature)
+    for s in range(b):
+        lq = log_softmax(np.asarray(q_logits[s], dtype=np.float64) / T)
+        lp = log_softmax(np.asarray(p_logits[s], dtype=np.float64) / T)
+        j = 0
+        while j < B:
+            d = int(draft[s, j])
+            diff = (lp[j, d] - lq[j, d]) - np.log(float(u_accept[s, j]))
+            margins[s] = min(margins[s], abs(diff))
+            if diff >= 0.0:
+                j += 1
+            else:
+                break
+        if j < B:
+            w = np.maximum(0.0, np.exp(lp[j]) - np.exp(lq[j]))
+            with np.errstate(divide="ignore"):
+                logw = np.where(w > 0.0, np.log(np.where(w > 0.0, w, 1.0)), -np.inf)
+        else:
+            logw = lp[B]
+        t, gap = sample_categorical(logw, u_resid[s])
+        L[s], nxt[s], gaps[s] = j, int(t), float(gap)
+    return L, nxt, margins, gaps

@@ -468,6 +468,101 @@ def check_anchor_closed_form():
         assert np.allclose(out["attn_out"][0][a, 0], o, atol=1e-12), (C, out["attn_out"][0][a, 0], o)
 
 
+def _uniforms(rng, shape):
+    """Uniforms in (0, 1) on the 2^-24 grid (exact in fp32 and fp64)."""
+    return (np.floor(rng.random(shape) * (1 << 24)) + 0.5) / (1 << 24)
+
+
+def _chi2_pvalue(counts, probs):
+    from scipy.stats import chi2
+    counts = np.asarray(counts, dtype=np.float64)
+    exp = np.asarray(probs, dtype=np.float64) * counts.sum()
+    stat = float(np.sum((counts - exp) ** 2 / exp))
+    return float(chi2.sf(stat, len(probs) - 1))
+
+
+def _softmax(x):
+    e = np.exp(x - np.max(x))
+    return e / e.sum()
+
+
+def check_gumbel_max_is_softmax():
+    """Gumbel-max draws follow softmax(weights): chi-square on 40000 draws,
+    for two sets of weights, and a set of weights with a zero entry is never
+    drawn there."""
+    rng = np.random.default_rng(12)
+    for l in (np.array([0.3, -1.2, 1.5, 0.0, 0.8]), np.array([2.0, 2.0, -3.0, 0.5, 1.0])):
+        u = _uniforms(rng, (40000, 5))
+        tok, _ = O.sample_categorical(np.broadcast_to(l, u.shape), u)
+        assert _chi2_pvalue(np.bincount(tok, minlength=5), _softmax(l)) > 1e-4
+    lw = np.array([0.0, -np.inf, 1.0])
+    tok, _ = O.sample_categorical(np.broadcast_to(lw, (2000, 3)), _uniforms(rng, (2000, 3)))
+    assert not np.any(tok == 1)
+
+
+def check_draft_sample_temperature():
+    """Sampled drafting on the identity drafter (closed-form logits: the
+    embedding rows against the normalised block hidden state): the drafted
+    token follows softmax(logits / T) at T = 0.5 and 2 (chi-square), and a
+    vanishing temperature gives the greedy token."""
+    dims, w = _identity_drafter()
+    cache = O.OracleCache.empty(dims, 1, 8)
+    O.inject(dims, w, cache, [np.array([[1.0, 0.0]])])
+    greedy = O.draft_forward(dims, w, cache, np.array([1]), keep_logits=True)
+    logits = greedy["logits"][0, 0]
+    rng = np.random.default_rng(13)
+    for T in (0.5, 2.0):
+        toks = []
+        for _ in range(6000):
+            toks.append(int(O.draft_sample(dims, w, cache, np.array([1]), T, _uniforms(rng, (1, 1, 4)))["tokens"][0, 0]))
+        assert _chi2_pvalue(np.bincount(toks, minlength=4), _softmax(logits / T)) > 1e-4, T
+    z = O.draft_sample(dims, w, cache, np.array([1]), 1e-6, _uniforms(rng, (1, 1, 4)))
+    assert z["tokens"][0, 0] == greedy["tokens"][0, 0]
+
+
+def check_speculative_sampling_is_lossless():
+    """The defining property of the acceptance rule: every emitted token is
+    distributed as the target's distribution at its position.  Over 30000
+    sampled drafts (V = 6, B = 3) the first emitted token follows p_0, the
+    second (given the first draft accepted) p_1, the third p_2, and the token
+    after a fully accepted block p_3, at T = 1 and T = 0.7 (chi-square)."""
+    rng = np.random.default_rng(14)
+    V, B, N = 6, 3, 30000
+    ql = rng.standard_normal((B, V)) * 1.2
+    pl = np.concatenate([ql + rng.standard_normal((B, V)) * 0.8, rng.standard_normal((1, V))])
+    for T in (1.0, 0.7):
+        qN = np.broadcast_to(ql, (N, B, V))
+        pN = np.broadcast_to(pl, (N, B + 1, V))
+        d, _ = O.sample_categorical(qN / T, _uniforms(rng, (N, B, V)))
+        L, nxt, _, _ = O.speculative_verify(d, qN, pN, T, _uniforms(rng, (N, B)), _uniforms(rng, (N, V)))
+        assert np.all((L >= 0) & (L <= B))
+        for j in range(B + 1):
+            reach = L >= j                        # position j is emitted in these trials
+            emitted = np.where(L[reach] > j, d[reach, min(j, B - 1)], nxt[reach])
+            if j == B:
+                emitted = nxt[reach]
+            assert reach.sum() > 2000, (j, reach.sum())
+            pj = _softmax(pl[j] / T)
+            assert _chi2_pvalue(np.bincount(emitted, minlength=V), pj) > 1e-4, (T, j)
+
+
+def check_speculative_special_cases():
+    """Closed cases of the rule: a draft whose distribution equals the
+    target's is always accepted; a drafted token the target gives (almost)
+    no mass is rejected, and the token drawn in its place is never it."""
+    rng = np.random.default_rng(15)
+    V, B, N = 5, 4, 500
+    ql = rng.standard_normal((N, B, V))
+    pl = np.concatenate([ql, rng.standard_normal((N, 1, V))], axis=1)
+    d, _ = O.sample_categorical(ql, _uniforms(rng, (N, B, V)))
+    L, _, _, _ = O.speculative_verify(d, ql, pl, 1.0, _uniforms(rng, (N, B)), _uniforms(rng, (N, V)))
+    assert np.all(L == B)
+    pl2 = pl.copy()
+    pl2[np.arange(N), 0, d[:, 0]] = -60.0          # the target all but forbids the first draft
+    L, nxt, _, _ = O.speculative_verify(d, ql, pl2, 1.0, _uniforms(rng, (N, B)), _uniforms(rng, (N, V)))
+    assert np.all(L == 0) and np.all(nxt != d[:, 0])
+
+
 def check_planted_recovery():
     """Verify on planted target states recovers the planted accept length
     and fallback token exactly (the self-logit margin is large)."""
@@ -510,5 +605,7 @@ ALL_CHECKS = [
     check_draft_closed_form,
     check_anchor_frontier_is_the_draft, check_anchor_sees_only_its_prefix,
     check_anchor_blocks_independent, check_anchor_closed_form,
+    check_gumbel_max_is_softmax, check_draft_sample_temperature,
+    check_speculative_sampling_is_lossless, check_speculative_special_cases,
     check_planted_recovery, check_cost_model_simulation,
 ]

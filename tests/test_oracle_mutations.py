@@ -40,6 +40,15 @@ MUTATIONS = {
     "anchor sees the whole context": ("np.array([p], dtype=np.int64))", "cache.length[s:s + 1].copy())"),
     "anchor one position late": ("view = OracleCache(cache.k[:, s:s + 1], cache.v[:, s:s + 1], np.array([p], dtype=np.int64))",
                                  "view = OracleCache(cache.k[:, s:s + 1], cache.v[:, s:s + 1], np.array([p + 1], dtype=np.int64))"),
+    "gumbel sign": ("return -np.log(-np.log(u))", "return np.log(-np.log(u))"),
+    "draft sample ignores temperature": ('tok, gaps = sample_categorical(dr["logits"] / float(temperature), u)',
+                                         'tok, gaps = sample_categorical(dr["logits"], u)'),
+    "accept ratio inverted": ("diff = (lp[j, d] - lq[j, d]) - np.log(float(u_accept[s, j]))",
+                              "diff = (lq[j, d] - lp[j, d]) - np.log(float(u_accept[s, j]))"),
+    "residual q minus p": ("w = np.maximum(0.0, np.exp(lp[j]) - np.exp(lq[j]))",
+                           "w = np.maximum(0.0, np.exp(lq[j]) - np.exp(lp[j]))"),
+    "residual without clipping": ("w = np.maximum(0.0, np.exp(lp[j]) - np.exp(lq[j]))", "w = np.exp(lp[j])"),
+    "bonus from the last drafted row": ("logw = lp[B]", "logw = lp[B - 1]"),
     "inject wrong slot": ("cache.k[l, s, :, start:start + n, :] = k.transpose(1, 0, 2)",
                           "cache.k[l, s, :, start + 1:start + n + 1, :] = k.transpose(1, 0, 2)"),
 }
@@ -71,4 +80,5 @@ def test_planted_mistake_is_caught(tag, monkeypatch):
             check()
         except Exception as exc:  # AssertionError or a shape error: either way caught
             caught.append(check.__name__)
+            break                 # one catching pin is enough
     assert caught, f"no pin catches the planted mistake '{tag}'"
