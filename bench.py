@@ -58,6 +58,9 @@ STEP_TILED_MIN_ROWS = 17
 EXTRAS = [("qwen3-8b-b32", 16), ("qwen3-8b-long", 16), ("larger-b8", 4), ("larger-b8", 8),
           ("larger-b8", 16)]
 EXTRA_STEPS, EXTRA_WARMUP = 10, 3
+# Workloads that also time a temperature-1 step (sampled drafting and
+# speculative-sampling verification).
+SAMPLING_WORKLOADS = ("qwen3-8b-b1", "qwen3-8b-b32")
 
 
 def time_graph(args, torch, b: int, rewind, run, outs):
@@ -182,6 +185,48 @@ def copy_ceiling(torch, dev, mib: int = 1024, reps: int = 5):
     del src, dst
     return {"GBs": round(2 * n / (ms * 1e-3) / 1e9, 1), "bytes_moved": 2 * n, "ms": round(ms, 4),
             "method": f"torch copy_ of {mib} MiB on the device, read + write bytes / mean event time of {reps}"}
+
+
+def time_sampling(torch, dr, b, B, V, feats_t, cu, R, last_t, th, rewind, steps, greedy_ms):
+    """The same step at temperature 1: inject, sampled drafting
+    (dflash_draft_sample) and speculative-sampling verification
+    (dflash_verify_sample), the uniforms drawn on the device beforehand
+    (seeded inputs).  Returns its time per step next to the greedy one."""
+    dev = dr.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    grid = float(1 << 24)
+    unif = lambda *shape: (torch.randint(0, 1 << 24, shape, device=dev, generator=gen).float() + 0.5) / grid
+    u_draft, u_acc, u_res = unif(b * B, V), unif(b, B), unif(b, V)
+    dlog = torch.empty((b * B, V), dtype=torch.float32, device=dev)
+    tlog = torch.empty((b * (B + 1), V), dtype=torch.float32, device=dev)
+    out = torch.empty((b, B), dtype=torch.int32, device=dev)
+    al = torch.empty(b, dtype=torch.int32, device=dev)
+    nx = torch.empty(b, dtype=torch.int32, device=dev)
+
+    def step():
+        rewind()
+        dr.inject(feats_t, cu, b, R)
+        dr.draft_sample(last_t, 1.0, u_draft, out, dlog, b)
+        dr.verify_sample(th, out, dlog, 1.0, u_acc, u_res, tlog, al, nx, b)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"temperature": 1.0, "ms_per_step": round(ms, 4), "value": round(b * 1000.0 / ms, 2),
+            "unit": "block-steps/s", "vs_greedy_step": round(ms / greedy_ms, 4), "steps": steps,
+            "mean_accept_len": float(al.float().mean().item()),
+            "note": "inject + dflash_draft_sample + dflash_verify_sample; logits of both heads in HBM "
+                    "(fp32), uniforms generated on the device before timing; includes one rewind of the "
+                    "context lengths per step"}
 
 
 def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cpu_leg: str):
@@ -358,6 +403,10 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
     verify_ms = float(np.mean(verify_samples))
     status = dr_gpu.read_status()
 
+    sampled = None
+    if getattr(args, "sampling_steps", 0) > 0 and name in SAMPLING_WORKLOADS:
+        sampled = time_sampling(torch, dr_gpu, b, B, d.vocab, feats_t, cu, R, last_t, th, rewind,
+                                args.sampling_steps, ms_step)
     got_draft = draft_out.cpu().numpy()
     got_acc = acc.cpu().numpy()
     parity = None
@@ -451,6 +500,7 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
                    "planted_against": "oracle draft" if cpu_leg == "full" else
                    ("oracle draft (sequence 0), random tokens elsewhere" if cpu_leg == "one" else "random tokens")},
         "draft_parity": parity,
+        "sampling_T1": sampled,
         "status": status,
     }
 
@@ -470,6 +520,8 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", type=int, default=1024, metavar="MIB",
                     help="size of the timed plain device copy (a measured HBM ceiling; the reference "
                          "dispatch for HBM byte counters); 0 skips it")
+    ap.add_argument("--sampling-steps", type=int, default=10,
+                    help="timed temperature-1 steps on the batch-1 and batch-32 workloads (0: none)")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the headline workload only")
     ap.add_argument("--extras", default="",

@@ -161,16 +161,24 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
 }
 
 struct VerifyLayout {
-  size_t end;
+  size_t lse, end;
   GemmPlan lm;
 };
 
-VerifyLayout verify_layout(const dflash_dims *d, int batch) {
+// The greedy verify call needs the counter area only; the sampling one adds
+// the log-sum-exp of its batch * (2B + 1) logit rows.
+VerifyLayout verify_layout(const dflash_dims *d, int batch, bool sampling = false) {
   VerifyLayout L{};
   L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, 2, STEP_TILED_MIN_ROWS);
-  L.end = WS_COUNTER_BYTES;
+  Bump b;
+  L.lse = sampling ? b.take(size_t(batch) * (2 * d->block_size + 1) * 4) : 0;
+  L.end = sampling ? b.off : WS_COUNTER_BYTES;
   return L;
 }
+
+// Vocabulary chunks per row of the sampling kernels: about 2048 entries
+// each, at most one per argmax slot.
+int sample_chunks(int vocab) { return std::max(1, std::min(ARGMAX_SLOTS, (vocab + 2047) / 2048)); }
 
 struct InjectLayout {
   size_t u, xc, ssq, rs, part, end, pc;
@@ -506,7 +514,7 @@ int dflash_kv_export(const dflash_dims *d, const dflash_kv *kv, void *k, void *v
 size_t dflash_workspace_bytes(const dflash_dims *d, int32_t max_batch, int32_t max_rows) {
   if (check_dims(d) != DFLASH_OK || max_batch < 1 || max_batch > MAX_BATCH || max_rows < 0) return 0;
   size_t need = draft_layout(d, max_batch).end;
-  need = std::max(need, verify_layout(d, max_batch).end);
+  need = std::max(need, verify_layout(d, max_batch, true).end);
   need = std::max(need, inject_layout(d, std::max(1, max_rows)).end);
   return (need + 255) & ~size_t(255);
 }
@@ -626,7 +634,8 @@ int dflash_inject_kv(const dflash_dims *d, const dflash_weights *w, const dflash
 // read).
 static int draft_impl(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
                       const int32_t *anchor_seq, const int32_t *anchor_pos, int32_t batch, int32_t *draft, void *ws,
-                      size_t ws_bytes, hipStream_t stream) {
+                      size_t ws_bytes, hipStream_t stream, float temperature = 0.f, const float *u_draft = nullptr,
+                      float *draft_logits = nullptr) {
   TRY(check_dims(d));
   TRY(check_weights(d, w, false, true));
   TRY(check_kv(d, kv));
@@ -810,7 +819,24 @@ static int draft_impl(const dflash_dims *d, const dflash_weights *w, const dflas
   fp.block = d->block_size;
   fp.verify = 0;
   fp.tok_out = draft;
-  return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "draft");
+  if (temperature <= 0.f) return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "draft");
+  // Sampling: the head stores its logits; Gumbel-max per row, folded by the
+  // argmax finish.
+  lm.out_f32 = draft_logits;
+  lm.ld_out = d->vocab;
+  e = launch_gemm(d->dtype, EPI_LOGITS, lm, stream);
+  if (e != hipSuccess) return hip_fail(e, "draft logits");
+  SampleParams sp{};
+  sp.logits = draft_logits;
+  sp.ld = d->vocab;
+  sp.vocab = d->vocab;
+  sp.chunks = sample_chunks(d->vocab);
+  sp.inv_t = 1.0f / temperature;
+  sp.u = u_draft;
+  sp.keys = lm.keys;
+  e = launch_gumbel_draft(sp, L.M, stream);
+  if (e == hipSuccess) e = launch_argmax_finish(fp, batch, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "draft sampling");
 }
 
 int dflash_draft_forward(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
@@ -823,6 +849,80 @@ int dflash_draft_anchors(const dflash_dims *d, const dflash_weights *w, const df
                          void *ws, size_t ws_bytes, hipStream_t stream) {
   TRY(check_ptr(anchor_pos, "anchor_pos", false));
   return draft_impl(d, w, kv, anchor_tok, anchor_seq, anchor_pos, nblocks, draft, ws, ws_bytes, stream);
+}
+
+int dflash_draft_sample(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
+                        int32_t batch, float temperature, const float *u_draft, int32_t *draft, float *draft_logits,
+                        void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_ERR_SHAPE, "temperature must be positive and finite (greedy drafting: dflash_draft_forward)");
+  TRY(check_ptr(u_draft, "u_draft", false));
+  TRY(check_ptr(draft_logits, "draft_logits", false));
+  return draft_impl(d, w, kv, last_tok, nullptr, nullptr, batch, draft, ws, ws_bytes, stream, temperature, u_draft,
+                    draft_logits);
+}
+
+int dflash_verify_sample(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,
+                         const float *draft_logits, int32_t batch, float temperature, const float *u_accept,
+                         const float *u_resid, float *target_logits, int32_t *accept_len, int32_t *next_tok,
+                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  TRY(check_dims(d));
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_ERR_SHAPE, "temperature must be positive and finite (greedy verification: dflash_verify_accept)");
+  TRY(check_ptr(lm_head, "lm_head"));
+  TRY(check_ptr(target_hidden, "target_hidden"));
+  TRY(check_ptr(draft, "draft", false));
+  TRY(check_ptr(draft_logits, "draft_logits", false));
+  TRY(check_ptr(u_accept, "u_accept", false));
+  TRY(check_ptr(u_resid, "u_resid", false));
+  TRY(check_ptr(target_logits, "target_logits", false));
+  TRY(check_ptr(accept_len, "accept_len", false));
+  TRY(check_ptr(next_tok, "next_tok", false));
+  TRY(check_ptr(ws, "ws"));
+  if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
+  const VerifyLayout L = verify_layout(d, batch, true);
+  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
+  char *wsb = static_cast<char *>(ws);
+  const int B = d->block_size, V = d->vocab;
+  GemmParams lm{};
+  fill_gemm(lm, L.lm);
+  lm.w_seg[0] = static_cast<const char *>(lm_head);
+  lm.x = static_cast<const char *>(target_hidden);
+  lm.x_ld = d->hidden;
+  lm.vocab = V;
+  lm.out_f32 = target_logits;
+  lm.ld_out = V;
+  hipError_t e = launch_gemm(d->dtype, EPI_LOGITS, lm, stream);
+  if (e != hipSuccess) return hip_fail(e, "verify logits");
+  const float inv_t = 1.0f / temperature;
+  float *lse_q = reinterpret_cast<float *>(wsb + L.lse), *lse_p = lse_q + size_t(batch) * B;
+  e = launch_row_lse(draft_logits, V, V, inv_t, batch * B, lse_q, stream);
+  if (e == hipSuccess) e = launch_row_lse(target_logits, V, V, inv_t, batch * (B + 1), lse_p, stream);
+  if (e != hipSuccess) return hip_fail(e, "verify log-sum-exp");
+  SampleParams sp{};
+  sp.ld = V;
+  sp.vocab = V;
+  sp.chunks = sample_chunks(V);
+  sp.inv_t = inv_t;
+  sp.keys = reinterpret_cast<unsigned long long *>(wsb);
+  sp.q_logits = draft_logits;
+  sp.p_logits = target_logits;
+  sp.lse_q = lse_q;
+  sp.lse_p = lse_p;
+  sp.draft = draft;
+  sp.block = B;
+  sp.u_accept = u_accept;
+  sp.u_resid = u_resid;
+  sp.accept_len = accept_len;
+  e = launch_spec_sample(sp, batch, stream);
+  ArgmaxFinishParams fp{};
+  fp.keys = sp.keys;
+  fp.rows_per_seq = 1;
+  fp.block = 1;
+  fp.verify = 0;
+  fp.tok_out = next_tok;
+  if (e == hipSuccess) e = launch_argmax_finish(fp, batch, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "verify sampling");
 }
 
 int dflash_verify_accept(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *draft,

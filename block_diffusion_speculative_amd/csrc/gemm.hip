@@ -157,6 +157,12 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
         store_elem<T>(base + vcache_offset<T>(pos, dd, d), v);
       }
     }
+  } else if constexpr (EPI == EPI_LOGITS) {
+    for (int e = threadIdx.x; e < R * CN; e += NT) {
+      const int ml = e / CN, nl = e % CN;
+      const int m = mblk * R + ml, n = nblk * CN + nl;
+      if (m < p.M && n < p.vocab) p.out_f32[size_t(m) * p.ld_out + n] = val(ml, nl);
+    }
   } else if constexpr (EPI == EPI_ARGMAX) {
     // Running best (logit, index) key per row over this workgroup's tiles:
     // one element per thread, a 32-lane shuffle max per row (CN == 32), and
@@ -245,7 +251,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   // Consumers of an RMSNorm (packed activations into QKV, KV injection,
   // gate/up, the draft head) scale their output rows; the other launches
   // carry no row-scale code.
-  constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX);
+  constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX ||
+                                EPI == EPI_LOGITS);
   __shared__ float rs_row[RS ? R : 1];
   __shared__ f32x4 rs_stage[RS ? RS_STAGE_FLOATS / 4 : 1];  // tile sums of the block's rows
 
@@ -692,6 +699,7 @@ static hipError_t launch_t(int epi, const GemmParams &p, hipStream_t s) {
     case EPI_KVINJ: return p.NB == 1 ? launch_mt<T, EPI_KVINJ, 1>(p, s) : hipErrorInvalidValue;
     case EPI_SWIGLU: return p.NB == 2 ? launch_mt<T, EPI_SWIGLU, 2>(p, s) : hipErrorInvalidValue;
     case EPI_ARGMAX: return p.NB == 2 ? launch_mt<T, EPI_ARGMAX, 2>(p, s) : hipErrorInvalidValue;
+    case EPI_LOGITS: return p.NB == 2 ? launch_mt<T, EPI_LOGITS, 2>(p, s) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

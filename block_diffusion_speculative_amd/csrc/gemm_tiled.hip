@@ -38,8 +38,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   static_assert(TL_WM * WGM == TM && TL_WN * WGN == TN, "wave grid divides the tile");
   static_assert(TM * 16 <= TL_WAVES * 64, "one thread per token row of the tile");
   // two-tile items (gate/up pairs, the heads) use the paired weight layout
-  constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_ARGMAX;
-  constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX);
+  constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_ARGMAX || EPI == EPI_LOGITS;
+  constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX ||
+                                EPI == EPI_LOGITS);
   constexpr int XT = TL_MT * XS;                              // activation fragments per stage
   constexpr int ST = XT + TL_NT;                              // fragments per stage
   constexpr int LPW = (ST + TL_WAVES - 1) / TL_WAVES;         // loads per wavefront per stage
@@ -215,6 +216,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
         o = __shfl_xor(k, 32, 64);
         k = o > k ? o : k;
         if (g == 0 && mok) __hip_atomic_fetch_max(best_row + ml, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+        for (int b = 0; b < TL_WN; ++b) {
+          const int n0 = (nblk * TL_NT + wn * TL_WN + b) * 16 + 4 * g;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (mok && n0 + i < p.vocab) p.out_f32[size_t(m) * p.ld_out + n0 + i] = acc[a][b][i] * rs;
+        }
       } else if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int b = 0; b < TL_WN; b += 2) {
@@ -467,7 +476,8 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   const int cu = p.grid_cap;
   auto blocks = [](int n, int b) { return (n + b - 1) / b; };
   const int mt = blocks(p.M, 16);
-  if (EPI == EPI_ARGMAX) {
+  constexpr bool HEAD = EPI == EPI_ARGMAX || EPI == EPI_LOGITS;   // vocabulary-wide heads
+  if (HEAD) {
     // at least 4 fragments: 2 (17-32 rows) would leave half the wave grid
     // without a row tile
     if (mt <= 12) p.tile_m = mt <= 4 ? 4 : (mt + 1) & ~1;
@@ -483,7 +493,7 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   // Too few items for the compute units: split each item's k-tiles into
   // parts of at least 16.
   p.ksplit = 1;
-  if (EPI != EPI_ARGMAX && p.part_ws && p.part_cnt && 2 * items <= cu) {
+  if (!HEAD && p.part_ws && p.part_cnt && 2 * items <= cu) {
     const int cap = cu < MAX_SPLIT_UNITS ? cu : MAX_SPLIT_UNITS;
     int ks = cap / items;
     if (ks > p.k_tiles / 16) ks = p.k_tiles / 16;
@@ -493,7 +503,7 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   const int units = items * p.ksplit;
   int grid = units < cu ? units : cu;
   grid = grid < TL_XCDS ? TL_XCDS : grid - grid % TL_XCDS;
-  if constexpr (EPI == EPI_ARGMAX && XS == 1) {
+  if constexpr (HEAD && XS == 1) {
     switch (p.tile_m) {
       case 4: launch_tiled_shape<T, EPI, XS, XROW, 4, 16, 2, 4>(p, grid, s); break;
       case 6: launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s); break;
@@ -503,7 +513,7 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else {
-    if (EPI == EPI_ARGMAX && p.tile_m != 8) return hipErrorInvalidValue;
+    if (HEAD && p.tile_m != 8) return hipErrorInvalidValue;
     if (p.tile_m == 8) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
     else launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
   }
@@ -528,6 +538,7 @@ static hipError_t launch_tiled_t(int epi, const GemmParams &p, hipStream_t s) {
     case EPI_KVINJ: return launch_tiled_x<T, EPI_KVINJ>(p, s);
     case EPI_SWIGLU: return launch_tiled_x<T, EPI_SWIGLU>(p, s);
     case EPI_ARGMAX: return launch_tiled_x<T, EPI_ARGMAX>(p, s);
+    case EPI_LOGITS: return launch_tiled_x<T, EPI_LOGITS>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -42,6 +42,7 @@ enum Epilogue : int {
   EPI_QKV = 3,     // RoPE on q and k of the block; q -> qbuf, k/v -> kblk/vblk
   EPI_KVINJ = 4,   // RoPE on injected k; k/v appended to the cache
   EPI_ARGMAX = 5,  // lowest-index argmax over the vocabulary (+ acceptance)
+  EPI_LOGITS = 6,  // fp32 logits out_f32[m, n] for n < vocab (temperature sampling)
 };
 
 struct ArgmaxFinishParams {
@@ -182,6 +183,28 @@ struct EmbedParams {
   int max_batch, capacity;
   int *blk_ctx, *blk_region;
 };
+
+// Temperature sampling (sampling.hip).  Logit rows are fp32 [rows][ld];
+// uniforms u lie in (0, 1).  Gumbel-max: a row's sample is the lowest-index
+// argmax of logit * inv_t - log(-log u).
+struct SampleParams {
+  const float *logits;          // draft: the rows sampled
+  int ld, vocab, chunks;        // chunks of the vocabulary per row (<= ARGMAX_SLOTS)
+  float inv_t;                  // 1 / temperature
+  const float *u;               // draft: [rows][vocab] uniforms
+  unsigned long long *keys;     // argmax key slots, [rows][ARGMAX_SLOTS]
+  // speculative verification (one sequence per grid row)
+  const float *q_logits, *p_logits;   // draft rows [b * B][ld], target rows [b * (B + 1)][ld]
+  const float *lse_q, *lse_p;         // their log-sum-exp of logit * inv_t
+  const int *draft;                   // [b][B]
+  int block;
+  const float *u_accept;              // [b][B]
+  const float *u_resid;               // [b][vocab]
+  int *accept_len;                    // [b] out
+};
+hipError_t launch_gumbel_draft(const SampleParams &p, int rows, hipStream_t s);
+hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, int rows, float *lse, hipStream_t s);
+hipError_t launch_spec_sample(const SampleParams &p, int batch, hipStream_t s);
 
 // Greedy verification with its scratch (argmax key slots and the arrival
 // counter, at least WS_COUNTER_BYTES, zero on entry) at wsb: the body of

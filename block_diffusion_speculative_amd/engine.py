@@ -167,6 +167,24 @@ class Drafter:
                   _ptr(anchor_seq), _ptr(anchor_pos), _ptr(anchor_tok), nblocks, _ptr(out),
                   self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
 
+    def draft_sample(self, last_tok: torch.Tensor, temperature: float, u_draft: torch.Tensor,
+                     out: torch.Tensor, draft_logits: torch.Tensor, batch: int, stream=None,
+                     block_size: Optional[int] = None):
+        cd = self.dims_for(block_size)
+        _lib.call("dflash_draft_sample", ctypes.byref(cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
+                  _ptr(last_tok), batch, float(temperature), _ptr(u_draft), _ptr(out), _ptr(draft_logits),
+                  self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
+
+    def verify_sample(self, target_hidden: torch.Tensor, draft: torch.Tensor, draft_logits: torch.Tensor,
+                      temperature: float, u_accept: torch.Tensor, u_resid: torch.Tensor,
+                      target_logits: torch.Tensor, accept_len: torch.Tensor, next_tok: torch.Tensor,
+                      batch: int, stream=None, block_size: Optional[int] = None):
+        cd = self.dims_for(block_size)
+        _lib.call("dflash_verify_sample", ctypes.byref(cd), self.lm_head.data_ptr(), _ptr(target_hidden),
+                  _ptr(draft), _ptr(draft_logits), batch, float(temperature), _ptr(u_accept), _ptr(u_resid),
+                  _ptr(target_logits), _ptr(accept_len), _ptr(next_tok), self.ws.data_ptr(), self.ws_bytes,
+                  _stream_ptr(stream))
+
     def verify(self, target_hidden: torch.Tensor, draft: torch.Tensor, target_argmax: torch.Tensor,
                accept_len: torch.Tensor, bonus: torch.Tensor, batch: int, stream=None,
                block_size: Optional[int] = None):

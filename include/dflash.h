@@ -263,6 +263,48 @@ int dflash_draft_anchors(const dflash_dims *dims, const dflash_weights *w, const
                          const int32_t *anchor_seq, const int32_t *anchor_pos, const int32_t *anchor_tok,
                          int32_t nblocks, int32_t *draft, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Temperature sampling ("Term: DFlash speculative decoding", "DFlash:
+ * architecture and workflow": the speculator fills masked positions with
+ * sampled tokens and the target applies an acceptance criterion; "DFlash,
+ * Diffusion LLMs, dLLM, MTP and Speculative Decoding: A Deep Research
+ * Report", "DFlash benchmark results": temperature 1).  The criterion is the
+ * standard speculative-sampling rule: with q_j = softmax(l_j / T) the
+ * drafter's and p_j = softmax(l'_j / T) the target's distribution at slot
+ * j, drafted token d_j is accepted with probability min(1, p_j(d_j) /
+ * q_j(d_j)) in slot order; at the first rejected slot the next token is
+ * drawn from the normalised residual max(0, p_j - q_j), and after B
+ * accepted slots from p_B.  Random numbers are inputs: uniforms in (0, 1),
+ * turned into Gumbel noise g = -log(-log u); a categorical draw is the
+ * lowest-index argmax of log(weight) + g over the vocabulary.
+ *
+ * dflash_draft_sample: the drafting pass of dflash_draft_forward, but each
+ * slot's token is drawn from q_j: draft[m] = argmax_v l_m(v) / T + g_m(v)
+ * with u_draft [batch * B, vocab] the uniforms of row m = s * B + j.  The
+ * head's fp32 logits l (before the temperature) go to draft_logits
+ * [batch * B, vocab] (caller-owned, read again by dflash_verify_sample).
+ * temperature > 0 (DFLASH_ERR_SHAPE otherwise). */
+int dflash_draft_sample(const dflash_dims *dims, const dflash_weights *w, const dflash_kv *kv,
+                        const int32_t *last_tok, int32_t batch, float temperature, const float *u_draft,
+                        int32_t *draft, float *draft_logits, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* dflash_verify_sample: the speculative-sampling verification of a sampled
+ * draft.  target_hidden [batch, B+1, H] and lm_head as for
+ * dflash_verify_accept; draft [batch, B] and draft_logits [batch * B, vocab]
+ * from dflash_draft_sample at the same temperature; u_accept [batch, B] the
+ * acceptance uniforms (slot j is accepted when u <= p_j(d_j) / q_j(d_j));
+ * u_resid [batch, vocab] the uniforms of the one draw per sequence (from the
+ * residual of the first rejected slot, else from p_B).  target_logits
+ * [batch * (B+1), vocab] is caller-owned scratch (it receives the target's
+ * logits).  Outputs: accept_len [batch] in [0, B] and next_tok [batch], the
+ * token the step emits after the accepted prefix.  Drafted ids outside
+ * [0, vocab) are clamped.  The workspace needs
+ * dflash_workspace_bytes(dims, batch, .). */
+int dflash_verify_sample(const dflash_dims *dims, const void *lm_head, const void *target_hidden,
+                         const int32_t *draft, const float *draft_logits, int32_t batch, float temperature,
+                         const float *u_accept, const float *u_resid, float *target_logits,
+                         int32_t *accept_len, int32_t *next_tok, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* Greedy verification.  target_hidden: [batch, B+1, H] row-major, storage
  * dtype: the target's final hidden states at its pass over
  * [x, d_0, ..., d_{B-1}].  lm_head: dflash_pack_lm_head output.  Outputs:

@@ -694,3 +694,119 @@ def test_decode_loop_block_size_per_step():
     assert gpu.drafter.read_status() == 0
     assert not tr.mismatched, tr.mismatched
     print("compared", tr.compared, "below_gap", tr.below_gap, "ctx", cache.length)
+
+
+def _grid_uniforms(seed, tid, shape):
+    """Uniforms in (0, 1) on the 2^-24 grid (exact in fp32), seeded."""
+    g = I.stream(seed, 60 + tid)
+    return ((g.integers(0, 1 << 24, size=shape) + 0.5) / float(1 << 24)).astype(np.float32)
+
+
+def _sampling_step(dims, batch, ctx, T, seed, seqs=None, kv_mode="inject"):
+    """Sampled drafting and speculative-sampling verification on both
+    sides from the same uniforms.  Drafted tokens are compared where the
+    oracle's top-1/top-2 gap of logit / T + g, in logit units (times T),
+    exceeds 1e-2; the accepted length where every acceptance decision's
+    margin |log(p/q) - log u| times T exceeds 1e-2; the emitted token where,
+    in addition, the final draw's gap does."""
+    import torch
+    d = dims
+    B, V, H = d.block_size, d.vocab, d.hidden
+    case = Hn.build_case(d, batch, ctx, seed=seed, kv_mode=kv_mode)
+    seqs = list(range(batch)) if seqs is None else list(seqs)
+    gpu = Hn.GpuRunner(case)
+    feats, last = Hn.step_inputs(case, 0, [3] * batch)
+    gpu.inject(feats)
+    cache = Hn.oracle_prefill(case, seqs)
+    O.inject(d, case.weights, cache, [feats[s] for s in seqs])
+    u_draft = _grid_uniforms(seed, 0, (batch, B, V))
+    u_acc = _grid_uniforms(seed, 1, (batch, B))
+    u_res = _grid_uniforms(seed, 2, (batch, V))
+    ref = O.draft_sample(d, case.weights, cache, last[seqs], T, u_draft[seqs])
+    dev = gpu.drafter.device
+    t = lambda a: torch.as_tensor(np.ascontiguousarray(a)).to(dev)
+    out = torch.full((batch, B), -1, dtype=torch.int32, device=dev)
+    dlog = torch.empty((batch * B, V), dtype=torch.float32, device=dev)
+    gpu.drafter.draft_sample(t(last), T, t(u_draft), out, dlog, batch)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    tr = Hn.TokenReport()
+    tr.add(got[seqs], ref["tokens"], ref["gaps"] * T, "draft")
+    assert not tr.mismatched, tr.mismatched
+    rows = np.concatenate([np.arange(s * B, (s + 1) * B) for s in seqs])
+    e_logits = Hn.rel_err_rows(dlog.cpu().numpy()[rows], ref["logits"].reshape(-1, V))
+    assert e_logits <= Hn.REL_TOL, e_logits
+    # verification of the oracle's drafted tokens (random stand-ins for the
+    # sequences the oracle does not follow) on planted target states
+    all_tok = I.stream(seed, 99, 0).integers(0, V - 1, size=(batch, B))
+    all_tok[seqs] = ref["tokens"]
+    L_plant = I.planted_accept(seed, 0, batch, 0.12, B)
+    _, hid = I.planted_targets(d, seed, 0, case.weights.lm_head, all_tok, L_plant)
+    p_logits = O.linear(hid[seqs].astype(np.float64), case.weights.lm_head)
+    L_ref, nxt_ref, margins, gaps = O.speculative_verify(all_tok[seqs], ref["logits"], p_logits, T,
+                                                         u_acc[seqs], u_res[seqs])
+    th = gpu.upload(hid.reshape(batch * (B + 1), H), gpu.drafter.dt, dev).reshape(batch, B + 1, H)
+    tlog = torch.empty((batch * (B + 1), V), dtype=torch.float32, device=dev)
+    al = torch.full((batch,), -1, dtype=torch.int32, device=dev)
+    nx = torch.full((batch,), -1, dtype=torch.int32, device=dev)
+    gpu.drafter.verify_sample(th, t(all_tok.astype(np.int32)), dlog, T, t(u_acc), t(u_res), tlog, al, nx, batch)
+    torch.cuda.synchronize()
+    al, nx = al.cpu().numpy(), nx.cpu().numpy()
+    trows = np.concatenate([np.arange(s * (B + 1), (s + 1) * (B + 1)) for s in seqs])
+    assert Hn.rel_err_rows(tlog.cpu().numpy()[trows], p_logits.reshape(-1, V)) <= Hn.REL_TOL
+    decided = compared = 0
+    for i, s in enumerate(seqs):
+        assert 0 <= al[s] <= B and 0 <= nx[s] < V
+        if margins[i] * T > Hn.GAP:
+            decided += 1
+            assert al[s] == L_ref[i], (s, al[s], L_ref[i], margins[i])
+            if gaps[i] * T > Hn.GAP:
+                compared += 1
+                assert nx[s] == nxt_ref[i], (s, nx[s], nxt_ref[i], gaps[i])
+    assert gpu.drafter.read_status() == 0
+    print(f"T={T} draft compared {tr.compared} below_gap {tr.below_gap}; accept decided {decided}/{len(seqs)}, "
+          f"next token compared {compared}; logits err {e_logits:.2e}; L {L_ref.tolist()}")
+    return tr, decided, compared
+
+
+@pytest.mark.parametrize("batch,T", [(1, 1.0), (1, 0.05), (3, 1.0), (3, 0.05)])
+def test_sampling_small(batch, T):
+    """Temperature 1 (near-uniform distributions: rejections and residual
+    draws) and 0.05 (peaked: planted prefixes accepted); batch 1 runs the
+    skinny heads, batch 3 (48 draft / 51 verify rows) the tiled ones."""
+    tr, decided, _ = _sampling_step(SMALL_BF16, batch, [40, 77, 130][:batch], T, seed=70 + batch)
+    assert tr.compared >= 8 and decided >= 1
+
+
+def test_sampling_large_vocab():
+    """A 65536-token vocabulary: 32 chunks per row in the sampling kernels."""
+    d = C.Dims(**{**SMALL_BF16.__dict__, "vocab": 65536})
+    _sampling_step(d, 2, [50, 90], 1.0, seed=74)
+
+
+def test_sampling_repeatable():
+    """Same uniforms, same draws; other uniforms, other draws."""
+    import torch
+    d = SMALL_BF16
+    case = Hn.build_case(d, 1, [33], seed=75)
+    gpu = Hn.GpuRunner(case)
+    dev = gpu.drafter.device
+    last = torch.as_tensor(I.last_tokens(d, 75, 0, 1)).to(dev)
+    outs = []
+    for tid in (0, 0, 5):
+        u = torch.as_tensor(_grid_uniforms(75, tid, (1, d.block_size, d.vocab))).to(dev)
+        out = torch.empty((1, d.block_size), dtype=torch.int32, device=dev)
+        dlog = torch.empty((d.block_size, d.vocab), dtype=torch.float32, device=dev)
+        gpu.drafter.draft_sample(last, 1.0, u, out, dlog, 1)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and not np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.slow
+def test_sampling_qwen3_8b_full_shape():
+    """Temperature 1 on the Qwen3-8B-shaped drafter at batch 1 over a
+    2048-position cache (imported)."""
+    w = C.get("qwen3-8b-b1")
+    tr, _, _ = _sampling_step(w.dims, 1, [2048], 1.0, seed=76, kv_mode="import")
+    assert tr.compared >= 8
