@@ -11,6 +11,8 @@ it; see ``tests/test_oracle_*.py``):
 * ``rms_norm``, ``rope``, ``silu``, ``linear``, ``attention``,
   ``argmax_lowest``, ``accept``, ``inject``, ``draft_forward``,
   ``draft_anchors``, ``verify``, ``gumbel``, ``sample_categorical``,
+  ``causal_attention``, ``target_forward``, ``commit`` (brute force,
+  causality, incremental passes over a committed cache, a closed form);
   ``draft_sample``, ``speculative_verify`` (the last four by closed-form
   distribution tests: chi-square against softmax and against the target's
   distribution at every emitted position),
@@ -25,6 +27,8 @@ from .dflash_oracle import (  # noqa: F401
     accept,
     argmax_lowest,
     attention,
+    causal_attention,
+    commit,
     draft_anchors,
     draft_block,
     draft_forward,
@@ -38,5 +42,7 @@ from .dflash_oracle import (  # noqa: F401
     sample_categorical,
     speculative_verify,
     speedup,
+    target_feature_layers,
+    target_forward,
     verify,
 )

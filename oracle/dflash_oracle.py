@@ -389,3 +389,88 @@ def speculative_verify(draft, q_logits, p_logits, temperature: float, u_accept, 
         t, gap = sample_categorical(logw, u_resid[s])
         L[s], nxt[s], gaps[s] = j, int(t), float(gap)
     return L, nxt, margins, gaps
+
+
+# ----------------------------------------------------- target verify pass
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, C: int) -> np.ndarray:
+    """Softmax attention of n new queries over C cached keys followed by
+    the n new keys, causal over the new ones: query i (position C + i) sees
+    keys 0 .. C + i.  q: [n, n_q, d]; k, v: [C + n, n_kv, d]; grouped K/V
+    heads as in ``attention``."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, nq, d = q.shape
+    group = nq // k.shape[1]
+    out = np.empty_like(q)
+    for i in range(n):
+        T = C + i + 1
+        for h in range(nq):
+            g = h // group
+            s = (k[:T, g, :] @ q[i, h, :]) / np.sqrt(d)
+            p = np.exp(s - s.max())
+            out[i, h, :] = (p / p.sum()) @ v[:T, g, :]
+    return out
+
+
+def target_feature_layers(n_layers: int, n_feat: int) -> List[int]:
+    """Reading of which target layers feed the drafter: n_feat layers spread
+    evenly through the depth, the residual stream after layer
+    floor((k + 1) * n_layers / (n_feat + 1)) (1-based) for k = 0 .. n_feat - 1,
+    returned 0-based."""
+    return [(k + 1) * n_layers // (n_feat + 1) - 1 for k in range(n_feat)]
+
+
+def target_forward(tdims, tweights, cache: OracleCache, tokens, feat_layers) -> Dict[str, np.ndarray]:
+    """The target's causal pass over n new tokens per sequence ([Term/WF]
+    stage three: the target computes its own logits at every block position;
+    [Report/KP]: the drafter is conditioned on hidden features from several
+    target layers).
+
+    The target is read as a decoder of the drafter's layer type (RMSNorm,
+    q/k/v with RoPE, grouped attention, o_proj and residual, RMSNorm, SwiGLU
+    and residual) with causal attention.  tokens [b, n] sit at positions
+    C_s .. C_s + n - 1 (C_s the cached length); their K/V are written to the
+    cache at those positions, the cached length is left as it was (the
+    caller commits the accepted rows).  Returns the final normalised hidden
+    states "hidden" [b, n, H] (what the verify head multiplies by W_lm), the
+    features [b, n, len(feat_layers) * H] (the residual stream after each
+    listed layer, layer-major) and the residual after every layer."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    b, n = tokens.shape
+    H, nq, nkv, d = tdims.hidden, tdims.n_q_heads, tdims.n_kv_heads, tdims.head_dim
+    h = np.asarray(_get(tweights, "embed")[tokens.reshape(-1)], dtype=np.float64).reshape(b, n, H)
+    resid = []
+    for l, lw in enumerate(_get(tweights, "layers")):
+        a = rms_norm(h, lw["attn_norm"], tdims.rms_eps)
+        q = linear(a, lw["wq"]).reshape(b, n, nq, d)
+        k = linear(a, lw["wk"]).reshape(b, n, nkv, d)
+        v = linear(a, lw["wv"]).reshape(b, n, nkv, d)
+        o = np.empty((b, n, nq, d))
+        for s in range(b):
+            C = int(cache.length[s])
+            if C + n > cache.k.shape[3]:
+                raise ValueError("cache capacity exceeded")
+            pos = np.arange(C, C + n)
+            qs = rope(q[s], pos, tdims.rope_theta)
+            ks = rope(k[s], pos, tdims.rope_theta)
+            cache.k[l, s, :, C:C + n, :] = ks.transpose(1, 0, 2)
+            cache.v[l, s, :, C:C + n, :] = v[s].transpose(1, 0, 2)
+            keys = cache.k[l, s, :, :C + n, :].transpose(1, 0, 2)
+            vals = cache.v[l, s, :, :C + n, :].transpose(1, 0, 2)
+            o[s] = causal_attention(qs, keys, vals, C)
+        h = h + linear(o.reshape(b, n, nq * d), lw["wo"])
+        a = rms_norm(h, lw["mlp_norm"], tdims.rms_eps)
+        h = h + linear(silu(linear(a, lw["w_gate"])) * linear(a, lw["w_up"]), lw["w_down"])
+        resid.append(h.copy())
+    feats = [resid[l] for l in feat_layers]
+    z = rms_norm(h, _get(tweights, "final_norm"), tdims.rms_eps)
+    features = np.concatenate(feats, axis=-1) if feats else np.zeros((b, n, 0))
+    return {"hidden": z, "features": features, "residual": resid}
+
+
+def commit(cache: OracleCache, accept_len) -> None:
+    """After verification the accepted prefix and the target's own next
+    token stay in the target cache: the cached length grows by L + 1."""
+    cache.length += np.asarray(accept_len, dtype=np.int64) + 1

@@ -563,6 +563,94 @@ def check_speculative_special_cases():
     assert np.all(L == 0) and np.all(nxt != d[:, 0])
 
 
+TARGET = Dims(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, n_layers=4,
+              intermediate=48, vocab=64, n_feat_layers=2, block_size=6,
+              rope_theta=1e4, rms_eps=1e-6, dtype="f32")
+
+
+def _target_cache(tdims, w, batch, C, seed=16):
+    """A target cache holding C committed positions per sequence (the
+    target's own pass over C random tokens)."""
+    cache = O.OracleCache.empty(tdims, batch, C + 40)
+    if C:
+        toks = np.random.default_rng(seed).integers(0, tdims.vocab, size=(batch, C))
+        O.target_forward(tdims, w, cache, toks, [])
+        O.commit(cache, np.full(batch, C - 1))
+    return cache
+
+
+def check_causal_attention_bruteforce():
+    """Causal attention against a per-query, per-key pure-Python loop."""
+    g = np.random.default_rng(17)
+    C, n, nq, nkv, d = 3, 4, 4, 2, 8
+    q = g.standard_normal((n, nq, d))
+    k = g.standard_normal((C + n, nkv, d))
+    v = g.standard_normal((C + n, nkv, d))
+    out = O.causal_attention(q, k, v, C)
+    for i in range(n):
+        for h in range(nq):
+            kv = h // (nq // nkv)
+            scores = []
+            for t in range(C + i + 1):
+                scores.append(sum(q[i, h, c] * k[t, kv, c] for c in range(d)) / math.sqrt(d))
+            m = max(scores)
+            e = [math.exp(x - m) for x in scores]
+            ref = [sum(e[t] * v[t, kv, c] for t in range(len(e))) / sum(e) for c in range(d)]
+            assert np.allclose(out[i, h], ref, atol=1e-12)
+
+
+def check_target_causality():
+    """Row i of the target pass does not depend on the tokens after it."""
+    w = small_weights(TARGET)
+    toks = np.random.default_rng(18).integers(0, TARGET.vocab, size=(2, 5))
+    a = O.target_forward(TARGET, w, _target_cache(TARGET, w, 2, 7), toks, [1])
+    toks2 = toks.copy()
+    toks2[:, 3] = (toks2[:, 3] + 5) % TARGET.vocab
+    b = O.target_forward(TARGET, w, _target_cache(TARGET, w, 2, 7), toks2, [1])
+    assert np.allclose(a["hidden"][:, :3], b["hidden"][:, :3], atol=1e-13)
+    assert not np.allclose(a["hidden"][:, 3], b["hidden"][:, 3])
+
+
+def check_target_incremental():
+    """Passing n tokens at once equals passing the first n1, committing
+    them, and passing the rest: positions, the cache writes and the causal
+    mask all agree.  Features are the listed layers' residuals, and the last
+    residual through the final norm is the hidden output."""
+    w = small_weights(TARGET)
+    toks = np.random.default_rng(19).integers(0, TARGET.vocab, size=(2, 7))
+    full = O.target_forward(TARGET, w, _target_cache(TARGET, w, 2, 5), toks, [0, 2])
+    c = _target_cache(TARGET, w, 2, 5)
+    first = O.target_forward(TARGET, w, c, toks[:, :3], [0, 2])
+    O.commit(c, np.full(2, 2))
+    rest = O.target_forward(TARGET, w, c, toks[:, 3:], [0, 2])
+    assert np.allclose(full["hidden"], np.concatenate([first["hidden"], rest["hidden"]], 1), atol=1e-11)
+    assert np.allclose(full["features"], np.concatenate([first["features"], rest["features"]], 1), atol=1e-11)
+    H = TARGET.hidden
+    assert np.allclose(full["features"][..., :H], full["residual"][0], atol=0)
+    assert np.allclose(full["features"][..., H:], full["residual"][2], atol=0)
+    z = O.rms_norm(full["residual"][-1], w.final_norm, TARGET.rms_eps)
+    assert np.allclose(z, full["hidden"], atol=1e-13)
+    assert O.target_feature_layers(36, 5) == [5, 11, 17, 23, 29]
+
+
+def check_target_closed_form():
+    """The identity model as a target over an empty cache, tokens [e1, e0]
+    at positions 0 and 1: row 0 attends to itself only and returns its own
+    value; row 1 weighs both rows by the cosines of their rotated keys."""
+    dims, w = _identity_drafter()
+    cache = O.OracleCache.empty(dims, 1, 8)
+    out = O.target_forward(dims, w, cache, np.array([[1, 0]]), [0])
+    r2 = math.sqrt(2.0)
+    h0 = np.array([0.0, 1.0]) + np.array([0.0, r2])          # row 0: value of itself
+    assert np.allclose(out["features"][0, 0], h0, atol=1e-12)
+    # row 1: query e0 at position 1 (angle 1), keys e1 at 0 (angle pi/2) and e0 at 1 (angle 1)
+    scores = [2.0 * math.cos(1.0 - math.pi / 2) / r2, 2.0 / r2]
+    vals = [np.array([0.0, r2]), np.array([r2, 0.0])]
+    e = [math.exp(x) for x in scores]
+    o = sum(ei * v for ei, v in zip(e, vals)) / sum(e)
+    assert np.allclose(out["features"][0, 1], np.array([1.0, 0.0]) + o, atol=1e-12)
+
+
 def check_planted_recovery():
     """Verify on planted target states recovers the planted accept length
     and fallback token exactly (the self-logit margin is large)."""
@@ -607,5 +695,7 @@ ALL_CHECKS = [
     check_anchor_blocks_independent, check_anchor_closed_form,
     check_gumbel_max_is_softmax, check_draft_sample_temperature,
     check_speculative_sampling_is_lossless, check_speculative_special_cases,
+    check_causal_attention_bruteforce, check_target_causality, check_target_incremental,
+    check_target_closed_form,
     check_planted_recovery, check_cost_model_simulation,
 ]

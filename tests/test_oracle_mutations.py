@@ -49,6 +49,14 @@ MUTATIONS = {
                            "w = np.maximum(0.0, np.exp(lq[j]) - np.exp(lp[j]))"),
     "residual without clipping": ("w = np.maximum(0.0, np.exp(lp[j]) - np.exp(lq[j]))", "w = np.exp(lp[j])"),
     "bonus from the last drafted row": ("logw = lp[B]", "logw = lp[B - 1]"),
+    "target not causal": ("T = C + i + 1", "T = C + n"),
+    "target sees one key ahead": ("T = C + i + 1", "T = min(C + i + 2, C + n)"),
+    "target positions from 0": ("            pos = np.arange(C, C + n)\n            qs = rope(q[s], pos, tdims.rope_theta)",
+                                "            pos = np.arange(0, n)\n            qs = rope(q[s], pos, tdims.rope_theta)"),
+    "commit without the next token": ("cache.length += np.asarray(accept_len, dtype=np.int64) + 1",
+                                      "cache.length += np.asarray(accept_len, dtype=np.int64)"),
+    "features one layer late": ("feats = [resid[l] for l in feat_layers]",
+                                "feats = [resid[min(l + 1, len(resid) - 1)] for l in feat_layers]"),
     "inject wrong slot": ("cache.k[l, s, :, start:start + n, :] = k.transpose(1, 0, 2)",
                           "cache.k[l, s, :, start + 1:start + n + 1, :] = k.transpose(1, 0, 2)"),
 }
