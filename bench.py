@@ -61,6 +61,9 @@ EXTRA_STEPS, EXTRA_WARMUP = 10, 3
 # Workloads that also time a temperature-1 step (sampled drafting and
 # speculative-sampling verification).
 SAMPLING_WORKLOADS = ("qwen3-8b-b1", "qwen3-8b-b32")
+# Workloads that also time the 36-layer target's verify pass and an
+# autoregressive target step (the measured cost model).
+TARGET_WORKLOADS = ("qwen3-8b-b1", "qwen3-8b-b32")
 
 
 def time_graph(args, torch, b: int, rewind, run, outs):
@@ -227,6 +230,99 @@ def time_sampling(torch, dr, b, B, V, feats_t, cu, R, last_t, th, rewind, steps,
             "note": "inject + dflash_draft_sample + dflash_verify_sample; logits of both heads in HBM "
                     "(fp32), uniforms generated on the device before timing; includes one rewind of the "
                     "context lengths per step"}
+
+
+def device_target_weights(torch, td, seed, dev):
+    """Seeded random target weights generated on the device (bf16 values of
+    N(0, 0.02^2) draws, unit gains): the 36-layer target is only timed, and
+    host generation of its seven billion values would dominate the run."""
+    from block_diffusion_speculative_amd.inputs import TargetWeights
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    H, d, I_, V = td.hidden, td.head_dim, td.intermediate, td.vocab
+    rn = lambda *shape: (torch.randn(shape, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    ones = lambda: torch.ones(H, device=dev, dtype=torch.bfloat16)
+    layers = [{"attn_norm": ones(), "wq": rn(td.n_q_heads * d, H), "wk": rn(td.n_kv_heads * d, H),
+               "wv": rn(td.n_kv_heads * d, H), "wo": rn(H, td.n_q_heads * d), "mlp_norm": ones(),
+               "w_gate": rn(I_, H), "w_up": rn(I_, H), "w_down": rn(H, I_)} for _ in range(td.n_layers)]
+    return TargetWeights(embed=rn(V, H), final_norm=ones(), layers=layers)
+
+
+def time_target(torch, dr, d, b, ctx, B, verify_bytes, step_ms, e_l, steps):
+    """The target's side of a decode step, measured: its causal verify pass
+    over the B + 1 block rows (dflash_target_forward) and an autoregressive
+    step (the same pass over one row followed by the lm_head argmax, the
+    verify call at block size 1).  Then the pages' speedup model S ~ C_AR E /
+    C_DF ("Term: DFlash speculative decoding", "Mathematical view of
+    acceptance and speedup") on measured costs: C_AR the autoregressive step,
+    C_DF this draft step plus the target's verify pass."""
+    from block_diffusion_speculative_amd import configs as C
+    from block_diffusion_speculative_amd.engine import Target
+    td = C.QWEN3_8B_TARGET
+    dev = dr.device
+    t0 = time.time()
+    cap = C.kv_capacity(int(np.max(ctx)) + B + 1)
+    tg = Target(td, device_target_weights(torch, td, 77, dev), b, cap, max_rows=B + 1, device=dev)
+    shape = (td.n_layers, b, td.n_kv_heads, cap, td.head_dim)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(78)
+    kv = [(torch.randn(shape, device=dev, generator=gen) * 1.28).to(torch.bfloat16) for _ in range(2)]
+    tg.kv_import(kv[0], kv[1])
+    del kv
+    tg.set_ctx_len(ctx)
+    feat_layers = [(k + 1) * td.n_layers // (td.n_feat_layers + 1) - 1 for k in range(td.n_feat_layers)]
+    toks = torch.randint(0, td.vocab - 1, (b, B + 1), device=dev, generator=gen, dtype=torch.int32)
+    hid = torch.empty((b, B + 1, td.hidden), dtype=torch.bfloat16, device=dev)
+    feats = torch.empty((b, B + 1, td.n_feat_layers * td.hidden), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] target (36 layers) set up in {time.time() - t0:.1f}s")
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # the pass leaves ctx_len alone, so every repetition runs at the same shape
+    t_verify_pass = timed(lambda: tg.forward(toks, b, B + 1, feat_layers, hid, feats))
+    t_one = timed(lambda: tg.forward(toks[:, :1].contiguous(), b, 1, [], hid[:, :1], None))
+    th2 = hid[:, :2].contiguous()
+    d2 = torch.zeros((b, 1), dtype=torch.int32, device=dev)
+    ta = torch.empty((b, 2), dtype=torch.int32, device=dev)
+    al = torch.empty(b, dtype=torch.int32, device=dev)
+    bo = torch.empty(b, dtype=torch.int32, device=dev)
+    t_head = timed(lambda: dr.verify(th2, d2, ta, al, bo, b, block_size=1))
+    status = tg.read_status()
+    del tg
+    torch.cuda.empty_cache()
+    H, I_ = td.hidden, td.intermediate
+    layer_bytes = ((td.n_q_heads + 2 * td.n_kv_heads) * td.head_dim * H + H * td.n_q_heads * td.head_dim
+                   + 3 * I_ * H) * 2
+    kv_bytes = int(np.sum(ctx) + b * (B + 1)) * td.n_layers * 2 * td.n_kv_heads * td.head_dim * 2
+    pass_bytes = td.n_layers * layer_bytes + kv_bytes
+    c_ar = t_one + t_head
+    c_df = step_ms + t_verify_pass
+    return {
+        "target": "Qwen3-8B-shaped: the drafter's layer type, 36 layers, hidden 4096, 32/8 heads, "
+                  "intermediate 12288, shared lm_head; seeded random weights",
+        "verify_pass_ms": round(t_verify_pass, 4), "verify_pass_rows": B + 1,
+        "verify_pass_GBs": round(pass_bytes / (t_verify_pass * 1e-3) / 1e9, 1),
+        "verify_pass_hbm_frac": round(pass_bytes / (t_verify_pass * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "verify_pass_algorithmic_bytes": pass_bytes,
+        "ar_step_ms": round(c_ar, 4), "ar_pass_one_row_ms": round(t_one, 4), "lm_head_argmax_ms": round(t_head, 4),
+        "C_AR_ms": round(c_ar, 4), "C_DF_ms": round(c_df, 4),
+        "S_with_E_L": round(c_ar * e_l / c_df, 3), "S_with_E_L_plus_bonus": round(c_ar * (e_l + 1) / c_df, 3),
+        "E_L_planted": round(e_l, 4), "status": status,
+        "source": "S = C_AR * E / C_DF, C_AR = one-row target pass + lm_head argmax, "
+                  "C_DF = draft step + the target's (B+1)-row verify pass, all measured",
+    }
 
 
 def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cpu_leg: str):
@@ -403,6 +499,10 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
     verify_ms = float(np.mean(verify_samples))
     status = dr_gpu.read_status()
 
+    measured_cost = None
+    if getattr(args, "target_steps", 0) > 0 and name in TARGET_WORKLOADS:
+        e_l_target = I.geometric_mean_accept(I.workload_geom_p(w), B)
+        measured_cost = time_target(torch, dr_gpu, d, b, ctx, B, None, ms_step, e_l_target, args.target_steps)
     sampled = None
     if getattr(args, "sampling_steps", 0) > 0 and name in SAMPLING_WORKLOADS:
         sampled = time_sampling(torch, dr_gpu, b, B, d.vocab, feats_t, cu, R, last_t, th, rewind,
@@ -491,6 +591,7 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
         "roofline": lm_roof,
         "cpu_baseline": cpu,
         "cost_model": cost,
+        "cost_model_measured": measured_cost,
         "graph": graph_res,
         "wall_s_timed": round(wall, 4),
         # Targets are planted against the oracle's drafted tokens; without the
@@ -522,6 +623,8 @@ def main(argv=None):
                          "dispatch for HBM byte counters); 0 skips it")
     ap.add_argument("--sampling-steps", type=int, default=10,
                     help="timed temperature-1 steps on the batch-1 and batch-32 workloads (0: none)")
+    ap.add_argument("--target-steps", type=int, default=10,
+                    help="timed passes of the 36-layer target on the batch-1 and batch-32 workloads (0: none)")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the headline workload only")
     ap.add_argument("--extras", default="",

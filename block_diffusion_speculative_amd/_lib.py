@@ -33,6 +33,7 @@ EXPORTED = [
     "dflash_kv_bytes", "dflash_kv_import", "dflash_kv_export",
     "dflash_workspace_bytes", "dflash_workspace_init", "dflash_workspace_view",
     "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_anchors", "dflash_draft_sample",
+    "dflash_target_workspace_bytes", "dflash_target_forward", "dflash_kv_commit",
     "dflash_verify_sample", "dflash_verify_accept", "dflash_verify_accept_noalloc",
     "dflash_status_str", "dflash_last_error", "dflash_abi_version", "dflash_build_id",
 ]
@@ -100,6 +101,10 @@ def load() -> ctypes.CDLL:
                                            c_int32, P, P, c_size_t, P]),
         "dflash_draft_anchors": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, P, P,
                                            c_int32, P, P, c_size_t, P]),
+        "dflash_target_workspace_bytes": (c_size_t, [POINTER(Dims), c_int32, c_int32]),
+        "dflash_target_forward": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, c_int32, c_int32,
+                                            P, c_int32, P, P, P, c_size_t, P]),
+        "dflash_kv_commit": (c_int32, [POINTER(Dims), POINTER(KV), P, c_int32, c_int32, P]),
         "dflash_draft_sample": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, c_int32,
                                           c_float, P, P, P, P, c_size_t, P]),
         "dflash_verify_sample": (c_int32, [POINTER(Dims), P, P, P, P, c_int32, c_float, P, P, P, P, P,

@@ -95,6 +95,12 @@ LARGER_DRAFT = Dims(hidden=5120, n_q_heads=40, n_kv_heads=8, head_dim=128,
                     n_layers=8, intermediate=17408, vocab=151936,
                     n_feat_layers=5, dtype="bf16")
 
+# The target of the Qwen3-8B-shaped drafter: the drafter's layer type at
+# Qwen3-8B's sizes (36 layers); its five feature layers feed the fc.
+QWEN3_8B_TARGET = Dims(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                       n_layers=36, intermediate=12288, vocab=151936,
+                       n_feat_layers=5, dtype="bf16")
+
 TINY_DRAFT = Dims(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                   n_layers=1, intermediate=512, vocab=1024, n_feat_layers=2,
                   dtype="f32")

@@ -31,6 +31,7 @@ size_t packed_bytes(int dtype, long long rows, long long cols) {
 }
 
 constexpr int MAX_BATCH = 64;
+constexpr int MAX_TARGET_LAYERS = 128;
 
 // Launches of more rows than these use the tiled kernel: from two row tiles
 // on, the skinny kernel's activation stream per item (every row tile and
@@ -116,16 +117,23 @@ struct DraftLayout {
   size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, anc, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
   int M, Mp, S, xs, act_xs;  // planes of the packed activations and of the SwiGLU output
+  int rows, q_tiles;         // rows per sequence; 16-row query tiles per sequence
   bool rs_inline;  // consumers reduce the RMSNorm tile sums themselves (one row block)
   GemmPlan qkv, o, gu, down, lm;
 };
 
-DraftLayout draft_layout(const dflash_dims *d, int batch) {
+// Workspace of a layer stack over `batch` sequences of `rows` rows: the
+// drafting pass (rows = B; every layer's residuals and attention output are
+// kept for the views) or the target's causal pass (target: rows up to 32,
+// two residual buffers used in turn and one attention output).
+DraftLayout draft_layout(const dflash_dims *d, int batch, int rows = 0, bool target = false) {
   DraftLayout L{};
   const int es = esize_of(d->dtype), kt = kt_of(d->dtype);
   const int H = d->hidden, NQD = d->n_q_heads * d->head_dim, I = d->intermediate, hd = d->head_dim;
-  L.M = batch * d->block_size;
-  L.S = attn_splits(d, batch);
+  L.rows = rows > 0 ? rows : d->block_size;
+  L.q_tiles = (L.rows + 15) / 16;
+  L.M = batch * L.rows;
+  L.S = attn_splits(d, batch * L.q_tiles);
   L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1, STEP_TILED_MIN_ROWS);
   L.o = plan_gemm(d->dtype, L.M, H, NQD, 1, STEP_TILED_MIN_ROWS);
   L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2, STEP_TILED_MIN_ROWS);
@@ -135,16 +143,16 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.Mp = L.qkv.m_blocks * L.qkv.MT * 16;
   Bump b;
   const size_t row = size_t(L.M) * H * 4;
-  L.hidden = b.take(row * (d->n_layers + 1));
-  L.mid = b.take(row * d->n_layers);
-  L.attn = b.take(size_t(L.M) * NQD * 4 * d->n_layers);
+  L.hidden = b.take(row * (target ? 2 : d->n_layers + 1));
+  L.mid = b.take(row * (target ? 1 : d->n_layers));
+  L.attn = b.take(size_t(L.M) * NQD * 4 * (target ? 1 : d->n_layers));
   L.ssq = b.take(size_t(L.M) * (H / 16) * 4);
   L.rs = b.take(size_t(L.M) * 4);
   L.xs = act_planes(d);
   L.pa = packed_bytes(d->dtype, L.Mp, H);
   L.po = packed_bytes(d->dtype, L.Mp, NQD);
   L.pact = packed_bytes(d->dtype, L.Mp, I);
-  L.pq = size_t(batch) * d->n_q_heads * (hd / kt) * 1024;
+  L.pq = size_t(batch) * d->n_q_heads * L.q_tiles * (hd / kt) * 1024;
   L.xa = b.take(L.pa * L.xs);
   L.xo = b.take(L.po * L.xs);
   L.act_xs = mlp_act_planes(d, L.M);
@@ -152,7 +160,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch) {
   L.qbuf = b.take(L.pq * L.xs);
   L.kblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
   L.vblk = b.take(size_t(batch) * d->n_kv_heads * kt * hd * es);
-  L.apart = b.take(size_t(batch) * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
+  L.apart = b.take(size_t(batch) * L.q_tiles * d->n_q_heads * L.S * ((hd / 16) * 1024 + 128));
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
   L.part = L.M > STEP_TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.anc = b.take(size_t(2) * MAX_BATCH * 4);   // anchored blocks: checked context lengths, cache regions
@@ -207,7 +215,7 @@ InjectLayout inject_layout(const dflash_dims *d, int rows) {
   return L;
 }
 
-int check_dims(const dflash_dims *d) {
+int check_dims(const dflash_dims *d, int max_layers = MAX_SEGMENTS) {
   if (!d) return fail(DFLASH_ERR_NULL, "dims is NULL");
   if (d->dtype != DFLASH_BF16 && d->dtype != DFLASH_F32) return fail(DFLASH_ERR_DTYPE, "dtype must be DFLASH_BF16 or DFLASH_F32");
   // Malformed dimensions: DFLASH_ERR_SHAPE.
@@ -225,7 +233,8 @@ int check_dims(const dflash_dims *d) {
   if (d->hidden % 64 || d->hidden > 8192) return fail(DFLASH_ERR_UNSUPPORTED, "hidden must be a multiple of 64, at most 8192");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (d->n_q_heads / d->n_kv_heads > 16) return fail(DFLASH_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
-  if (d->n_layers > MAX_SEGMENTS) return fail(DFLASH_ERR_UNSUPPORTED, "at most 16 layers");
+  if (d->n_layers > max_layers)
+    return fail(DFLASH_ERR_UNSUPPORTED, max_layers == MAX_SEGMENTS ? "at most 16 layers" : "at most 128 target layers");
   return DFLASH_OK;
 }
 
@@ -371,6 +380,150 @@ void fill_gemm(GemmParams &p, const GemmPlan &g) {
   if (g.tiled) p.tiled = 1;
 }
 
+// One decoder layer of the drafting pass or of the target's causal pass:
+// QKV with RoPE, the attention (and its split merge), o_proj with the
+// residual, gate/up with SwiGLU and down with the residual.  RMSNorms are
+// split between producer and consumer launches; the down projection produces
+// the next layer's input norm (next_gain).
+struct LayerRun {
+  const dflash_dims *d;
+  const DraftLayout *L;
+  char *wsb;
+  int batch;
+  const int *ctx_of;            // per sequence: cached positions attended (rotary base)
+  const int *region_of;         // per sequence: its cache region (null: its own)
+  const char *kcache, *vcache;  // the whole cache; layer l at l * region_layer
+  size_t region_layer;
+  int capacity, max_batch;
+  bool causal;                  // target pass: causal block, new K/V appended to the cache
+  unsigned *status;
+  const char *what;
+};
+
+int run_layer(const LayerRun &r, const dflash_layer &lw, int l, const void *next_gain, float *h_in, float *h_mid,
+              float *h_out, float *attn_out, char *aux_out, int aux_ld, hipStream_t stream) {
+  const dflash_dims *d = r.d;
+  const DraftLayout &L = *r.L;
+  char *wsb = r.wsb;
+  const int H = d->hidden, kt = kt_of(d->dtype), hd = d->head_dim;
+  const int NQD = d->n_q_heads * hd, I = d->intermediate;
+  float *ssq = reinterpret_cast<float *>(wsb + L.ssq);
+  float *rs = reinterpret_cast<float *>(wsb + L.rs);
+  const std::string what(r.what);
+  hipError_t e;
+
+  GemmParams q{};
+  fill_gemm(q, L.qkv);
+  set_split(q, wsb, L.part);
+  q.w_seg[0] = static_cast<const char *>(lw.w_qkv);
+  q.x = wsb + L.xa;
+  q.xs = L.xs;
+  q.x_plane = L.pa;
+  q.q_plane = L.pq;
+  q.q_planes = L.xs;   // q itself goes to the attention as hi + lo
+  q.q_tiles = L.q_tiles;
+  q.block = L.rows;
+  q.n_q = d->n_q_heads;
+  q.n_kv = d->n_kv_heads;
+  q.head_dim = hd;
+  fill_rope(q, d);
+  q.ctx_len = r.ctx_of;
+  q.qbuf = wsb + L.qbuf;
+  q.kblk = wsb + L.kblk;
+  q.vblk = wsb + L.vblk;
+  if (r.causal) {
+    q.qkv_to_cache = 1;
+    q.kcache = const_cast<char *>(r.kcache);
+    q.vcache = const_cast<char *>(r.vcache);
+    q.layer0 = l;
+    q.capacity = r.capacity;
+    q.max_batch = r.max_batch;
+    q.status = r.status;
+  }
+  e = set_norm_in(q, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
+  if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_QKV, q, stream);
+  if (e != hipSuccess) return hip_fail(e, (what + " qkv").c_str());
+
+  AttnParams a{};
+  a.qbuf = wsb + L.qbuf;
+  a.q_plane = L.pq;
+  a.xs = L.xs;
+  a.xo_plane = L.po;
+  a.kblk = wsb + L.kblk;
+  a.vblk = wsb + L.vblk;
+  a.kcache = r.kcache + r.region_layer * l;
+  a.vcache = r.vcache + r.region_layer * l;
+  a.ctx_len = r.ctx_of;
+  a.region_of = r.region_of;
+  a.part = reinterpret_cast<float *>(wsb + L.apart);
+  a.block = L.rows;
+  a.q_tiles = L.q_tiles;
+  a.causal = r.causal ? 1 : 0;
+  a.n_q = d->n_q_heads;
+  a.n_kv = d->n_kv_heads;
+  a.head_dim = hd;
+  a.group = d->n_q_heads / d->n_kv_heads;
+  a.splits = L.S;
+  a.head_split = attn_head_split(d, r.batch * L.q_tiles, L.S);
+  a.capacity = r.capacity;
+  a.scale_log2 = 1.4426950408889634f / sqrtf(float(hd));
+  a.attn_out = attn_out;
+  a.xo = wsb + L.xo;
+  a.xo_kt = NQD / kt;
+  e = launch_attention(d->dtype, a, r.batch, stream);
+  if (e != hipSuccess) return hip_fail(e, (what + " attention").c_str());
+  if (a.splits > 1) {
+    e = launch_attn_merge(d->dtype, a, r.batch, stream);
+    if (e != hipSuccess) return hip_fail(e, (what + " attention merge").c_str());
+  }
+
+  GemmParams o{};
+  fill_gemm(o, L.o);
+  set_split(o, wsb, L.part);
+  o.w_seg[0] = static_cast<const char *>(lw.w_o);
+  o.x = wsb + L.xo;
+  o.xs = L.xs;
+  o.x_plane = L.po;
+  o.out_f32 = h_mid;
+  o.resid = h_in;
+  o.ld_out = H;
+  set_norm_out(o, wsb + L.xa, H / kt, L.xs, L.pa, L.Mp, lw.mlp_norm, ssq);
+  e = launch_gemm(d->dtype, EPI_RESID, o, stream);
+  if (e != hipSuccess) return hip_fail(e, (what + " o_proj").c_str());
+
+  GemmParams gu{};
+  fill_gemm(gu, L.gu);
+  set_split(gu, wsb, L.part);
+  gu.w_seg[0] = static_cast<const char *>(lw.w_gate_up);
+  gu.x = wsb + L.xa;
+  gu.xs = L.xs;
+  gu.x_plane = L.pa;
+  gu.out_planes = L.act_xs;
+  gu.out_plane = L.pact;
+  gu.out_packed = wsb + L.xact;
+  gu.out_kt = I / kt;
+  e = set_norm_in(gu, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
+  if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_SWIGLU, gu, stream);
+  if (e != hipSuccess) return hip_fail(e, (what + " gate_up").c_str());
+
+  GemmParams dn{};
+  fill_gemm(dn, L.down);
+  set_split(dn, wsb, L.part);
+  dn.w_seg[0] = static_cast<const char *>(lw.w_down);
+  dn.x = wsb + L.xact;
+  dn.xs = L.act_xs;
+  dn.x_plane = L.pact;
+  dn.out_f32 = h_out;
+  dn.resid = h_mid;
+  dn.ld_out = H;
+  dn.aux_out = aux_out;
+  dn.aux_ld = aux_ld;
+  set_norm_out(dn, wsb + L.xa, H / kt, L.xs, L.pa, L.Mp, next_gain, ssq);
+  e = launch_gemm(d->dtype, EPI_RESID, dn, stream);
+  if (e != hipSuccess) return hip_fail(e, (what + " down").c_str());
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 namespace dflash {
@@ -464,7 +617,7 @@ int dflash_pack_lm_head(int32_t dtype, const void *src, int32_t vocab, int32_t h
 }
 
 int dflash_pack_qkv(const dflash_dims *d, const void *wq, const void *wk, const void *wv, void *dst, hipStream_t stream) {
-  TRY(check_dims(d));
+  TRY(check_dims(d, MAX_TARGET_LAYERS));
   TRY(check_ptr(wq, "wq"));
   TRY(check_ptr(wk, "wk"));
   TRY(check_ptr(wv, "wv"));
@@ -478,7 +631,7 @@ int dflash_pack_qkv(const dflash_dims *d, const void *wq, const void *wk, const 
 }
 
 int dflash_pack_gate_up(const dflash_dims *d, const void *wg, const void *wu, void *dst, hipStream_t stream) {
-  TRY(check_dims(d));
+  TRY(check_dims(d, MAX_TARGET_LAYERS));
   TRY(check_ptr(wg, "w_gate"));
   TRY(check_ptr(wu, "w_up"));
   TRY(check_ptr(dst, "dst"));
@@ -489,12 +642,12 @@ int dflash_pack_gate_up(const dflash_dims *d, const void *wg, const void *wu, vo
 }
 
 size_t dflash_kv_bytes(const dflash_dims *d, int32_t capacity, int32_t max_batch) {
-  if (check_dims(d) != DFLASH_OK || capacity <= 0 || max_batch <= 0) return 0;
+  if (check_dims(d, MAX_TARGET_LAYERS) != DFLASH_OK || capacity <= 0 || max_batch <= 0) return 0;
   return size_t(d->n_layers) * max_batch * d->n_kv_heads * size_t(capacity) * d->head_dim * esize_of(d->dtype);
 }
 
 static int kv_convert(const dflash_dims *d, const dflash_kv *kv, void *kp, void *vp, bool to_packed, hipStream_t s) {
-  TRY(check_dims(d));
+  TRY(check_dims(d, MAX_TARGET_LAYERS));
   TRY(check_kv(d, kv));
   TRY(check_ptr(kp, "k_plain"));
   TRY(check_ptr(vp, "v_plain"));
@@ -696,108 +849,27 @@ static int draft_impl(const dflash_dims *d, const dflash_weights *w, const dflas
   e = launch_embed(d->dtype, ep, stream);
   if (e != hipSuccess) return hip_fail(e, "draft embed");
 
+  LayerRun run{};
+  run.d = d;
+  run.L = &L;
+  run.wsb = wsb;
+  run.batch = batch;
+  run.ctx_of = ctx_of;
+  run.region_of = anchor_pos ? blk_region : nullptr;
+  run.kcache = static_cast<const char *>(kv->k);
+  run.vcache = static_cast<const char *>(kv->v);
+  run.region_layer = region_layer;
+  run.capacity = kv->capacity;
+  run.max_batch = kv->max_batch;
+  run.status = kv->status;
+  run.what = "draft";
   for (int l = 0; l < NL; ++l) {
-    const dflash_layer &lw = w->layers[l];
     float *h_in = reinterpret_cast<float *>(reinterpret_cast<char *>(hidden) + row * l);
     float *h_mid = reinterpret_cast<float *>(reinterpret_cast<char *>(mid) + row * l);
     float *h_out = reinterpret_cast<float *>(reinterpret_cast<char *>(hidden) + row * (l + 1));
-
-    GemmParams q{};
-    fill_gemm(q, L.qkv);
-    set_split(q, wsb, L.part);
-    q.w_seg[0] = static_cast<const char *>(lw.w_qkv);
-    q.x = wsb + L.xa;
-    q.xs = L.xs;
-    q.x_plane = L.pa;
-    q.q_plane = L.pq;
-    q.q_planes = L.xs;   // q itself goes to the attention as hi + lo
-    q.block = d->block_size;
-    q.n_q = d->n_q_heads;
-    q.n_kv = d->n_kv_heads;
-    q.head_dim = hd;
-    fill_rope(q, d);
-    q.ctx_len = ctx_of;
-    q.qbuf = wsb + L.qbuf;
-    q.kblk = wsb + L.kblk;
-    q.vblk = wsb + L.vblk;
-    e = set_norm_in(q, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
-    if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_QKV, q, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft qkv");
-
-    AttnParams a{};
-    a.qbuf = wsb + L.qbuf;
-    a.q_plane = L.pq;
-    a.xs = L.xs;
-    a.xo_plane = L.po;
-    a.kblk = wsb + L.kblk;
-    a.vblk = wsb + L.vblk;
-    a.kcache = static_cast<const char *>(kv->k) + region_layer * l;
-    a.vcache = static_cast<const char *>(kv->v) + region_layer * l;
-    a.ctx_len = ctx_of;
-    a.region_of = anchor_pos ? blk_region : nullptr;
-    a.part = reinterpret_cast<float *>(wsb + L.apart);
-    a.block = d->block_size;
-    a.n_q = d->n_q_heads;
-    a.n_kv = d->n_kv_heads;
-    a.head_dim = hd;
-    a.group = d->n_q_heads / d->n_kv_heads;
-    a.splits = L.S;
-    a.head_split = attn_head_split(d, batch, L.S);
-    a.capacity = kv->capacity;
-    a.scale_log2 = 1.4426950408889634f / sqrtf(float(hd));
-    a.attn_out = reinterpret_cast<float *>(wsb + L.attn + size_t(L.M) * NQD * 4 * l);
-    a.xo = wsb + L.xo;
-    a.xo_kt = NQD / kt;
-    e = launch_attention(d->dtype, a, batch, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft attention");
-    if (a.splits > 1) {
-      e = launch_attn_merge(d->dtype, a, batch, stream);
-      if (e != hipSuccess) return hip_fail(e, "draft attention merge");
-    }
-
-    GemmParams o{};
-    fill_gemm(o, L.o);
-    set_split(o, wsb, L.part);
-    o.w_seg[0] = static_cast<const char *>(lw.w_o);
-    o.x = wsb + L.xo;
-    o.xs = L.xs;
-    o.x_plane = L.po;
-    o.out_f32 = h_mid;
-    o.resid = h_in;
-    o.ld_out = H;
-    set_norm_out(o, wsb + L.xa, H / kt, L.xs, L.pa, L.Mp, lw.mlp_norm, ssq);
-    e = launch_gemm(d->dtype, EPI_RESID, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft o_proj");
-
-    GemmParams gu{};
-    fill_gemm(gu, L.gu);
-    set_split(gu, wsb, L.part);
-    gu.w_seg[0] = static_cast<const char *>(lw.w_gate_up);
-    gu.x = wsb + L.xa;
-    gu.xs = L.xs;
-    gu.x_plane = L.pa;
-    gu.out_planes = L.act_xs;
-    gu.out_plane = L.pact;
-    gu.out_packed = wsb + L.xact;
-    gu.out_kt = I / kt;
-    e = set_norm_in(gu, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
-    if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_SWIGLU, gu, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft gate_up");
-
-    GemmParams dn{};
-    fill_gemm(dn, L.down);
-    set_split(dn, wsb, L.part);
-    dn.w_seg[0] = static_cast<const char *>(lw.w_down);
-    dn.x = wsb + L.xact;
-    dn.xs = L.act_xs;
-    dn.x_plane = L.pact;
-    dn.out_f32 = h_out;
-    dn.resid = h_mid;
-    dn.ld_out = H;
-    set_norm_out(dn, wsb + L.xa, H / kt, L.xs, L.pa, L.Mp, l + 1 < NL ? w->layers[l + 1].attn_norm : w->final_norm,
-                 ssq);
-    e = launch_gemm(d->dtype, EPI_RESID, dn, stream);
-    if (e != hipSuccess) return hip_fail(e, "draft down");
+    float *attn_out = reinterpret_cast<float *>(wsb + L.attn + size_t(L.M) * NQD * 4 * l);
+    const void *next_gain = l + 1 < NL ? w->layers[l + 1].attn_norm : w->final_norm;
+    TRY(run_layer(run, w->layers[l], l, next_gain, h_in, h_mid, h_out, attn_out, nullptr, 0, stream));
   }
 
   GemmParams lm{};
@@ -849,6 +921,116 @@ int dflash_draft_anchors(const dflash_dims *d, const dflash_weights *w, const df
                          void *ws, size_t ws_bytes, hipStream_t stream) {
   TRY(check_ptr(anchor_pos, "anchor_pos", false));
   return draft_impl(d, w, kv, anchor_tok, anchor_seq, anchor_pos, nblocks, draft, ws, ws_bytes, stream);
+}
+
+size_t dflash_target_workspace_bytes(const dflash_dims *td, int32_t max_batch, int32_t rows) {
+  if (check_dims(td, MAX_TARGET_LAYERS) != DFLASH_OK || max_batch < 1 || max_batch > MAX_BATCH || rows < 1 ||
+      rows > 32)
+    return 0;
+  return (draft_layout(td, max_batch, rows, true).end + 255) & ~size_t(255);
+}
+
+int dflash_target_forward(const dflash_dims *td, const dflash_weights *tw, const dflash_kv *tkv,
+                          const int32_t *tokens, int32_t batch, int32_t rows, const int32_t *feat_layers,
+                          int32_t n_feat, void *out_hidden, void *out_feats, void *ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  TRY(check_dims(td, MAX_TARGET_LAYERS));
+  if (!tw) return fail(DFLASH_ERR_NULL, "weights is NULL");
+  if (!tw->layers) return fail(DFLASH_ERR_NULL, "weights->layers is NULL");
+  TRY(check_ptr(tw->embed, "embed"));
+  TRY(check_ptr(tw->final_norm, "final_norm"));
+  for (int l = 0; l < td->n_layers; ++l) {
+    const dflash_layer &L = tw->layers[l];
+    TRY(check_ptr(L.attn_norm, "layers[].attn_norm"));
+    TRY(check_ptr(L.w_qkv, "layers[].w_qkv"));
+    TRY(check_ptr(L.w_o, "layers[].w_o"));
+    TRY(check_ptr(L.mlp_norm, "layers[].mlp_norm"));
+    TRY(check_ptr(L.w_gate_up, "layers[].w_gate_up"));
+    TRY(check_ptr(L.w_down, "layers[].w_down"));
+  }
+  TRY(check_kv(td, tkv));
+  TRY(check_ptr(tokens, "tokens", false));
+  TRY(check_ptr(out_hidden, "out_hidden", false));
+  TRY(check_ptr(ws, "ws"));
+  if (batch < 1 || batch > tkv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  // the block's K/V are one key step of the attention: 32 rows (bf16), 16 (fp32)
+  if (rows < 1 || rows > kt_of(td->dtype))
+    return fail(DFLASH_ERR_SHAPE, "rows must be in [1, 32] (bf16) or [1, 16] (fp32)");
+  if (n_feat < 0 || n_feat > 16) return fail(DFLASH_ERR_SHAPE, "n_feat must be in [0, 16]");
+  if (n_feat > 0) {
+    TRY(check_ptr(feat_layers, "feat_layers", false));
+    TRY(check_ptr(out_feats, "out_feats", false));
+    for (int k = 0; k < n_feat; ++k) {
+      if (feat_layers[k] < 0 || feat_layers[k] >= td->n_layers)
+        return fail(DFLASH_ERR_SHAPE, "feat_layers entries must lie in [0, n_layers)");
+      for (int k2 = 0; k2 < k; ++k2)
+        if (feat_layers[k2] == feat_layers[k]) return fail(DFLASH_ERR_SHAPE, "feat_layers entries must be distinct");
+    }
+  }
+  const DraftLayout L = draft_layout(td, batch, rows, true);
+  if (ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small (dflash_target_workspace_bytes)");
+  char *wsb = static_cast<char *>(ws);
+  const int H = td->hidden, kt = kt_of(td->dtype), es = esize_of(td->dtype);
+  const size_t row = size_t(L.M) * H * 4;
+  float *hbuf[2] = {reinterpret_cast<float *>(wsb + L.hidden), reinterpret_cast<float *>(wsb + L.hidden + row)};
+  float *mid = reinterpret_cast<float *>(wsb + L.mid);
+  float *attn_out = reinterpret_cast<float *>(wsb + L.attn);
+
+  EmbedParams ep{};
+  ep.embed = static_cast<const char *>(tw->embed);
+  ep.tokens = tokens;
+  ep.block = rows;
+  ep.vocab = td->vocab;
+  ep.status = tkv->status;
+  ep.gathered = hbuf[0];
+  ep.gain = static_cast<const char *>(tw->layers[0].attn_norm);
+  ep.M = L.M;
+  ep.rows_pad = L.Mp;
+  ep.H = H;
+  ep.xpacked = wsb + L.xa;
+  ep.x_kt = H / kt;
+  ep.planes = L.xs;
+  ep.x_plane = L.pa;
+  ep.ssq = reinterpret_cast<float *>(wsb + L.ssq);
+  hipError_t e = launch_embed(td->dtype, ep, stream);
+  if (e != hipSuccess) return hip_fail(e, "target embed");
+
+  LayerRun run{};
+  run.d = td;
+  run.L = &L;
+  run.wsb = wsb;
+  run.batch = batch;
+  run.ctx_of = tkv->ctx_len;
+  run.kcache = static_cast<const char *>(tkv->k);
+  run.vcache = static_cast<const char *>(tkv->v);
+  run.region_layer = size_t(tkv->max_batch) * td->n_kv_heads * size_t(tkv->capacity) * td->head_dim * es;
+  run.capacity = tkv->capacity;
+  run.max_batch = tkv->max_batch;
+  run.causal = true;
+  run.status = tkv->status;
+  run.what = "target";
+  const int NL = td->n_layers;
+  for (int l = 0; l < NL; ++l) {
+    char *aux = nullptr;   // feature k: columns [k H, (k + 1) H) of out_feats
+    for (int k = 0; k < n_feat; ++k)
+      if (feat_layers[k] == l) aux = static_cast<char *>(out_feats) + size_t(k) * H * es;
+    const void *next_gain = l + 1 < NL ? tw->layers[l + 1].attn_norm : tw->final_norm;
+    TRY(run_layer(run, tw->layers[l], l, next_gain, hbuf[l & 1], mid, hbuf[(l + 1) & 1], attn_out, aux,
+                  n_feat * H, stream));
+  }
+  e = launch_rownorm(td->dtype, hbuf[NL & 1], L.M, H, tw->final_norm, td->rms_eps, out_hidden, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "target final norm");
+}
+
+int dflash_kv_commit(const dflash_dims *d, const dflash_kv *kv, const int32_t *accept_len, int32_t batch,
+                     int32_t max_commit, hipStream_t stream) {
+  TRY(check_dims(d, MAX_TARGET_LAYERS));
+  TRY(check_kv(d, kv));
+  TRY(check_ptr(accept_len, "accept_len", false));
+  if (batch < 1 || batch > kv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  if (max_commit < 0) return fail(DFLASH_ERR_SHAPE, "max_commit must be >= 0");
+  const hipError_t e = launch_kv_commit(kv->ctx_len, accept_len, batch, max_commit, kv->capacity, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "kv commit");
 }
 
 int dflash_draft_sample(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,

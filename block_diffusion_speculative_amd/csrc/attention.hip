@@ -70,7 +70,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   constexpr int MREC = ATTN_MAX_WAVES * REC / 4;    // uint4 of one record per wavefront
   __shared__ uint4 lds[RING > MREC ? RING : MREC];
 
-  const int z = blockIdx.x, s = blockIdx.z;
+  const int z = blockIdx.x;
+  const int QT = p.q_tiles, s = blockIdx.z / QT, qt = blockIdx.z % QT;   // sequence, query tile
   const int g = blockIdx.y / p.head_split, hs = blockIdx.y % p.head_split;
   const int gw = p.group / p.head_split;            // query heads of this workgroup
   const int waves = blockDim.x >> 6;
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 
   uint4 qf[XS][DT];
   {
-    const char *qb = p.qbuf + (size_t(s) * p.n_q + h) * DT * 1024;
-    const bool ok = (lane & 15) < p.block;
+    const char *qb = p.qbuf + ((size_t(s) * p.n_q + h) * QT + qt) * DT * 1024;
+    const bool ok = qt * 16 + (lane & 15) < p.block;
 #pragma unroll
     for (int xp = 0; xp < XS; ++xp)
 #pragma unroll
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 #pragma unroll
   for (int i = 0; i < DV; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int gq = lane >> 4;
+  const int qrow = qt * 16 + (lane & 15);   // this lane's query row in the block
 
   auto compute = [&](int st, const uint4 *kl) {
     const bool blk = st == n_ctx;
@@ -148,7 +150,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = 16 * t + 4 * gq + i;
-        const float x = pos < nvalid ? sacc[t][i] * p.scale_log2 : -INFINITY;
+        // a causal pass lets block row qrow see block positions <= qrow only
+        const bool seen = pos < nvalid && !(blk && p.causal && pos > qrow);
+        const float x = seen ? sacc[t][i] * p.scale_log2 : -INFINITY;
         sv[4 * t + i] = x;
         mx = fmaxf(mx, x);
       }
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   }
   const bool final_out = p.splits == 1;
   const float inv = 1.0f / L;
-  float *rec = p.part + ((size_t(s) * p.n_q + h) * p.splits + z) * REC;
+  float *rec = p.part + (((size_t(s) * QT + qt) * p.n_q + h) * p.splits + z) * REC;
   for (int dv = ss; dv < DV; dv += SUB) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < SUB; ++j) {
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       acc += exp2f(r[DV * 256 + q] - M) * reinterpret_cast<const f32x4 *>(r)[dv * 64 + lane];
     }
     if (final_out) {
-      if (q < p.block) {
-        const int row = s * p.block + q;
+      if (qt * 16 + q < p.block) {
+        const int row = s * p.block + qt * 16 + q;
         const int nqd = p.n_q * HD;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -254,9 +258,10 @@ template <typename T, int HD, int ZMAX>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
   constexpr int DV = HD / 16;
   constexpr int REC = DV * 256 + 32;
-  const int dv = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int dv = blockIdx.x, h = blockIdx.y;
+  const int QT = p.q_tiles, s = blockIdx.z / QT, qt = blockIdx.z % QT;
   const int lane = threadIdx.x, q = lane & 15;
-  const float *base = p.part + (size_t(s) * p.n_q + h) * p.splits * REC;
+  const float *base = p.part + ((size_t(s) * QT + qt) * p.n_q + h) * p.splits * REC;
   float mz[ZMAX], lz[ZMAX];
   f32x4 oz[ZMAX];
 #pragma unroll
@@ -280,9 +285,9 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
       acc += w * oz[z];
     }
   }
-  if (q >= p.block) return;
+  if (qt * 16 + q >= p.block) return;
   const float inv = 1.0f / L;
-  const int row = s * p.block + q;
+  const int row = s * p.block + qt * 16 + q;
   const int nqd = p.n_q * HD;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
 
 template <typename T, int HD, int XS, int NW>
 static hipError_t launch_attn_nw(const AttnParams &p, int batch, int rc, int threads, hipStream_t s) {
-  const dim3 grid(p.splits, p.n_kv * p.head_split, batch), block(threads);
+  const dim3 grid(p.splits, p.n_kv * p.head_split, batch * p.q_tiles), block(threads);
   if (rc <= 2) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 2, NW>), grid, block, 0, s, p);
   else if (rc <= 4) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 4, NW>), grid, block, 0, s, p);
   else if (rc <= 8) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 8, NW>), grid, block, 0, s, p);
@@ -319,6 +324,7 @@ template <typename T, int XS>
 static hipError_t launch_attn_xs(const AttnParams &p, int batch, hipStream_t s) {
   if (p.group < 1 || p.group > ATTN_MAX_WAVES || p.splits < 1 || p.splits > ATTN_MAX_SPLITS) return hipErrorInvalidValue;
   if (p.head_split < 1 || p.group % p.head_split) return hipErrorInvalidValue;
+  if (p.q_tiles < 1 || p.block > 16 * p.q_tiles || p.block > Ty<T>::KT) return hipErrorInvalidValue;
   if (p.head_dim == 128) return launch_attn_rc<T, 128, XS>(p, batch, s);
   if (p.head_dim == 64) return launch_attn_rc<T, 64, XS>(p, batch, s);
   return hipErrorInvalidValue;
@@ -334,7 +340,8 @@ static hipError_t launch_attn_t(const AttnParams &p, int batch, hipStream_t s) {
 
 template <typename T>
 static hipError_t launch_merge_t(const AttnParams &p, int batch, hipStream_t s) {
-  const dim3 grid(p.head_dim / 16, p.n_q, batch), block(64);
+  const dim3 grid(p.head_dim / 16, p.n_q, batch * p.q_tiles), block(64);
+  if (p.q_tiles < 1) return hipErrorInvalidValue;
   if (p.splits > ATTN_MAX_SPLITS) return hipErrorInvalidValue;
   if (p.head_dim == 128) {
     if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 128, 16>), grid, block, 0, s, p);

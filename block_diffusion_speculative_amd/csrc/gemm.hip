@@ -71,6 +71,7 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
         const size_t o = size_t(m) * p.ld_out + n;
         if constexpr (EPI == EPI_RESID) v += p.resid[o];
         p.out_f32[o] = v;
+        if (p.aux_out) store_elem<T>(p.aux_out + (size_t(m) * p.aux_ld + n) * ES, v);
       }
       if (p.nx_packed && n < p.N && m < p.nx_rows) {
         const float y = ok ? v * to_f32<T>(reinterpret_cast<const T *>(p.nx_gain)[n]) : 0.f;
@@ -111,18 +112,20 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
         v = rope_apply(v, val(ml, nl ^ 8), dd, d, pos, p);
         if (n < nqd) {
           const int h = n / d;
-          char *base = p.qbuf + (size_t(s) * p.n_q + h) * dt_count * 1024;
+          char *base = p.qbuf + (size_t(s) * p.n_q + h) * p.q_tiles * dt_count * 1024;
           store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.q_planes, v);
         } else {
           const int g = (n - nqd) / d;
           char *base = p.kblk + (size_t(s) * p.n_kv + g) * size_t(KT) * d * ES;
           store_elem<T>(base + kcache_offset<T>(j, dd, d), v);
+          if (p.qkv_to_cache) qkv_cache_store<T>(p, true, s, g, pos, dd, v);
         }
       } else {
         const int c = n - nqd - nkd;
         const int g = c / d, dd = c % d;
         char *base = p.vblk + (size_t(s) * p.n_kv + g) * size_t(KT) * d * ES;
         store_elem<T>(base + vcache_offset<T>(j, dd, d), v);
+        if (p.qkv_to_cache) qkv_cache_store<T>(p, false, s, g, p.ctx_len[s] + j, dd, v);
       }
     }
   } else if constexpr (EPI == EPI_KVINJ) {

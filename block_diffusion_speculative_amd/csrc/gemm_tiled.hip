@@ -252,6 +252,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
             if (mok && nok) {
               if constexpr (EPI == EPI_RESID) v += *reinterpret_cast<const f32x4 *>(p.resid + o);
               *reinterpret_cast<f32x4 *>(p.out_f32 + o) = v;
+              if (p.aux_out) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store_elem<T>(p.aux_out + (size_t(m) * p.aux_ld + n0 + i) * ES, v[i]);
+              }
             } else {
               v = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -283,16 +287,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
                 const int dd = rot_channel(n % d, d);
                 x = rope_apply(x, partner, dd, d, p.ctx_len[sq] + j, p);
                 if (n < nqd) {
-                  char *base = p.qbuf + (size_t(sq) * p.n_q + n / d) * dt_count * 1024;
+                  char *base = p.qbuf + (size_t(sq) * p.n_q + n / d) * p.q_tiles * dt_count * 1024;
                   store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.q_planes, x);
                 } else {
                   char *base = p.kblk + (size_t(sq) * p.n_kv + (n - nqd) / d) * size_t(KT) * d * ES;
                   store_elem<T>(base + kcache_offset<T>(j, dd, d), x);
+                  if (p.qkv_to_cache) qkv_cache_store<T>(p, true, sq, (n - nqd) / d, p.ctx_len[sq] + j, dd, x);
                 }
               } else {
                 const int cc = n - nqd - nkd;
                 char *base = p.vblk + (size_t(sq) * p.n_kv + cc / d) * size_t(KT) * d * ES;
                 store_elem<T>(base + vcache_offset<T>(j, cc % d, d), x);
+                if (p.qkv_to_cache) qkv_cache_store<T>(p, false, sq, cc / d, p.ctx_len[sq] + j, cc % d, x);
               }
             }
           } else if constexpr (EPI == EPI_KVINJ) {

@@ -26,6 +26,21 @@ template <> __device__ inline void store_elem<bf16_t>(char *p, float v) {
   *reinterpret_cast<uint16_t *>(p) = f32_to_bf16(v);
 }
 
+// A causal pass's new K (is_k) or V element of sequence s, KV head g,
+// channel dd (the packed rotary order for K) at cache position pos of layer
+// layer0; a position past the capacity sets DFLASH_STATUS_CAPACITY instead.
+template <typename T>
+__device__ inline void qkv_cache_store(const GemmParams &p, bool is_k, int s, int g, int pos, int dd, float v) {
+  if (pos >= p.capacity) {
+    if (dd == 0) atomicOr(p.status, DFLASH_STATUS_CAPACITY);
+    return;
+  }
+  const int d = p.head_dim;
+  const size_t region = size_t(p.capacity) * d * Ty<T>::SIZE;
+  char *base = (is_k ? p.kcache : p.vcache) + ((size_t(p.layer0) * p.max_batch + s) * p.n_kv + g) * region;
+  store_elem<T>(base + (is_k ? kcache_offset<T>(pos, dd, d) : vcache_offset<T>(pos, dd, d)), v);
+}
+
 // Orderable 64-bit key: larger value first, then lower index.
 __device__ inline unsigned long long argmax_key(float v, int n) {
   if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal

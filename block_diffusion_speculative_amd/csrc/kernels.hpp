@@ -83,6 +83,10 @@ struct GemmParams {
   char *qbuf, *kblk, *vblk;
   size_t q_plane;
   int q_planes;               // planes of q written for the attention (1, or 2 = hi + lo)
+  int q_tiles;                // 16-row tiles of q per (sequence, head): 1 for a draft block, 2 for up to 32 rows
+  // EPI_QKV of a causal pass: the new rows' K/V also go to the cache
+  // (kcache / vcache, layer layer0) at position ctx_len[s] + j.
+  int qkv_to_cache;
   char *kcache, *vcache;
   int layer0, capacity, max_batch;
   const int *cu_new;
@@ -103,6 +107,10 @@ struct GemmParams {
   size_t nx_plane;
   float *ssq_out;
   int ssq_ld;
+  // EPI_STORE / EPI_RESID: a copy of the output rows in the storage type,
+  // aux_out[m * aux_ld + n] (the target's captured features).
+  char *aux_out;
+  int aux_ld;
   const float *rs_ssq;
   const float *rs_direct;
   int rs_tiles, rs_K;
@@ -152,6 +160,8 @@ struct AttnParams {
   float *part;                      // [batch][n_q][splits] partial records
   int block, n_q, n_kv, head_dim, group, splits, capacity;
   int head_split;                   // workgroups sharing one KV head's query group
+  int q_tiles;                      // 16-row query tiles per sequence (block rows up to 16 * q_tiles)
+  int causal;                       // block row i sees block positions <= i only
   float scale_log2;                 // log2(e) / sqrt(head_dim)
   // merge
   float *attn_out;                  // fp32 [batch*block, n_q*d]
@@ -165,6 +175,7 @@ struct AttnParams {
 struct EmbedParams {
   const char *embed;       // T [V, H]
   const int *last_tok;     // [batch]
+  const int *tokens;       // [batch * block]: every row's token (a target pass); null: last_tok + mask
   int block, mask_id, vocab;
   unsigned *status;
   float *gathered;         // fp32 [M, H]
@@ -233,5 +244,11 @@ hipError_t launch_kv_convert(int dtype, bool to_packed, void *packed_k, void *pa
                              void *plain_k, void *plain_v, long long regions, int capacity,
                              int head_dim, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gain, rows of H, in the storage type.
+hipError_t launch_rownorm(int dtype, const float *x, int M, int H, const void *gain, float eps, void *out,
+                          hipStream_t s);
+// ctx_len[s] += min(max(accept_len[s] + 1, 0), max_commit), at most capacity.
+hipError_t launch_kv_commit(int *ctx_len, const int *accept_len, int batch, int max_commit, int capacity,
+                            hipStream_t s);
 
 }  // namespace dflash

@@ -2,6 +2,7 @@
 // embedding gather), weight packing, KV-cache layout conversion, fills.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "gemm_util.hpp"
 
 namespace dflash {
 
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const EmbedParams p) {
     p.blk_region[s] = seq;
     p.blk_ctx[s] = pos;
   }
-  int tok = j == 0 ? p.last_tok[s] : p.mask_id;
+  int tok = p.tokens ? p.tokens[m] : (j == 0 ? p.last_tok[s] : p.mask_id);
   if (tok < 0 || tok >= p.vocab) {
     if (threadIdx.x == 0) atomicOr(p.status, DFLASH_STATUS_TOKEN);
     tok = tok < 0 ? 0 : p.vocab - 1;
@@ -207,6 +208,52 @@ hipError_t launch_kv_convert(int dtype, bool to_packed, void *pk, void *pv, void
   else
     hipLaunchKernelGGL(kv_convert_kernel<float>, dim3(grid_for(work)), dim3(256), 0, s, to_packed,
                        (char *)pk, (char *)pv, (char *)k, (char *)v, regions, capacity, hd);
+  return hipGetLastError();
+}
+
+// One workgroup per row: out = x / sqrt(mean(x^2) + eps) * gain in the
+// storage type (the target's final normalised hidden state, the verify
+// head's input); the sum of squares runs per thread in order and then over a
+// fixed tree.
+template <typename T>
+__global__ __launch_bounds__(256) void rownorm_kernel(const float *x, int H, const T *gain, float eps, char *out) {
+  __shared__ float red[256];
+  const float *r = x + size_t(blockIdx.x) * H;
+  float s = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) s += __fmul_rn(r[c], r[c]);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float inv = 1.0f / sqrtf(red[0] / float(H) + eps);
+  for (int c = threadIdx.x; c < H; c += 256)
+    store_elem<T>(out + (size_t(blockIdx.x) * H + c) * Ty<T>::SIZE, r[c] * inv * to_f32<T>(gain[c]));
+}
+
+__global__ void kv_commit_kernel(int *ctx_len, const int *accept_len, int batch, int max_commit, int capacity) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= batch) return;
+  const int add = min(max(accept_len[s] + 1, 0), max_commit);
+  ctx_len[s] = min(ctx_len[s] + add, capacity);
+}
+
+hipError_t launch_rownorm(int dtype, const float *x, int M, int H, const void *gain, float eps, void *out,
+                          hipStream_t s) {
+  if (dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(rownorm_kernel<bf16_t>, dim3(M), dim3(256), 0, s, x, H,
+                       static_cast<const bf16_t *>(gain), eps, static_cast<char *>(out));
+  else
+    hipLaunchKernelGGL(rownorm_kernel<float>, dim3(M), dim3(256), 0, s, x, H, static_cast<const float *>(gain),
+                       eps, static_cast<char *>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_commit(int *ctx_len, const int *accept_len, int batch, int max_commit, int capacity,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(kv_commit_kernel, dim3((batch + 63) / 64), dim3(64), 0, s, ctx_len, accept_len, batch,
+                     max_commit, capacity);
   return hipGetLastError();
 }
 

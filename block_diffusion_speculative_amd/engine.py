@@ -37,8 +37,11 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def upload(arr: np.ndarray, dtype: torch.dtype, device, chunk_rows: int = 1 << 14) -> torch.Tensor:
-    """Host float32 (storage-representable values) -> device tensor of dtype."""
+def upload(arr, dtype: torch.dtype, device, chunk_rows: int = 1 << 14) -> torch.Tensor:
+    """Host float32 (storage-representable values) -> device tensor of dtype
+    (a tensor already on the device is converted in place of a copy)."""
+    if isinstance(arr, torch.Tensor):
+        return arr.to(device=device, dtype=dtype).contiguous()
     arr = np.ascontiguousarray(arr)
     out = torch.empty(arr.shape, dtype=dtype, device=device)
     if arr.ndim == 1:
@@ -47,6 +50,101 @@ def upload(arr: np.ndarray, dtype: torch.dtype, device, chunk_rows: int = 1 << 1
     for r0 in range(0, arr.shape[0], chunk_rows):
         out[r0:r0 + chunk_rows].copy_(torch.from_numpy(arr[r0:r0 + chunk_rows]))
     return out
+
+
+def pack_layers(lib, cd, dims: Dims, layers, dt, device, sp):
+    """Pack a stack of decoder layers (q/k/v, o, gate/up, down and the norm
+    gains) on the device; returns the tensors and the ctypes layer array."""
+    dcode = cd.dtype
+    H = dims.hidden
+    out = []
+    for lw in layers:
+        wq = upload(lw["wq"], dt, device)
+        wk = upload(lw["wk"], dt, device)
+        wv = upload(lw["wv"], dt, device)
+        qkv = torch.empty(lib.dflash_packed_bytes(dcode, dims.qkv_rows, H), dtype=torch.uint8, device=device)
+        _lib.call("dflash_pack_qkv", ctypes.byref(cd), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
+                  qkv.data_ptr(), sp)
+        del wq, wk, wv
+        wg = upload(lw["w_gate"], dt, device)
+        wu = upload(lw["w_up"], dt, device)
+        gu = torch.empty(lib.dflash_packed_bytes(dcode, 2 * dims.intermediate, H), dtype=torch.uint8,
+                         device=device)
+        _lib.call("dflash_pack_gate_up", ctypes.byref(cd), wg.data_ptr(), wu.data_ptr(), gu.data_ptr(), sp)
+        del wg, wu
+        packed = {}
+        for name, key in (("w_o", "wo"), ("w_down", "w_down")):
+            src = upload(lw[key], dt, device)
+            dst = torch.empty(lib.dflash_packed_bytes(dcode, *lw[key].shape), dtype=torch.uint8, device=device)
+            _lib.call("dflash_pack_matrix", dcode, src.data_ptr(), lw[key].shape[0], lw[key].shape[1],
+                      dst.data_ptr(), sp)
+            packed[name] = dst
+        out.append({"attn_norm": upload(lw["attn_norm"], dt, device),
+                    "mlp_norm": upload(lw["mlp_norm"], dt, device),
+                    "w_qkv": qkv, "w_gate_up": gu, **packed})
+    arr = (_lib.Layer * len(out))()
+    for i, L in enumerate(out):
+        arr[i] = _lib.Layer(L["attn_norm"].data_ptr(), L["w_qkv"].data_ptr(), L["w_o"].data_ptr(),
+                            L["mlp_norm"].data_ptr(), L["w_gate_up"].data_ptr(), L["w_down"].data_ptr())
+    return out, arr
+
+
+class Target:
+    """The target model's device state for its verify pass: packed layers,
+    embedding and final norm, its own KV cache and a workspace (the lm_head
+    is the drafter's shared one, applied by the verify call)."""
+
+    def __init__(self, dims: Dims, weights, max_batch: int, capacity: int, max_rows: int = 17,
+                 device="cuda:0"):
+        self.lib = _lib.load()
+        self.dims = dims
+        self.cd = cdims(dims)
+        self.dt = torch_dtype(dims)
+        self.device = torch.device(device)
+        self.max_batch, self.capacity, self.max_rows = max_batch, capacity, max_rows
+        sp = _stream_ptr(None)
+        self.embed = upload(weights.embed, self.dt, self.device)
+        self.final_norm = upload(weights.final_norm, self.dt, self.device)
+        self.layers, self._layer_arr = pack_layers(self.lib, self.cd, dims, weights.layers, self.dt,
+                                                   self.device, sp)
+        self.cw = _lib.Weights(None, None, self.embed.data_ptr(), self.final_norm.data_ptr(), None,
+                               ctypes.cast(self._layer_arr, ctypes.POINTER(_lib.Layer)))
+        kvb = self.lib.dflash_kv_bytes(ctypes.byref(self.cd), capacity, max_batch)
+        if kvb == 0:
+            raise ValueError("invalid KV cache shape")
+        self.k_cache = torch.zeros(kvb, dtype=torch.uint8, device=self.device)
+        self.v_cache = torch.zeros(kvb, dtype=torch.uint8, device=self.device)
+        self.ctx_len = torch.zeros(max_batch, dtype=torch.int32, device=self.device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self.ckv = _lib.KV(self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.ctx_len.data_ptr(),
+                           self.status.data_ptr(), capacity, max_batch)
+        self.ws_bytes = self.lib.dflash_target_workspace_bytes(ctypes.byref(self.cd), max_batch, max_rows)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid target workspace request")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        _lib.call("dflash_workspace_init", self.ws.data_ptr(), self.ws_bytes, sp)
+
+    def forward(self, tokens: torch.Tensor, batch: int, rows: int, feat_layers: Sequence[int],
+                out_hidden: torch.Tensor, out_feats: Optional[torch.Tensor], stream=None):
+        fl = (ctypes.c_int32 * max(1, len(feat_layers)))(*feat_layers)
+        _lib.call("dflash_target_forward", ctypes.byref(self.cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
+                  _ptr(tokens), batch, rows, fl, len(feat_layers), _ptr(out_hidden), _ptr(out_feats),
+                  self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
+
+    def commit(self, accept_len: torch.Tensor, batch: int, max_commit: int, stream=None):
+        _lib.call("dflash_kv_commit", ctypes.byref(self.cd), ctypes.byref(self.ckv), _ptr(accept_len), batch,
+                  max_commit, _stream_ptr(stream))
+
+    def kv_import(self, k: torch.Tensor, v: torch.Tensor, stream=None):
+        _lib.call("dflash_kv_import", ctypes.byref(self.cd), ctypes.byref(self.ckv), k.data_ptr(),
+                  v.data_ptr(), _stream_ptr(stream))
+
+    def set_ctx_len(self, lens: Sequence[int]):
+        t = torch.as_tensor(np.asarray(lens, dtype=np.int32))
+        self.ctx_len[:len(t)].copy_(t)
+
+    def read_status(self) -> int:
+        return int(self.status.item())
 
 
 class Drafter:

@@ -151,6 +151,52 @@ def make_weights(dims: Dims, seed: int, gain_std: float = 0.0) -> Weights:
     )
 
 
+@dataclass
+class TargetWeights:
+    """The target's weights for its verify pass (the lm_head is the
+    drafter's shared one)."""
+
+    embed: np.ndarray
+    final_norm: np.ndarray
+    layers: List[Dict[str, np.ndarray]]
+
+
+# Tensor ids of the target's weights: the drafter's ids + TARGET_TID.
+TARGET_TID = 100
+
+
+def make_target_weights(dims: Dims, seed: int, gain_std: float = 0.0) -> TargetWeights:
+    """Target layers of the drafter's layer type, ~N(0, 0.02^2), gains 1,
+    from streams of their own (ids offset by TARGET_TID)."""
+    H, d, I, V = dims.hidden, dims.head_dim, dims.intermediate, dims.vocab
+    dt = dims.dtype
+    T = TARGET_TID
+    layers = []
+    for l in range(dims.n_layers):
+        layers.append({
+            "attn_norm": _gain(seed, (T + TID["attn_norm"], l), H, dt, gain_std),
+            "wq": normal(seed, (T + TID["wq"], l), (dims.n_q_heads * d, H), WEIGHT_STD, dt),
+            "wk": normal(seed, (T + TID["wk"], l), (dims.n_kv_heads * d, H), WEIGHT_STD, dt),
+            "wv": normal(seed, (T + TID["wv"], l), (dims.n_kv_heads * d, H), WEIGHT_STD, dt),
+            "wo": normal(seed, (T + TID["wo"], l), (H, dims.n_q_heads * d), WEIGHT_STD, dt),
+            "mlp_norm": _gain(seed, (T + TID["mlp_norm"], l), H, dt, gain_std),
+            "w_gate": normal(seed, (T + TID["w_gate"], l), (I, H), WEIGHT_STD, dt),
+            "w_up": normal(seed, (T + TID["w_up"], l), (I, H), WEIGHT_STD, dt),
+            "w_down": normal(seed, (T + TID["w_down"], l), (H, I), WEIGHT_STD, dt),
+        })
+    return TargetWeights(
+        embed=normal(seed, (T + TID["embed"],), (V, H), WEIGHT_STD, dt),
+        final_norm=_gain(seed, (T + TID["final_norm"],), H, dt, gain_std),
+        layers=layers,
+    )
+
+
+def target_tokens(dims: Dims, seed: int, step: int, batch: int, rows: int) -> np.ndarray:
+    """Token ids of a target pass, uniform over [0, vocab - 1)."""
+    g = stream(seed, TID["last_tok"] + TARGET_TID, step)
+    return g.integers(0, dims.vocab - 1, size=(batch, rows), dtype=np.int64).astype(np.int32)
+
+
 # ----------------------------------------------------------------- features
 
 def features(dims: Dims, seed: int, step: int, seq: int, rows: int) -> np.ndarray:

@@ -263,6 +263,39 @@ int dflash_draft_anchors(const dflash_dims *dims, const dflash_weights *w, const
                          const int32_t *anchor_seq, const int32_t *anchor_pos, const int32_t *anchor_tok,
                          int32_t nblocks, int32_t *draft, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------- target pass */
+
+/* The target's verify pass ("Term: DFlash speculative decoding", "DFlash:
+ * architecture and workflow", stage three: the target computes its own
+ * logits at every block position; "DFlash, Diffusion LLMs, dLLM, MTP and
+ * Speculative Decoding: A Deep Research Report", "Key points": the drafter
+ * is conditioned on hidden features from several target layers).  The
+ * target is a decoder of the drafter's layer type (weights packed by the
+ * same calls, dims with up to 128 layers) with causal attention: row i of
+ * sequence s holds tokens[s][i] at rotary position ctx_len[s] + i and sees
+ * the cached positions [0, ctx_len[s]) and rows 0 .. i.  The rows' K/V are
+ * written to the cache at ctx_len[s] + i (DFLASH_STATUS_CAPACITY past the
+ * capacity); ctx_len is not changed (dflash_kv_commit keeps the accepted
+ * rows).  Outputs, storage dtype: out_hidden [batch, rows, H], the final
+ * normalised hidden states (dflash_verify_accept's target_hidden), and
+ * out_feats [batch, rows, n_feat * H], the residual stream after layer
+ * feat_layers[k] ([host] array, distinct indices in [0, n_layers)) in
+ * columns [k H, (k + 1) H) (dflash_inject_kv's feature rows).  tokens:
+ * [batch, rows] device int32; 1 <= rows <= 32 (bf16) or 16 (fp32); weights:
+ * embed, final_norm and the layers of `tw` (w_fc, fc_norm, lm_head unused).
+ * The workspace must hold dflash_target_workspace_bytes(dims, batch, rows). */
+size_t dflash_target_workspace_bytes(const dflash_dims *dims, int32_t max_batch, int32_t rows);
+int dflash_target_forward(const dflash_dims *dims, const dflash_weights *tw, const dflash_kv *kv,
+                          const int32_t *tokens, int32_t batch, int32_t rows, const int32_t *feat_layers,
+                          int32_t n_feat, void *out_hidden, void *out_feats, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* After verification: ctx_len[s] += min(max(accept_len[s] + 1, 0),
+ * max_commit), at most kv->capacity (the accepted drafts and the target's
+ * next token stay in the cache; the rest of the pass's rows are dropped). */
+int dflash_kv_commit(const dflash_dims *dims, const dflash_kv *kv, const int32_t *accept_len, int32_t batch,
+                     int32_t max_commit, hipStream_t stream);
+
 /* Temperature sampling ("Term: DFlash speculative decoding", "DFlash:
  * architecture and workflow": the speculator fills masked positions with
  * sampled tokens and the target applies an acceptance criterion; "DFlash,
