@@ -169,7 +169,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch, int rows = 0, bool tar
 }
 
 struct VerifyLayout {
-  size_t lse, end;
+  size_t lse, lse_part, end;
   GemmPlan lm;
 };
 
@@ -180,6 +180,8 @@ VerifyLayout verify_layout(const dflash_dims *d, int batch, bool sampling = fals
   L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, 2, STEP_TILED_MIN_ROWS);
   Bump b;
   L.lse = sampling ? b.take(size_t(batch) * (2 * d->block_size + 1) * 4) : 0;
+  // chunk partials of the log-sum-exp (one float2 per row and chunk)
+  L.lse_part = sampling ? b.take(size_t(batch) * (2 * d->block_size + 1) * ARGMAX_SLOTS * 8) : 0;
   L.end = sampling ? b.off : WS_COUNTER_BYTES;
   return L;
 }
@@ -1078,8 +1080,11 @@ int dflash_verify_sample(const dflash_dims *d, const void *lm_head, const void *
   if (e != hipSuccess) return hip_fail(e, "verify logits");
   const float inv_t = 1.0f / temperature;
   float *lse_q = reinterpret_cast<float *>(wsb + L.lse), *lse_p = lse_q + size_t(batch) * B;
-  e = launch_row_lse(draft_logits, V, V, inv_t, batch * B, lse_q, stream);
-  if (e == hipSuccess) e = launch_row_lse(target_logits, V, V, inv_t, batch * (B + 1), lse_p, stream);
+  float2 *part = reinterpret_cast<float2 *>(wsb + L.lse_part);
+  const int ch = sample_chunks(V);
+  e = launch_row_lse(draft_logits, V, V, inv_t, batch * B, ch, part, lse_q, stream);
+  if (e == hipSuccess)
+    e = launch_row_lse(target_logits, V, V, inv_t, batch * (B + 1), ch, part + size_t(batch) * B * ch, lse_p, stream);
   if (e != hipSuccess) return hip_fail(e, "verify log-sum-exp");
   SampleParams sp{};
   sp.ld = V;

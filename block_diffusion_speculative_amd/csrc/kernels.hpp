@@ -214,7 +214,10 @@ struct SampleParams {
   int *accept_len;                    // [b] out
 };
 hipError_t launch_gumbel_draft(const SampleParams &p, int rows, hipStream_t s);
-hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, int rows, float *lse, hipStream_t s);
+// lse[r] = log sum_v exp(logits[r][v] * inv_t), through chunk partials part
+// [rows][chunks] (scratch).
+hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, int rows, int chunks, float2 *part,
+                          float *lse, hipStream_t s);
 hipError_t launch_spec_sample(const SampleParams &p, int batch, hipStream_t s);
 
 // Greedy verification with its scratch (argmax key slots and the arrival

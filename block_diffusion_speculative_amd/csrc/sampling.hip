@@ -71,32 +71,60 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void gumbel_draft_kernel(const Samp
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// log sum_v exp(l(v) * inv_t) of one row: the maximum, then the sum of
-// exp(l * inv_t - max), each thread over its strided elements in order and
-// the threads combined by a fixed tree, so the result is deterministic.
-__global__ __launch_bounds__(SAMPLE_THREADS) void row_lse_kernel(const float *logits, int ld, int vocab, float inv_t,
-                                                                  float *lse) {
-  __shared__ float red[SAMPLE_THREADS];
-  const float *lg = logits + size_t(blockIdx.x) * ld;
-  float mx = -INFINITY;
-  for (int v = threadIdx.x; v < vocab; v += SAMPLE_THREADS) mx = fmaxf(mx, lg[v] * inv_t);
-  red[threadIdx.x] = mx;
+// log sum_v exp(l(v) * inv_t) of a row, in two launches.  Every chunk of
+// the row keeps a running (max, sum of exp(x - max)) per thread over its
+// strided elements in order (rescaling the sum when the max grows), the
+// threads are merged by a fixed tree, and the chunk's pair goes to part;
+// row_lse_merge_kernel then merges a row's chunk pairs in chunk order.  The
+// result is deterministic.
+__device__ inline void lse_merge(float &m, float &s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;   // both empty
+  s = s * expf(m - mm) + s2 * expf(m2 - mm);
+  m = mm;
+}
+
+__global__ __launch_bounds__(SAMPLE_THREADS) void row_lse_part_kernel(const float *logits, int ld, int vocab,
+                                                                       float inv_t, int chunks, float2 *part) {
+  __shared__ float rm[SAMPLE_THREADS], rsum[SAMPLE_THREADS];
+  const int row = blockIdx.y, chunk = blockIdx.x;
+  const float *lg = logits + size_t(row) * ld;
+  const int per = (vocab + chunks - 1) / chunks;
+  const int v0 = chunk * per, v1 = min(v0 + per, vocab);
+  float m = -INFINITY, sum = 0.f;
+  for (int v = v0 + threadIdx.x; v < v1; v += SAMPLE_THREADS) {
+    const float x = lg[v] * inv_t;
+    if (x > m) {
+      sum = sum * expf(m - x) + 1.0f;
+      m = x;
+    } else {
+      sum += expf(x - m);
+    }
+  }
+  rm[threadIdx.x] = m;
+  rsum[threadIdx.x] = sum;
   __syncthreads();
   for (int w = SAMPLE_THREADS / 2; w >= 1; w >>= 1) {
-    if (int(threadIdx.x) < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    if (int(threadIdx.x) < w) {
+      float a = rm[threadIdx.x], b = rsum[threadIdx.x];
+      lse_merge(a, b, rm[threadIdx.x + w], rsum[threadIdx.x + w]);
+      rm[threadIdx.x] = a;
+      rsum[threadIdx.x] = b;
+    }
     __syncthreads();
   }
-  mx = red[0];
-  __syncthreads();
-  float sum = 0.f;
-  for (int v = threadIdx.x; v < vocab; v += SAMPLE_THREADS) sum += expf(lg[v] * inv_t - mx);
-  red[threadIdx.x] = sum;
-  __syncthreads();
-  for (int w = SAMPLE_THREADS / 2; w >= 1; w >>= 1) {
-    if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
+  if (threadIdx.x == 0) part[size_t(row) * chunks + chunk] = make_float2(rm[0], rsum[0]);
+}
+
+__global__ __launch_bounds__(64) void row_lse_merge_kernel(const float2 *part, int chunks, int rows, float *lse) {
+  const int row = blockIdx.x * 64 + threadIdx.x;
+  if (row >= rows) return;
+  float m = -INFINITY, sum = 0.f;
+  for (int c = 0; c < chunks; ++c) {
+    const float2 pc = part[size_t(row) * chunks + c];
+    lse_merge(m, sum, pc.x, pc.y);
   }
-  if (threadIdx.x == 0) lse[blockIdx.x] = mx + logf(red[0]);
+  lse[row] = m + logf(sum);
 }
 
 // One chunk of one sequence's vocabulary.  Every workgroup of the sequence
@@ -157,8 +185,12 @@ hipError_t launch_gumbel_draft(const SampleParams &p, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, int rows, float *lse, hipStream_t s) {
-  hipLaunchKernelGGL(row_lse_kernel, dim3(rows), dim3(SAMPLE_THREADS), 0, s, logits, ld, vocab, inv_t, lse);
+hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, int rows, int chunks, float2 *part,
+                          float *lse, hipStream_t s) {
+  if (chunks < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_lse_part_kernel, dim3(chunks, rows), dim3(SAMPLE_THREADS), 0, s, logits, ld, vocab, inv_t,
+                     chunks, part);
+  hipLaunchKernelGGL(row_lse_merge_kernel, dim3((rows + 63) / 64), dim3(64), 0, s, part, chunks, rows, lse);
   return hipGetLastError();
 }
 
