@@ -11,6 +11,10 @@ it; see ``tests/test_oracle_*.py``):
 * ``rms_norm``, ``rope``, ``silu``, ``linear``, ``attention``,
   ``argmax_lowest``, ``accept``, ``inject``, ``draft_forward``,
   ``draft_anchors``, ``verify``, ``gumbel``, ``sample_categorical``,
+  ``build_tree``, ``topk_logprobs``, ``tree_mask``, ``masked_attention``,
+  ``tree_accept``, ``commit_path`` (brute-force enumeration of the best
+  continuations, chain trees equal to the causal pass and the chain accept,
+  a tree pass plus its commit equal to a causal pass over the path);
   ``causal_attention``, ``target_forward``, ``commit`` (brute force,
   causality, incremental passes over a committed cache, a closed form);
   ``draft_sample``, ``speculative_verify`` (the last four by closed-form
@@ -27,8 +31,10 @@ from .dflash_oracle import (  # noqa: F401
     accept,
     argmax_lowest,
     attention,
+    build_tree,
     causal_attention,
     commit,
+    commit_path,
     draft_anchors,
     draft_block,
     draft_forward,
@@ -36,6 +42,7 @@ from .dflash_oracle import (  # noqa: F401
     gumbel,
     inject,
     linear,
+    masked_attention,
     rms_norm,
     rope,
     silu,
@@ -44,5 +51,8 @@ from .dflash_oracle import (  # noqa: F401
     speedup,
     target_feature_layers,
     target_forward,
+    topk_logprobs,
+    tree_accept,
+    tree_mask,
     verify,
 )

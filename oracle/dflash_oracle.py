@@ -20,6 +20,10 @@ Sources (page title, then section):
   to the target for the next token.
 * [Term/Math]  same page, "Mathematical view of acceptance and speedup":
   S ~= C_AR / (C_DF / E[L]).
+* [Forum]  "LLMs hit ludicrous speed: diffusion decoding and dMoE supercharge
+  AI inference, shattering old benchmarks", the DDTree paragraph: a draft
+  tree built best-first from per-position distributions and verified in one
+  target pass under an ancestor-only attention mask.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): one drafting pass (T = 1); B drafted tokens, one per block
@@ -422,7 +426,7 @@ def target_feature_layers(n_layers: int, n_feat: int) -> List[int]:
     return [(k + 1) * n_layers // (n_feat + 1) - 1 for k in range(n_feat)]
 
 
-def target_forward(tdims, tweights, cache: OracleCache, tokens, feat_layers) -> Dict[str, np.ndarray]:
+def target_forward(tdims, tweights, cache: OracleCache, tokens, feat_layers, parents=None) -> Dict[str, np.ndarray]:
     """The target's causal pass over n new tokens per sequence ([Term/WF]
     stage three: the target computes its own logits at every block position;
     [Report/KP]: the drafter is conditioned on hidden features from several
@@ -433,7 +437,11 @@ def target_forward(tdims, tweights, cache: OracleCache, tokens, feat_layers) -> 
     and residual) with causal attention.  tokens [b, n] sit at positions
     C_s .. C_s + n - 1 (C_s the cached length); their K/V are written to the
     cache at those positions, the cached length is left as it was (the
-    caller commits the accepted rows).  Returns the final normalised hidden
+    caller commits the accepted rows).  With parents [b, n] (a draft tree,
+    parents[s][0] = -1, parents before children) row i is a tree node: its
+    rotary position is C_s + depth(i) and it sees the cached positions and
+    its ancestors and itself only (the ancestor-only mask of the DDTree
+    paragraph); without, the rows form a chain (causal).  Returns the final normalised hidden
     states "hidden" [b, n, H] (what the verify head multiplies by W_lm), the
     features [b, n, len(feat_layers) * H] (the residual stream after each
     listed layer, layer-major) and the residual after every layer."""
@@ -453,13 +461,22 @@ def target_forward(tdims, tweights, cache: OracleCache, tokens, feat_layers) -> 
             if C + n > cache.k.shape[3]:
                 raise ValueError("cache capacity exceeded")
             pos = np.arange(C, C + n)
+            if parents is not None:
+                par = np.asarray(parents[s])
+                depth = np.zeros(n, dtype=np.int64)
+                for i in range(1, n):
+                    depth[i] = depth[par[i]] + 1
+                pos = C + depth
             qs = rope(q[s], pos, tdims.rope_theta)
             ks = rope(k[s], pos, tdims.rope_theta)
             cache.k[l, s, :, C:C + n, :] = ks.transpose(1, 0, 2)
             cache.v[l, s, :, C:C + n, :] = v[s].transpose(1, 0, 2)
             keys = cache.k[l, s, :, :C + n, :].transpose(1, 0, 2)
             vals = cache.v[l, s, :, :C + n, :].transpose(1, 0, 2)
-            o[s] = causal_attention(qs, keys, vals, C)
+            if parents is None:
+                o[s] = causal_attention(qs, keys, vals, C)
+            else:
+                o[s] = masked_attention(qs, keys, vals, C, tree_mask(parents[s]))
         h = h + linear(o.reshape(b, n, nq * d), lw["wo"])
         a = rms_norm(h, lw["mlp_norm"], tdims.rms_eps)
         h = h + linear(silu(linear(a, lw["w_gate"])) * linear(a, lw["w_up"]), lw["w_down"])
@@ -474,3 +491,115 @@ def commit(cache: OracleCache, accept_len) -> None:
     """After verification the accepted prefix and the target's own next
     token stay in the target cache: the cached length grows by L + 1."""
     cache.length += np.asarray(accept_len, dtype=np.int64) + 1
+
+
+# ------------------------------------------------------------ draft trees
+
+def topk_logprobs(logits: np.ndarray, K: int):
+    """The K most probable tokens of each row (highest log-softmax first,
+    lowest index on ties) and their log-probabilities.  logits [..., V]."""
+    lp = log_softmax(logits)
+    order = np.argsort(-lp, axis=-1, kind="stable")[..., :K]
+    return order.astype(np.int64), np.take_along_axis(lp, order, axis=-1)
+
+
+def build_tree(draft_logits: np.ndarray, anchor: int, K: int, N: int):
+    """A draft tree from the drafter's per-position distributions by a
+    best-first heap ([Forum] the DDTree paragraph: multiple continuations
+    from per-position distributions, selected best-first, verified in one
+    target pass).
+
+    Reading: the block's slots are drafted independently in one pass, so a
+    continuation t_1 .. t_k (slot j proposing the (j+1)-th token after the
+    anchor) scores sum_j log q_j(t_j); the tree holds the N continuations of
+    highest score over the top-K tokens of each slot.  Every prefix scores
+    at least as much as its extensions, so these form a tree rooted at the
+    anchor.  The heap pops continuations in score order; after popping
+    (prefix, token of rank r at depth k) it pushes the prefix's next sibling
+    (rank r + 1) and the popped node's first child (rank 0 at depth k + 1).
+    Ties go to the smaller depth, then the smaller ranks.
+
+    draft_logits [B, V].  Returns node tokens [N+1] (node 0 the anchor),
+    parents [N+1] (-1 for the root), depths [N+1] and scores [N+1]; nodes
+    are numbered in pop order, so a parent precedes its children."""
+    import heapq
+    B = draft_logits.shape[0]
+    tok, lp = topk_logprobs(draft_logits, K)
+    tokens, parent, depth, score = [int(anchor)], [-1], [0], [0.0]
+    ranks = [()]
+    heap = [(-float(lp[0, 0]), 1, (0,), 0)]        # (-score, depth, ranks, parent node)
+    while heap and len(tokens) < N + 1:
+        neg, dep, rk, par = heapq.heappop(heap)
+        node = len(tokens)
+        tokens.append(int(tok[dep - 1, rk[-1]]))
+        parent.append(par)
+        depth.append(dep)
+        score.append(-neg)
+        ranks.append(rk)
+        if rk[-1] + 1 < K:                          # next sibling
+            heapq.heappush(heap, (-(score[par] + float(lp[dep - 1, rk[-1] + 1])), dep, rk[:-1] + (rk[-1] + 1,), par))
+        if dep < B:                                 # first child
+            heapq.heappush(heap, (-(-neg + float(lp[dep, 0])), dep + 1, rk + (0,), node))
+    return (np.array(tokens, dtype=np.int64), np.array(parent, dtype=np.int64),
+            np.array(depth, dtype=np.int64), np.array(score))
+
+
+def tree_mask(parent) -> np.ndarray:
+    """allowed[i, j]: node j is node i or one of its ancestors."""
+    n = len(parent)
+    allowed = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        j = i
+        while j >= 0:
+            allowed[i, j] = True
+            j = int(parent[j])
+    return allowed
+
+
+def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, C: int, allowed: np.ndarray) -> np.ndarray:
+    """Attention of n new queries over C cached keys (all seen) and the n
+    new keys, new key j seen by query i where allowed[i, j].  Causal
+    attention is the lower-triangular case."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, nq, d = q.shape
+    group = nq // k.shape[1]
+    out = np.empty_like(q)
+    for i in range(n):
+        keys = np.concatenate([np.arange(C), C + np.nonzero(allowed[i])[0]])
+        for h in range(nq):
+            g = h // group
+            s = (k[keys, g, :] @ q[i, h, :]) / np.sqrt(d)
+            p = np.exp(s - s.max())
+            out[i, h, :] = (p / p.sum()) @ v[keys, g, :]
+    return out
+
+
+def tree_accept(tokens, parent, target_argmax):
+    """Greedy acceptance over a tree ([Term/WF] stages three and four):
+    from the root, follow the child whose token is the target's argmax at
+    the current node (the lowest-numbered such child), as long as there is
+    one.  Returns the accepted length L (the depth reached), the fallback
+    token (the target's argmax at the last accepted node) and the path of
+    nodes [0, n_1, .., n_L]."""
+    node, path = 0, [0]
+    while True:
+        g = int(target_argmax[node])
+        kids = [c for c in range(len(tokens)) if int(parent[c]) == node and int(tokens[c]) == g]
+        if not kids:
+            break
+        node = kids[0]
+        path.append(node)
+    return len(path) - 1, int(target_argmax[node]), np.array(path, dtype=np.int64)
+
+
+def commit_path(cache: OracleCache, seq: int, path) -> None:
+    """Keep a tree pass's accepted path in the target cache: the K/V rows of
+    path node k (written at slot C + node) move to C + k, and the cached
+    length grows by len(path)."""
+    C = int(cache.length[seq])
+    rows = C + np.asarray(path, dtype=np.int64)
+    cache.k[:, seq, :, C:C + len(path)] = cache.k[:, seq][:, :, rows].copy()
+    cache.v[:, seq, :, C:C + len(path)] = cache.v[:, seq][:, :, rows].copy()
+    cache.length[seq] = C + len(path)

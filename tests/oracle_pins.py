@@ -651,6 +651,90 @@ def check_target_closed_form():
     assert np.allclose(out["features"][0, 1], np.array([1.0, 0.0]) + o, atol=1e-12)
 
 
+def check_tree_is_the_best_continuations():
+    """build_tree against brute force: every continuation of length 1 .. B
+    over the top-K tokens of each slot, scored by its summed log-probability;
+    the tree's nodes are the N best, form a tree (each node's parent is its
+    prefix) and sit at their prefix's depth."""
+    rng = np.random.default_rng(20)
+    for B, K, N in ((3, 3, 7), (4, 2, 9), (2, 4, 5)):
+        logits = rng.standard_normal((B, 10)) * 2.0
+        toks, par, dep, score = O.build_tree(logits, 7, K, N)
+        assert len(toks) == N + 1 and par[0] == -1 and toks[0] == 7
+        lp = O.log_softmax(logits)
+        top = np.argsort(-lp, axis=-1, kind="stable")[:, :K]
+        allc = []
+        for k in range(1, B + 1):
+            for rk in itertools.product(range(K), repeat=k):
+                allc.append((sum(lp[j, top[j, r]] for j, r in enumerate(rk)), tuple(int(top[j, r]) for j, r in enumerate(rk))))
+        allc.sort(key=lambda t: -t[0])
+        best = {c for _, c in allc[:N]}
+        seq = {}
+        for i in range(1, N + 1):
+            seq[i] = (seq[par[i]] if par[i] > 0 else ()) + (int(toks[i]),)
+            assert par[i] < i and dep[i] == len(seq[i])
+            assert abs(score[i] - sum(lp[j, t] for j, t in enumerate(seq[i]))) < 1e-12
+        assert set(seq.values()) == best
+
+
+def check_tree_chain_is_causal():
+    """A chain (each node the child of the one before) is the causal pass:
+    the tree form of target_forward over a chain equals the causal form, and
+    the tree accept over a chain is the chain accept."""
+    w = small_weights(TARGET)
+    toks = np.random.default_rng(21).integers(0, TARGET.vocab, size=(2, 6))
+    chain = np.tile(np.arange(-1, 5), (2, 1))
+    a = O.target_forward(TARGET, w, _target_cache(TARGET, w, 2, 6), toks, [1])
+    b = O.target_forward(TARGET, w, _target_cache(TARGET, w, 2, 6), toks, [1], parents=chain)
+    assert np.allclose(a["hidden"], b["hidden"], atol=1e-13)
+    g = np.random.default_rng(22)
+    for _ in range(50):
+        draft = g.integers(0, 3, size=5)
+        tgt = g.integers(0, 3, size=6)
+        L, bonus = O.accept(draft[None], tgt[None])
+        Lt, bt, path = O.tree_accept(np.concatenate([[9], draft]), np.arange(-1, 5), tgt)
+        assert Lt == L[0] and bt == bonus[0] and np.array_equal(path, np.arange(L[0] + 1))
+
+
+def check_tree_mask_and_accept_golden():
+    """A hand-built tree: root 0 with children 1 (token 5) and 2 (token 7);
+    node 1 with child 3 (token 4); node 2 with child 4 (token 4)."""
+    par = np.array([-1, 0, 0, 1, 2])
+    toks = np.array([3, 5, 7, 4, 4])
+    m = O.tree_mask(par)
+    assert m.tolist() == [[1, 0, 0, 0, 0], [1, 1, 0, 0, 0], [1, 0, 1, 0, 0], [1, 1, 0, 1, 0], [1, 0, 1, 0, 1]]
+    # target argmax per node: root -> 7 (node 2), node 2 -> 4 (node 4), node 4 -> 9 (stop)
+    L, bonus, path = O.tree_accept(toks, par, np.array([7, 4, 4, 0, 9]))
+    assert (L, bonus, path.tolist()) == (2, 9, [0, 2, 4])
+    L, bonus, path = O.tree_accept(toks, par, np.array([6, 4, 4, 0, 9]))
+    assert (L, bonus, path.tolist()) == (0, 6, [0])
+    # two children with the same token: the lower-numbered one is followed
+    par2 = np.array([-1, 0, 0, 2])
+    L, bonus, path = O.tree_accept(np.array([3, 5, 5, 8]), par2, np.array([5, 1, 8, 2]))
+    assert (L, bonus, path.tolist()) == (1, 1, [0, 1])
+
+
+def check_tree_commit_is_the_path():
+    """After a tree pass and commit_path of an accepted path, the cache is
+    the one a causal pass over the path's tokens leaves: a following pass
+    gives the same hidden states both ways."""
+    w = small_weights(TARGET)
+    par = np.array([[-1, 0, 0, 1, 2, 3]])
+    toks = np.array([[3, 5, 7, 4, 4, 11]])
+    path = np.array([0, 1, 3, 5])
+    c1 = _target_cache(TARGET, w, 1, 5)
+    O.target_forward(TARGET, w, c1, toks, [], parents=par)
+    O.commit_path(c1, 0, path)
+    c2 = _target_cache(TARGET, w, 1, 5)
+    O.target_forward(TARGET, w, c2, toks[:, path], [])
+    O.commit(c2, np.array([len(path) - 1]))
+    assert c1.length[0] == c2.length[0] == 9
+    nxt = np.array([[8, 2]])
+    a = O.target_forward(TARGET, w, c1, nxt, [])
+    b = O.target_forward(TARGET, w, c2, nxt, [])
+    assert np.allclose(a["hidden"], b["hidden"], atol=1e-12)
+
+
 def check_planted_recovery():
     """Verify on planted target states recovers the planted accept length
     and fallback token exactly (the self-logit margin is large)."""
@@ -697,5 +781,7 @@ ALL_CHECKS = [
     check_speculative_sampling_is_lossless, check_speculative_special_cases,
     check_causal_attention_bruteforce, check_target_causality, check_target_incremental,
     check_target_closed_form,
+    check_tree_is_the_best_continuations, check_tree_chain_is_causal,
+    check_tree_mask_and_accept_golden, check_tree_commit_is_the_path,
     check_planted_recovery, check_cost_model_simulation,
 ]

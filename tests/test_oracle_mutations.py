@@ -51,12 +51,18 @@ MUTATIONS = {
     "bonus from the last drafted row": ("logw = lp[B]", "logw = lp[B - 1]"),
     "target not causal": ("T = C + i + 1", "T = C + n"),
     "target sees one key ahead": ("T = C + i + 1", "T = min(C + i + 2, C + n)"),
-    "target positions from 0": ("            pos = np.arange(C, C + n)\n            qs = rope(q[s], pos, tdims.rope_theta)",
-                                "            pos = np.arange(0, n)\n            qs = rope(q[s], pos, tdims.rope_theta)"),
+    "target positions from 0": ("            pos = np.arange(C, C + n)\n            if parents is not None:",
+                                "            pos = np.arange(0, n)\n            if parents is not None:"),
     "commit without the next token": ("cache.length += np.asarray(accept_len, dtype=np.int64) + 1",
                                       "cache.length += np.asarray(accept_len, dtype=np.int64)"),
     "features one layer late": ("feats = [resid[l] for l in feat_layers]",
                                 "feats = [resid[min(l + 1, len(resid) - 1)] for l in feat_layers]"),
+    "tree sibling not pushed": ("        if rk[-1] + 1 < K:                          # next sibling",
+                                "        if False:                                   # next sibling"),
+    "tree positions in slot order": ("                pos = C + depth", "                pos = C + np.arange(n)"),
+    "tree mask without ancestors": ("            j = int(parent[j])", "            j = -1"),
+    "tree accept follows the last match": ("        node = kids[0]", "        node = kids[-1]"),
+    "tree commit keeps slot order": ("    rows = C + np.asarray(path, dtype=np.int64)", "    rows = C + np.arange(len(path))"),
     "inject wrong slot": ("cache.k[l, s, :, start:start + n, :] = k.transpose(1, 0, 2)",
                           "cache.k[l, s, :, start + 1:start + n + 1, :] = k.transpose(1, 0, 2)"),
 }
