@@ -299,6 +299,21 @@ def time_target(torch, dr, d, b, ctx, B, verify_bytes, step_ms, e_l, steps):
     al = torch.empty(b, dtype=torch.int32, device=dev)
     bo = torch.empty(b, dtype=torch.int32, device=dev)
     t_head = timed(lambda: dr.verify(th2, d2, ta, al, bo, b, block_size=1))
+    # a DDTree step's device work: the draft tree (drafting pass with its
+    # logits, top-4 per slot, 31 nodes best-first), the target's pass over
+    # the 32 tree nodes, the walk and the path commit
+    K, N = 4, 31
+    dlog = torch.empty((b * B, d.vocab), dtype=torch.float32, device=dev)
+    tt = torch.empty((b, N + 1), dtype=torch.int32, device=dev)
+    tp = torch.empty((b, N + 1), dtype=torch.int32, device=dev)
+    thid = torch.empty((b, N + 1, td.hidden), dtype=torch.bfloat16, device=dev)
+    tfeat = torch.empty((b, N + 1, td.n_feat_layers * td.hidden), dtype=torch.bfloat16, device=dev)
+    tta = torch.empty((b, N + 1), dtype=torch.int32, device=dev)
+    tpath = torch.empty((b, N + 1), dtype=torch.int32, device=dev)
+    last = torch.zeros(b, dtype=torch.int32, device=dev)
+    t_tree_draft = timed(lambda: dr.draft_tree(last, K, N, dlog, tt, tp, b))
+    t_tree_pass = timed(lambda: tg.forward(tt, b, N + 1, feat_layers, thid, tfeat, parents=tp))
+    t_tree_accept = timed(lambda: dr.tree_accept(thid, tt, tp, b, N + 1, tta, al, bo, tpath))
     status = tg.read_status()
     del tg
     torch.cuda.empty_cache()
@@ -320,6 +335,10 @@ def time_target(torch, dr, d, b, ctx, B, verify_bytes, step_ms, e_l, steps):
         "C_AR_ms": round(c_ar, 4), "C_DF_ms": round(c_df, 4),
         "S_with_E_L": round(c_ar * e_l / c_df, 3), "S_with_E_L_plus_bonus": round(c_ar * (e_l + 1) / c_df, 3),
         "E_L_planted": round(e_l, 4), "status": status,
+        "ddtree_step": {"topk": K, "nodes": N + 1, "draft_tree_ms": round(t_tree_draft, 4),
+                        "target_tree_pass_ms": round(t_tree_pass, 4), "tree_accept_ms": round(t_tree_accept, 4),
+                        "note": "the drafting pass with its logits, top-K and the best-first build; the 36-layer "
+                                "target over the tree nodes under the ancestor mask; lm_head argmax and walk"},
         "source": "S = C_AR * E / C_DF, C_AR = one-row target pass + lm_head argmax, "
                   "C_DF = draft step + the target's (B+1)-row verify pass, all measured",
     }

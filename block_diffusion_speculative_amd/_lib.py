@@ -25,6 +25,7 @@ DFLASH_ERR_UNSUPPORTED = -7
 DFLASH_STATUS_CAPACITY = 1
 DFLASH_STATUS_TOKEN = 2
 DFLASH_STATUS_ANCHOR = 4
+DFLASH_STATUS_TREE = 8
 VIEW_FUSED, VIEW_HIDDEN, VIEW_MID, VIEW_ATTN = range(4)
 
 EXPORTED = [
@@ -34,6 +35,7 @@ EXPORTED = [
     "dflash_workspace_bytes", "dflash_workspace_init", "dflash_workspace_view",
     "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_anchors", "dflash_draft_sample",
     "dflash_target_workspace_bytes", "dflash_target_forward", "dflash_kv_commit",
+    "dflash_draft_tree", "dflash_tree_accept", "dflash_kv_commit_path",
     "dflash_verify_sample", "dflash_verify_accept", "dflash_verify_accept_noalloc",
     "dflash_status_str", "dflash_last_error", "dflash_abi_version", "dflash_build_id",
 ]
@@ -102,8 +104,13 @@ def load() -> ctypes.CDLL:
         "dflash_draft_anchors": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, P, P,
                                            c_int32, P, P, c_size_t, P]),
         "dflash_target_workspace_bytes": (c_size_t, [POINTER(Dims), c_int32, c_int32]),
-        "dflash_target_forward": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, c_int32, c_int32,
-                                            P, c_int32, P, P, P, c_size_t, P]),
+        "dflash_target_forward": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, P, c_int32,
+                                            c_int32, P, c_int32, P, P, P, c_size_t, P]),
+        "dflash_draft_tree": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, c_int32, c_int32,
+                                        c_int32, P, P, P, P, c_size_t, P]),
+        "dflash_tree_accept": (c_int32, [POINTER(Dims), P, P, P, P, c_int32, c_int32, P, P, P, P, P,
+                                         c_size_t, P]),
+        "dflash_kv_commit_path": (c_int32, [POINTER(Dims), POINTER(KV), P, P, c_int32, c_int32, P]),
         "dflash_kv_commit": (c_int32, [POINTER(Dims), POINTER(KV), P, c_int32, c_int32, P]),
         "dflash_draft_sample": (c_int32, [POINTER(Dims), POINTER(Weights), POINTER(KV), P, c_int32,
                                           c_float, P, P, P, P, c_size_t, P]),

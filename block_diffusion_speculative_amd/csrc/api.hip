@@ -114,7 +114,7 @@ int act_planes(const dflash_dims *d) { return d->dtype == DFLASH_BF16 ? 2 : 1; }
 int mlp_act_planes(const dflash_dims *d, int rows) { return rows > MLP_ONE_PLANE_ROWS ? act_planes(d) : 1; }
 
 struct DraftLayout {
-  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, anc, end;
+  size_t hidden, mid, attn, xa, xo, xact, qbuf, kblk, vblk, apart, ssq, rs, part, anc, tree, end;
   size_t pa, po, pact, pq;  // bytes of one plane of xa, xo, xact, qbuf
   int M, Mp, S, xs, act_xs;  // planes of the packed activations and of the SwiGLU output
   int rows, q_tiles;         // rows per sequence; 16-row query tiles per sequence
@@ -164,6 +164,9 @@ DraftLayout draft_layout(const dflash_dims *d, int batch, int rows = 0, bool tar
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
   L.part = L.M > STEP_TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.anc = b.take(size_t(2) * MAX_BATCH * 4);   // anchored blocks: checked context lengths, cache regions
+  // draft trees: per slot row the log-sum-exp, its chunk partials and the
+  // top-K (value, index); target tree passes: per row depth and ancestor mask
+  L.tree = b.take(size_t(L.M) * (4 + ARGMAX_SLOTS * 8 + 8 * 8) + size_t(L.M) * 8);
   L.end = b.off;
   return L;
 }
@@ -398,6 +401,8 @@ struct LayerRun {
   size_t region_layer;
   int capacity, max_batch;
   bool causal;                  // target pass: causal block, new K/V appended to the cache
+  const int *row_pos;           // tree pass: per-row depth (rotary offset)
+  const unsigned *row_mask;     // tree pass: per-row ancestor mask
   unsigned *status;
   const char *what;
 };
@@ -441,6 +446,7 @@ int run_layer(const LayerRun &r, const dflash_layer &lw, int l, const void *next
     q.capacity = r.capacity;
     q.max_batch = r.max_batch;
     q.status = r.status;
+    q.row_pos = r.row_pos;
   }
   e = set_norm_in(q, L.rs_inline, ssq, rs, L.M, H, d->rms_eps, stream);
   if (e == hipSuccess) e = launch_gemm(d->dtype, EPI_QKV, q, stream);
@@ -460,7 +466,8 @@ int run_layer(const LayerRun &r, const dflash_layer &lw, int l, const void *next
   a.part = reinterpret_cast<float *>(wsb + L.apart);
   a.block = L.rows;
   a.q_tiles = L.q_tiles;
-  a.causal = r.causal ? 1 : 0;
+  a.causal = r.causal && !r.row_mask ? 1 : 0;
+  a.row_mask = r.row_mask;
   a.n_q = d->n_q_heads;
   a.n_kv = d->n_kv_heads;
   a.head_dim = hd;
@@ -795,7 +802,8 @@ static int draft_impl(const dflash_dims *d, const dflash_weights *w, const dflas
   TRY(check_weights(d, w, false, true));
   TRY(check_kv(d, kv));
   TRY(check_ptr(last_tok, anchor_pos ? "anchor_tok" : "last_tok", false));
-  TRY(check_ptr(draft, "draft", false));
+  const bool logits_only = draft_logits && !u_draft;   // draft trees: no per-slot tokens
+  if (!logits_only) TRY(check_ptr(draft, "draft", false));
   TRY(check_ptr(ws, "ws"));
   if (anchor_pos) {
     TRY(check_ptr(anchor_seq, "anchor_seq", false));
@@ -893,13 +901,14 @@ static int draft_impl(const dflash_dims *d, const dflash_weights *w, const dflas
   fp.block = d->block_size;
   fp.verify = 0;
   fp.tok_out = draft;
-  if (temperature <= 0.f) return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "draft");
-  // Sampling: the head stores its logits; Gumbel-max per row, folded by the
-  // argmax finish.
+  if (temperature <= 0.f && !draft_logits) return launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "draft");
+  // Sampling (and draft trees): the head stores its logits; for sampling a
+  // Gumbel-max per row, folded by the argmax finish.
   lm.out_f32 = draft_logits;
   lm.ld_out = d->vocab;
   e = launch_gemm(d->dtype, EPI_LOGITS, lm, stream);
   if (e != hipSuccess) return hip_fail(e, "draft logits");
+  if (!u_draft) return DFLASH_OK;
   SampleParams sp{};
   sp.logits = draft_logits;
   sp.ld = d->vocab;
@@ -933,9 +942,9 @@ size_t dflash_target_workspace_bytes(const dflash_dims *td, int32_t max_batch, i
 }
 
 int dflash_target_forward(const dflash_dims *td, const dflash_weights *tw, const dflash_kv *tkv,
-                          const int32_t *tokens, int32_t batch, int32_t rows, const int32_t *feat_layers,
-                          int32_t n_feat, void *out_hidden, void *out_feats, void *ws, size_t ws_bytes,
-                          hipStream_t stream) {
+                          const int32_t *tokens, const int32_t *parents, int32_t batch, int32_t rows,
+                          const int32_t *feat_layers, int32_t n_feat, void *out_hidden, void *out_feats, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
   TRY(check_dims(td, MAX_TARGET_LAYERS));
   if (!tw) return fail(DFLASH_ERR_NULL, "weights is NULL");
   if (!tw->layers) return fail(DFLASH_ERR_NULL, "weights->layers is NULL");
@@ -1011,6 +1020,14 @@ int dflash_target_forward(const dflash_dims *td, const dflash_weights *tw, const
   run.causal = true;
   run.status = tkv->status;
   run.what = "target";
+  if (parents) {
+    int *depth = reinterpret_cast<int *>(wsb + L.tree);
+    unsigned *mask = reinterpret_cast<unsigned *>(depth + L.M);
+    e = launch_tree_prep(parents, batch, rows, depth, mask, tkv->status, stream);
+    if (e != hipSuccess) return hip_fail(e, "target tree");
+    run.row_pos = depth;
+    run.row_mask = mask;
+  }
   const int NL = td->n_layers;
   for (int l = 0; l < NL; ++l) {
     char *aux = nullptr;   // feature k: columns [k H, (k + 1) H) of out_feats
@@ -1033,6 +1050,90 @@ int dflash_kv_commit(const dflash_dims *d, const dflash_kv *kv, const int32_t *a
   if (max_commit < 0) return fail(DFLASH_ERR_SHAPE, "max_commit must be >= 0");
   const hipError_t e = launch_kv_commit(kv->ctx_len, accept_len, batch, max_commit, kv->capacity, stream);
   return e == hipSuccess ? DFLASH_OK : hip_fail(e, "kv commit");
+}
+
+int dflash_draft_tree(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,
+                      int32_t batch, int32_t topk, int32_t nodes, float *draft_logits, int32_t *tree_tok,
+                      int32_t *tree_parent, void *ws, size_t ws_bytes, hipStream_t stream) {
+  TRY(check_dims(d));
+  if (topk < 1 || topk > 8) return fail(DFLASH_ERR_SHAPE, "topk must be in [1, 8]");
+  if (nodes < 1 || nodes > 31) return fail(DFLASH_ERR_SHAPE, "nodes must be in [1, 31]");
+  long long avail = 0, pw = 1;   // continuations of length 1 .. B over topk tokens per slot
+  for (int j = 0; j < d->block_size && avail < nodes; ++j) {
+    pw *= topk;
+    avail += pw;
+  }
+  if (avail < nodes) return fail(DFLASH_ERR_SHAPE, "nodes exceeds the continuations of block_size slots over topk tokens");
+  TRY(check_ptr(draft_logits, "draft_logits", false));
+  TRY(check_ptr(tree_tok, "tree_tok", false));
+  TRY(check_ptr(tree_parent, "tree_parent", false));
+  // the drafting pass with its logits (placeholder draft output: the tree
+  // replaces the per-slot tokens)
+  const DraftLayout L = draft_layout(d, batch);
+  if (!ws || ws_bytes < L.end) return fail(DFLASH_ERR_WORKSPACE, "workspace too small for this batch");
+  TRY(draft_impl(d, w, kv, last_tok, nullptr, nullptr, batch, nullptr, ws, ws_bytes, stream, 1.0f, nullptr,
+                 draft_logits));
+  char *wsb = static_cast<char *>(ws);
+  const int V = d->vocab, rows = L.M, ch = sample_chunks(V);
+  float *lse = reinterpret_cast<float *>(wsb + L.tree);
+  float2 *part = reinterpret_cast<float2 *>(lse + rows);
+  float *tv = reinterpret_cast<float *>(part + size_t(rows) * ARGMAX_SLOTS);
+  int *ti = reinterpret_cast<int *>(tv + size_t(rows) * 8);
+  hipError_t e = launch_row_lse(draft_logits, V, V, 1.0f, rows, ch, part, lse, stream);
+  if (e == hipSuccess) e = launch_row_topk(draft_logits, V, V, rows, topk, lse, tv, ti, stream);
+  if (e == hipSuccess)
+    e = launch_tree_build(tv, ti, last_tok, batch, d->block_size, topk, nodes, tree_tok, tree_parent, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "draft tree");
+}
+
+int dflash_tree_accept(const dflash_dims *d, const void *lm_head, const void *target_hidden, const int32_t *tree_tok,
+                       const int32_t *tree_parent, int32_t batch, int32_t n, int32_t *target_argmax,
+                       int32_t *accept_len, int32_t *bonus, int32_t *path, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  TRY(check_dims(d));
+  TRY(check_ptr(lm_head, "lm_head"));
+  TRY(check_ptr(target_hidden, "target_hidden"));
+  TRY(check_ptr(tree_tok, "tree_tok", false));
+  TRY(check_ptr(tree_parent, "tree_parent", false));
+  TRY(check_ptr(target_argmax, "target_argmax", false));
+  TRY(check_ptr(accept_len, "accept_len", false));
+  TRY(check_ptr(bonus, "bonus", false));
+  TRY(check_ptr(path, "path", false));
+  TRY(check_ptr(ws, "ws"));
+  if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
+  if (n < 1 || n > 32 || size_t(batch) * n > size_t(MAX_KEY_ROWS)) return fail(DFLASH_ERR_SHAPE, "n must be in [1, 32]");
+  if (ws_bytes < WS_COUNTER_BYTES) return fail(DFLASH_ERR_WORKSPACE, "workspace smaller than its counter area");
+  char *wsb = static_cast<char *>(ws);
+  GemmParams lm{};
+  fill_gemm(lm, plan_gemm(d->dtype, batch * n, d->vocab, d->hidden, 2, STEP_TILED_MIN_ROWS));
+  lm.w_seg[0] = static_cast<const char *>(lm_head);
+  lm.x = static_cast<const char *>(target_hidden);
+  lm.x_ld = d->hidden;
+  lm.vocab = d->vocab;
+  lm.keys = reinterpret_cast<unsigned long long *>(wsb);
+  ArgmaxFinishParams fp{};
+  fp.keys = lm.keys;
+  fp.rows_per_seq = n;
+  fp.block = n;
+  fp.verify = 0;
+  fp.tok_out = target_argmax;
+  TRY(launch_argmax_head(d->dtype, lm, fp, wsb, batch, stream, "tree verify"));
+  const hipError_t e = launch_tree_walk(tree_tok, tree_parent, target_argmax, batch, n, accept_len, bonus, path, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "tree walk");
+}
+
+int dflash_kv_commit_path(const dflash_dims *d, const dflash_kv *kv, const int32_t *path, const int32_t *accept_len,
+                          int32_t batch, int32_t n, hipStream_t stream) {
+  TRY(check_dims(d, MAX_TARGET_LAYERS));
+  TRY(check_kv(d, kv));
+  TRY(check_ptr(path, "path", false));
+  TRY(check_ptr(accept_len, "accept_len", false));
+  if (batch < 1 || batch > kv->max_batch) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, kv->max_batch]");
+  if (n < 1 || n > 32) return fail(DFLASH_ERR_SHAPE, "n must be in [1, 32]");
+  const hipError_t e = launch_commit_path(d->dtype, static_cast<char *>(kv->k), static_cast<char *>(kv->v), kv->ctx_len,
+                                          path, accept_len, batch, n, d->n_layers, kv->max_batch, d->n_kv_heads,
+                                          kv->capacity, d->head_dim, stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "kv commit path");
 }
 
 int dflash_draft_sample(const dflash_dims *d, const dflash_weights *w, const dflash_kv *kv, const int32_t *last_tok,

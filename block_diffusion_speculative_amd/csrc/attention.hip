@@ -150,8 +150,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = 16 * t + 4 * gq + i;
-        // a causal pass lets block row qrow see block positions <= qrow only
-        const bool seen = pos < nvalid && !(blk && p.causal && pos > qrow);
+        // a causal pass lets block row qrow see block positions <= qrow only,
+        // a tree pass its ancestors and itself (row_mask bits)
+        bool seen = pos < nvalid && !(blk && p.causal && pos > qrow);
+        if (blk && p.row_mask) seen = seen && qrow < p.block && ((p.row_mask[s * p.block + qrow] >> pos) & 1u);
         const float x = seen ? sacc[t][i] * p.scale_log2 : -INFINITY;
         sv[4 * t + i] = x;
         mx = fmaxf(mx, x);

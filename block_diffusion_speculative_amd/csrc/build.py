@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["gemm.hip", "gemm_tiled.hip", "attention.hip", "misc.hip", "sampling.hip", "api.hip", "noalloc.hip"]
+SOURCES = ["gemm.hip", "gemm_tiled.hip", "attention.hip", "misc.hip", "sampling.hip", "tree.hip", "api.hip", "noalloc.hip"]
 LIB = os.path.join(PKG, "libdflash.so")
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 

@@ -108,7 +108,7 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
       float v = val(ml, nl);
       if (n < nqd + nkd) {
         const int dd = rot_channel(n % d, d);
-        const int pos = p.ctx_len[s] + j;
+        const int pos = p.ctx_len[s] + (p.row_pos ? p.row_pos[m] : j);
         v = rope_apply(v, val(ml, nl ^ 8), dd, d, pos, p);
         if (n < nqd) {
           const int h = n / d;
@@ -118,7 +118,8 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
           const int g = (n - nqd) / d;
           char *base = p.kblk + (size_t(s) * p.n_kv + g) * size_t(KT) * d * ES;
           store_elem<T>(base + kcache_offset<T>(j, dd, d), v);
-          if (p.qkv_to_cache) qkv_cache_store<T>(p, true, s, g, pos, dd, v);
+          // cache slot ctx + j (slot order); its rotary position may be a tree depth
+          if (p.qkv_to_cache) qkv_cache_store<T>(p, true, s, g, p.ctx_len[s] + j, dd, v);
         }
       } else {
         const int c = n - nqd - nkd;

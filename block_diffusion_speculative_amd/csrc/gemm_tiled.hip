@@ -285,7 +285,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
               float x = v[i];
               if (n < nqd + nkd) {
                 const int dd = rot_channel(n % d, d);
-                x = rope_apply(x, partner, dd, d, p.ctx_len[sq] + j, p);
+                x = rope_apply(x, partner, dd, d, p.ctx_len[sq] + (p.row_pos ? p.row_pos[m] : j), p);
                 if (n < nqd) {
                   char *base = p.qbuf + (size_t(sq) * p.n_q + n / d) * p.q_tiles * dt_count * 1024;
                   store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.q_planes, x);

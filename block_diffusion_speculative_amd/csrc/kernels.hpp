@@ -87,6 +87,9 @@ struct GemmParams {
   // EPI_QKV of a causal pass: the new rows' K/V also go to the cache
   // (kcache / vcache, layer layer0) at position ctx_len[s] + j.
   int qkv_to_cache;
+  // Tree rows: row m's rotary position is ctx_len[s] + row_pos[m] (its
+  // depth) instead of ctx_len[s] + j; null: j.
+  const int *row_pos;
   char *kcache, *vcache;
   int layer0, capacity, max_batch;
   const int *cu_new;
@@ -162,6 +165,7 @@ struct AttnParams {
   int head_split;                   // workgroups sharing one KV head's query group
   int q_tiles;                      // 16-row query tiles per sequence (block rows up to 16 * q_tiles)
   int causal;                       // block row i sees block positions <= i only
+  const unsigned *row_mask;         // tree rows: block row i sees block positions j with bit j set
   float scale_log2;                 // log2(e) / sqrt(head_dim)
   // merge
   float *attn_out;                  // fp32 [batch*block, n_q*d]
@@ -219,6 +223,32 @@ hipError_t launch_gumbel_draft(const SampleParams &p, int rows, hipStream_t s);
 hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, int rows, int chunks, float2 *part,
                           float *lse, hipStream_t s);
 hipError_t launch_spec_sample(const SampleParams &p, int batch, hipStream_t s);
+
+// Draft trees (tree.hip).
+// Per row of logits, the K most probable entries as (log-probability,
+// index), highest first (lowest index on ties): topk_val / topk_idx
+// [rows][K]; lse[row] the row's log-sum-exp.
+hipError_t launch_row_topk(const float *logits, int ld, int vocab, int rows, int K, const float *lse,
+                           float *topk_val, int *topk_idx, hipStream_t s);
+// Best-first trees, one per sequence: from the top-K of its B slots
+// (rows s * B + j), N nodes after the anchor; tree_tok / tree_parent
+// [batch][N + 1].
+hipError_t launch_tree_build(const float *topk_val, const int *topk_idx, const int *anchor, int batch, int B,
+                             int K, int N, int *tree_tok, int *tree_parent, hipStream_t s);
+// Node depths and ancestor masks of trees of n rows (parents[s][0] = -1,
+// each parent before its child; a malformed parent sets status bit
+// DFLASH_STATUS_TREE and is read as the previous node).
+hipError_t launch_tree_prep(const int *parent, int batch, int n, int *depth, unsigned *mask, unsigned *status,
+                            hipStream_t s);
+// Greedy walk down each tree along the target's argmax: accept_len, bonus,
+// path [batch][n] (node ids, -1 past the end).
+hipError_t launch_tree_walk(const int *tree_tok, const int *parent, const int *target_argmax, int batch, int n,
+                            int *accept_len, int *bonus, int *path, hipStream_t s);
+// Move each sequence's accepted path rows (ctx_len + path[k]) to
+// ctx_len + k in every layer and KV head, then ctx_len += accept_len + 1.
+hipError_t launch_commit_path(int dtype, char *kcache, char *vcache, int *ctx_len, const int *path,
+                              const int *accept_len, int batch, int n, int n_layers, int max_batch, int n_kv,
+                              int capacity, int head_dim, hipStream_t s);
 
 // Greedy verification with its scratch (argmax key slots and the arrival
 // counter, at least WS_COUNTER_BYTES, zero on entry) at wsb: the body of

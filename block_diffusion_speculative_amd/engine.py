@@ -125,15 +125,20 @@ class Target:
         _lib.call("dflash_workspace_init", self.ws.data_ptr(), self.ws_bytes, sp)
 
     def forward(self, tokens: torch.Tensor, batch: int, rows: int, feat_layers: Sequence[int],
-                out_hidden: torch.Tensor, out_feats: Optional[torch.Tensor], stream=None):
+                out_hidden: torch.Tensor, out_feats: Optional[torch.Tensor], stream=None,
+                parents: Optional[torch.Tensor] = None):
         fl = (ctypes.c_int32 * max(1, len(feat_layers)))(*feat_layers)
         _lib.call("dflash_target_forward", ctypes.byref(self.cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
-                  _ptr(tokens), batch, rows, fl, len(feat_layers), _ptr(out_hidden), _ptr(out_feats),
-                  self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
+                  _ptr(tokens), _ptr(parents), batch, rows, fl, len(feat_layers), _ptr(out_hidden),
+                  _ptr(out_feats), self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
 
     def commit(self, accept_len: torch.Tensor, batch: int, max_commit: int, stream=None):
         _lib.call("dflash_kv_commit", ctypes.byref(self.cd), ctypes.byref(self.ckv), _ptr(accept_len), batch,
                   max_commit, _stream_ptr(stream))
+
+    def commit_path(self, path: torch.Tensor, accept_len: torch.Tensor, batch: int, n: int, stream=None):
+        _lib.call("dflash_kv_commit_path", ctypes.byref(self.cd), ctypes.byref(self.ckv), _ptr(path),
+                  _ptr(accept_len), batch, n, _stream_ptr(stream))
 
     def kv_import(self, k: torch.Tensor, v: torch.Tensor, stream=None):
         _lib.call("dflash_kv_import", ctypes.byref(self.cd), ctypes.byref(self.ckv), k.data_ptr(),
@@ -282,6 +287,19 @@ class Drafter:
                   _ptr(draft), _ptr(draft_logits), batch, float(temperature), _ptr(u_accept), _ptr(u_resid),
                   _ptr(target_logits), _ptr(accept_len), _ptr(next_tok), self.ws.data_ptr(), self.ws_bytes,
                   _stream_ptr(stream))
+
+    def draft_tree(self, last_tok: torch.Tensor, topk: int, nodes: int, draft_logits: torch.Tensor,
+                   tree_tok: torch.Tensor, tree_parent: torch.Tensor, batch: int, stream=None):
+        _lib.call("dflash_draft_tree", ctypes.byref(self.cd), ctypes.byref(self.cw), ctypes.byref(self.ckv),
+                  _ptr(last_tok), batch, topk, nodes, _ptr(draft_logits), _ptr(tree_tok), _ptr(tree_parent),
+                  self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
+
+    def tree_accept(self, target_hidden: torch.Tensor, tree_tok: torch.Tensor, tree_parent: torch.Tensor,
+                    batch: int, n: int, target_argmax: torch.Tensor, accept_len: torch.Tensor,
+                    bonus: torch.Tensor, path: torch.Tensor, stream=None):
+        _lib.call("dflash_tree_accept", ctypes.byref(self.cd), self.lm_head.data_ptr(), _ptr(target_hidden),
+                  _ptr(tree_tok), _ptr(tree_parent), batch, n, _ptr(target_argmax), _ptr(accept_len), _ptr(bonus),
+                  _ptr(path), self.ws.data_ptr(), self.ws_bytes, _stream_ptr(stream))
 
     def verify(self, target_hidden: torch.Tensor, draft: torch.Tensor, target_argmax: torch.Tensor,
                accept_len: torch.Tensor, bonus: torch.Tensor, batch: int, stream=None,

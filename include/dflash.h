@@ -86,6 +86,7 @@ typedef enum {
 #define DFLASH_STATUS_CAPACITY 1u  /* an injection would exceed kv->capacity */
 #define DFLASH_STATUS_TOKEN 2u     /* a token id outside [0, vocab) was clamped */
 #define DFLASH_STATUS_ANCHOR 4u    /* an anchor outside its sequence's cache was clamped */
+#define DFLASH_STATUS_TREE 8u      /* a malformed tree parent was read as the previous node */
 
 /* Drafter dimensions [host].  Every call that takes dims checks them first.
  * DFLASH_ERR_SHAPE (malformed): hidden, head_dim, intermediate and vocab
@@ -281,14 +282,52 @@ int dflash_draft_anchors(const dflash_dims *dims, const dflash_weights *w, const
  * out_feats [batch, rows, n_feat * H], the residual stream after layer
  * feat_layers[k] ([host] array, distinct indices in [0, n_layers)) in
  * columns [k H, (k + 1) H) (dflash_inject_kv's feature rows).  tokens:
- * [batch, rows] device int32; 1 <= rows <= 32 (bf16) or 16 (fp32); weights:
+ * [batch, rows] device int32.  parents: NULL for the causal chain, or a
+ * draft tree [batch, rows] (parents[s][0] = -1, 0 <= parents[s][i] < i):
+ * row i is a tree node at rotary position ctx_len[s] + depth(i) that sees
+ * the cached positions, its ancestors and itself (the ancestor-only mask of
+ * "LLMs hit ludicrous speed: diffusion decoding and dMoE supercharge AI
+ * inference, shattering old benchmarks", DDTree paragraph; a malformed
+ * parent sets DFLASH_STATUS_TREE and is read as row i - 1); its K/V still go
+ * to cache slot ctx_len[s] + i.  1 <= rows <= 32 (bf16) or 16 (fp32); weights:
  * embed, final_norm and the layers of `tw` (w_fc, fc_norm, lm_head unused).
  * The workspace must hold dflash_target_workspace_bytes(dims, batch, rows). */
 size_t dflash_target_workspace_bytes(const dflash_dims *dims, int32_t max_batch, int32_t rows);
 int dflash_target_forward(const dflash_dims *dims, const dflash_weights *tw, const dflash_kv *kv,
-                          const int32_t *tokens, int32_t batch, int32_t rows, const int32_t *feat_layers,
-                          int32_t n_feat, void *out_hidden, void *out_feats, void *ws, size_t ws_bytes,
-                          hipStream_t stream);
+                          const int32_t *tokens, const int32_t *parents, int32_t batch, int32_t rows,
+                          const int32_t *feat_layers, int32_t n_feat, void *out_hidden, void *out_feats, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Draft trees (the DDTree paragraph above): the drafting pass of
+ * dflash_draft_forward with its logits kept (draft_logits [batch * B,
+ * vocab], caller-owned), then per sequence the tree of the `nodes` best
+ * continuations of last_tok[s] over the topk most probable tokens of each
+ * slot, a continuation t_1 .. t_k scoring sum_j log softmax(l_j)(t_j);
+ * built best-first from a heap, ties to the smaller depth, then the smaller
+ * rank.  Outputs tree_tok and tree_parent [batch, nodes + 1]: node 0 is the
+ * anchor (parent -1), every parent precedes its children.  1 <= topk <= 8,
+ * 1 <= nodes <= 31 and at most the number of continuations of length 1..B. */
+int dflash_draft_tree(const dflash_dims *dims, const dflash_weights *w, const dflash_kv *kv,
+                      const int32_t *last_tok, int32_t batch, int32_t topk, int32_t nodes, float *draft_logits,
+                      int32_t *tree_tok, int32_t *tree_parent, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Greedy acceptance over draft trees: the shared lm_head's lowest-index
+ * argmax at each of the n tree rows of target_hidden [batch, n, H] (the
+ * target's tree pass) into target_argmax [batch, n]; then from the root
+ * down, the child (lowest-numbered) whose token equals the argmax at the
+ * current node, while there is one.  accept_len [batch] = depth reached,
+ * bonus [batch] = argmax at the last accepted node, path [batch, n] = the
+ * accepted nodes from the root (-1 after them).  1 <= n <= 32. */
+int dflash_tree_accept(const dflash_dims *dims, const void *lm_head, const void *target_hidden,
+                       const int32_t *tree_tok, const int32_t *tree_parent, int32_t batch, int32_t n,
+                       int32_t *target_argmax, int32_t *accept_len, int32_t *bonus, int32_t *path, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* After a tree pass: the K/V rows of path node k (cache slot ctx_len[s] +
+ * path[s][k]) move to ctx_len[s] + k for k <= accept_len[s], in every layer
+ * and KV head, then ctx_len[s] += accept_len[s] + 1.  n as for the pass. */
+int dflash_kv_commit_path(const dflash_dims *dims, const dflash_kv *kv, const int32_t *path,
+                          const int32_t *accept_len, int32_t batch, int32_t n, hipStream_t stream);
 
 /* After verification: ctx_len[s] += min(max(accept_len[s] + 1, 0),
  * max_commit), at most kv->capacity (the accepted drafts and the target's
