@@ -261,8 +261,9 @@ def time_target(torch, dr, d, b, ctx, B, verify_bytes, step_ms, e_l, steps):
     td = C.QWEN3_8B_TARGET
     dev = dr.device
     t0 = time.time()
-    cap = C.kv_capacity(int(np.max(ctx)) + B + 1)
-    tg = Target(td, device_target_weights(torch, td, 77, dev), b, cap, max_rows=B + 1, device=dev)
+    cap = C.kv_capacity(int(np.max(ctx)) + 32)
+    # workspace for the 17-row verify pass and the 32-node tree pass
+    tg = Target(td, device_target_weights(torch, td, 77, dev), b, cap, max_rows=32, device=dev)
     shape = (td.n_layers, b, td.n_kv_heads, cap, td.head_dim)
     gen = torch.Generator(device=dev)
     gen.manual_seed(78)
