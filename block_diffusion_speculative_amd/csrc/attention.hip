@@ -59,7 +59,8 @@ __host__ __device__ inline int attn_sub(int heads) {
 // RC: 1 KiB tiles each wavefront loads per round (a compile-time count, so the
 // wait for the older of two rounds in flight is an immediate).  NW: most
 // wavefronts per workgroup (8 leaves each 256 VGPRs, 16 leaves 128).
-template <typename T, int HD, int XS, int RC, int NW>
+// MASK: a causal or tree pass (block positions masked per query row).
+template <typename T, int HD, int XS, int RC, int NW, bool MASK>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   constexpr int KT = Ty<T>::KT, ES = Ty<T>::SIZE;
   constexpr int DT = HD / KT, DV = HD / 16, KTT = KT / 16;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   const int g = blockIdx.y / p.head_split, hs = blockIdx.y % p.head_split;
   const int gw = p.group / p.head_split;            // query heads of this workgroup
   const int waves = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int SUB = attn_sub(gw);
   const int hl = wave % gw, ss = wave / gw;
   const int h = g * p.group + hs * gw + hl;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       if (st >= st1) src = kbk;
       else if (tt < KB / 1024) src = (st == n_ctx ? kbk : kreg + size_t(st) * KB) + tt * 1024;
       else src = (st == n_ctx ? vbk : vreg + size_t(st) * VB) + (tt - KB / 1024) * 1024;
-      load_lds16(src + lane * 16, slot + j * 64);
+      load_lds16_s(src, lane * 16, slot + j * 64);
     }
   };
 
@@ -128,7 +129,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 #pragma unroll
   for (int i = 0; i < DV; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int gq = lane >> 4;
-  const int qrow = qt * 16 + (lane & 15);   // this lane's query row in the block
+  // Which of this lane's block-step positions its query row sees: all valid
+  // slots, or under a causal pass those at or before the row, or under a
+  // tree pass the row's ancestors and itself (row_mask bits).  Bit 4t + i
+  // stands for position 16t + 4gq + i, as in the S^T accumulators.
+  unsigned blk_seen = 0;
+  if constexpr (MASK) {
+    const int qrow = qt * 16 + (lane & 15);
+    const unsigned anc = p.row_mask ? (qrow < p.block ? p.row_mask[s * p.block + qrow] : 0u) : ~0u;
+#pragma unroll
+    for (int t = 0; t < KTT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = 16 * t + 4 * gq + i;
+        const bool ok = pos < p.block && !(p.causal && pos > qrow) && ((anc >> pos) & 1u);
+        blk_seen |= unsigned(ok) << (4 * t + i);
+      }
+  }
 
   auto compute = [&](int st, const uint4 *kl) {
     const bool blk = st == n_ctx;
@@ -150,10 +167,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = 16 * t + 4 * gq + i;
-        // a causal pass lets block row qrow see block positions <= qrow only,
-        // a tree pass its ancestors and itself (row_mask bits)
-        bool seen = pos < nvalid && !(blk && p.causal && pos > qrow);
-        if (blk && p.row_mask) seen = seen && qrow < p.block && ((p.row_mask[s * p.block + qrow] >> pos) & 1u);
+        bool seen = pos < nvalid;
+        if constexpr (MASK) seen = blk ? ((blk_seen >> (4 * t + i)) & 1u) != 0 : seen;
         const float x = seen ? sacc[t][i] * p.scale_log2 : -INFINITY;
         sv[4 * t + i] = x;
         mx = fmaxf(mx, x);
@@ -300,15 +315,21 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
   }
 }
 
-template <typename T, int HD, int XS, int NW>
-static hipError_t launch_attn_nw(const AttnParams &p, int batch, int rc, int threads, hipStream_t s) {
+template <typename T, int HD, int XS, int NW, bool MASK>
+static hipError_t launch_attn_mask(const AttnParams &p, int batch, int rc, int threads, hipStream_t s) {
   const dim3 grid(p.splits, p.n_kv * p.head_split, batch * p.q_tiles), block(threads);
-  if (rc <= 2) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 2, NW>), grid, block, 0, s, p);
-  else if (rc <= 4) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 4, NW>), grid, block, 0, s, p);
-  else if (rc <= 8) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 8, NW>), grid, block, 0, s, p);
-  else if (rc <= 16) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 16, NW>), grid, block, 0, s, p);
+  if (rc <= 2) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 2, NW, MASK>), grid, block, 0, s, p);
+  else if (rc <= 4) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 4, NW, MASK>), grid, block, 0, s, p);
+  else if (rc <= 8) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 8, NW, MASK>), grid, block, 0, s, p);
+  else if (rc <= 16) hipLaunchKernelGGL((attn_kernel<T, HD, XS, 16, NW, MASK>), grid, block, 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <typename T, int HD, int XS, int NW>
+static hipError_t launch_attn_nw(const AttnParams &p, int batch, int rc, int threads, hipStream_t s) {
+  if (p.causal || p.row_mask) return launch_attn_mask<T, HD, XS, NW, true>(p, batch, rc, threads, s);
+  return launch_attn_mask<T, HD, XS, NW, false>(p, batch, rc, threads, s);
 }
 
 template <typename T, int HD, int XS>

@@ -490,7 +490,9 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     else p.tile_m = blocks(mt, 12) * 12 < blocks(mt, 8) * 8 ? 12 : 8;
     p.n_blocks = blocks(p.n_tiles, 16);
   } else {
-    const bool big = blocks(p.M, 128) * blocks(p.n_tiles, 16) * 4 >= 3 * cu;
+    // (the rotary QKV epilogue keeps the 64 x 128 tile: at 128 x 256 its
+    // partner exchange does not fit the registers)
+    const bool big = EPI != EPI_QKV && blocks(p.M, 128) * blocks(p.n_tiles, 16) * 4 >= 3 * cu;
     p.tile_m = big ? 8 : 4;
     p.n_blocks = big ? blocks(p.n_tiles, 16) : blocks(p.n_tiles, 8);
   }
@@ -520,7 +522,8 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     }
   } else {
     if (HEAD && p.tile_m != 8) return hipErrorInvalidValue;
-    if (p.tile_m == 8) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
+    if constexpr (EPI == EPI_QKV) launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
+    else if (p.tile_m == 8) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
     else launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
   }
   return hipGetLastError();
