@@ -61,6 +61,10 @@ EXTRA_STEPS, EXTRA_WARMUP = 10, 3
 # Workloads that also time a temperature-1 step (sampled drafting and
 # speculative-sampling verification).
 SAMPLING_WORKLOADS = ("qwen3-8b-b1", "qwen3-8b-b32")
+# Multi-anchor drafting and the block-size policy are timed at batch 1.
+ANCHOR_WORKLOADS = ("qwen3-8b-b1",)
+ANCHOR_BLOCKS = (1, 2, 4, 8)
+POLICY_BLOCKS = (4, 8, 16)
 # Workloads that also time the 36-layer target's verify pass and an
 # autoregressive target step (the measured cost model).
 TARGET_WORKLOADS = ("qwen3-8b-b1", "qwen3-8b-b32")
@@ -230,6 +234,102 @@ def time_sampling(torch, dr, b, B, V, feats_t, cu, R, last_t, th, rewind, steps,
             "note": "inject + dflash_draft_sample + dflash_verify_sample; logits of both heads in HBM "
                     "(fp32), uniforms generated on the device before timing; includes one rewind of the "
                     "context lengths per step"}
+
+
+def time_anchors(torch, dr, d, b, ctx, last, steps):
+    """Drafting over several anchored blocks of one sequence per call
+    (dflash_draft_anchors): the frontier block and blocks anchored 16, 32,
+    ... positions before it, each attending to the context before its anchor.
+    Every block of a call shares the one weight stream, so the pass time grows
+    far slower than the block count."""
+    dev = dr.device
+    es = 2 if d.dtype == "bf16" else 4
+    H, hd, V = d.hidden, d.head_dim, d.vocab
+    per_layer = (d.qkv_rows * H + H * d.n_q_heads * hd + 3 * d.intermediate * H) * es
+    out = {}
+    for A in ANCHOR_BLOCKS:
+        if A > dr.max_blocks:
+            continue
+        pos = [int(ctx[0]) - 16 * a for a in range(A)]
+        seq_t = torch.zeros(A, dtype=torch.int32, device=dev)
+        pos_t = torch.as_tensor(np.asarray(pos, dtype=np.int32)).to(dev)
+        tok_t = torch.full((A,), int(last[0]), dtype=torch.int32, device=dev)
+        o = torch.empty((A, d.block_size), dtype=torch.int32, device=dev)
+        for _ in range(3):
+            dr.draft_anchors(seq_t, pos_t, tok_t, o, A)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            dr.draft_anchors(seq_t, pos_t, tok_t, o, A)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        byts = d.n_layers * per_layer + V * H * es + sum(pos) * d.n_layers * 2 * d.n_kv_heads * hd * es
+        out[str(A)] = {"ms_per_call": round(ms, 4), "blocks_per_s": round(A * 1000.0 / ms, 1),
+                       "drafted_tokens_per_s": round(A * d.block_size * 1000.0 / ms, 1),
+                       "algorithmic_bytes": int(byts),
+                       "hbm_frac": round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+    return {"blocks": out, "anchors": "sequence 0; the frontier and anchors 16, 32, ... positions before it",
+            "note": "one dflash_draft_anchors call per timed pass (embedding, 5 layers, draft head with argmax); "
+                    "bytes = the drafter's layer weights and W_lm once plus each block's context K/V"}
+
+
+def time_block_policy(torch, dr, d, b, rows, feats_t, last_t, th, rewind, p_acc, seed, steps):
+    """Adaptive block size: the whole step (inject + draft + verify) timed at
+    each candidate B (injecting min(n, B + 1) rows per sequence, the most a
+    step of that size commits), then the policy's choice from the planted
+    accept lengths of 64 steps at B = 16."""
+    from block_diffusion_speculative_amd import inputs as I
+    from block_diffusion_speculative_amd.policy import BlockSizePolicy, expected_accept
+    dev = dr.device
+    Bmax = d.block_size
+    cu_h = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    times = {}
+    for Bc in POLICY_BLOCKS:
+        if Bc > Bmax:
+            continue
+        r_b = np.minimum(rows, Bc + 1)
+        idx = np.concatenate([np.arange(cu_h[s], cu_h[s] + r_b[s]) for s in range(b)])
+        f_b = feats_t[torch.as_tensor(idx).to(dev)].contiguous()
+        cu_b = torch.as_tensor(np.concatenate([[0], np.cumsum(r_b)]).astype(np.int32)).to(dev)
+        R_b = int(np.sum(r_b))
+        th_b = th[:, :Bc + 1].contiguous()
+        o = torch.empty((b, Bc), dtype=torch.int32, device=dev)
+        tg = torch.empty((b, Bc + 1), dtype=torch.int32, device=dev)
+        al = torch.empty(b, dtype=torch.int32, device=dev)
+        bo = torch.empty(b, dtype=torch.int32, device=dev)
+
+        def step():
+            rewind()
+            dr.inject(f_b, cu_b, b, R_b)
+            dr.draft(last_t, o, b, block_size=Bc)
+            dr.verify(th_b, o, tg, al, bo, b, block_size=Bc)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        times[Bc] = e0.elapsed_time(e1) / steps
+    pol = BlockSizePolicy(times, prior_steps=0.0)
+    for k in range(64):
+        pol.observe_many(I.planted_accept(seed, 1000 + k, b, p_acc, Bmax), Bmax)
+    p_hat = pol.p_hat()
+    per_b = {str(Bc): {"ms_per_step": round(t, 4),
+                       "committed_tokens_per_s": round(b * (expected_accept(p_acc, Bc) + 1.0) * 1000.0 / t, 1)}
+             for Bc, t in times.items()}
+    return {"per_block_size": per_b, "p_planted": round(p_acc, 5), "p_estimated": round(p_hat, 5),
+            "chosen_block_size": pol.choose(),
+            "note": "committed tokens/s = batch x (E[min(G, B)] + 1) / step time at the planted geometric p; "
+                    "the choice maximises the same rate at the p estimated from 64 planted steps at B = 16; "
+                    "each step includes one rewind of the context lengths"}
 
 
 def device_target_weights(torch, td, seed, dev):
@@ -430,7 +530,9 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
 
     dev = torch.device("cuda:0")
     t0 = time.time()
-    dr_gpu = Drafter(d, weights, b, cap, int(max(17 * b, np.sum(rows))), device=dev)
+    n4 = getattr(args, "anchor_steps", 0) > 0 and name in ANCHOR_WORKLOADS and not block
+    dr_gpu = Drafter(d, weights, b, cap, int(max(17 * b, np.sum(rows))), device=dev,
+                     max_blocks=max(ANCHOR_BLOCKS) if n4 else 0)
     dr_gpu.kv_import(upload(k_plain.reshape(-1, d.head_dim), dr_gpu.dt, dev).reshape(shape),
                      upload(v_plain.reshape(-1, d.head_dim), dr_gpu.dt, dev).reshape(shape))
     del k_plain, v_plain
@@ -517,7 +619,6 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
     torch.cuda.synchronize()
     verify_samples = verify_in_region + [a.elapsed_time(e) for a, e in zip(pv0, pv1)]
     verify_ms = float(np.mean(verify_samples))
-    status = dr_gpu.read_status()
 
     measured_cost = None
     if getattr(args, "target_steps", 0) > 0 and name in TARGET_WORKLOADS:
@@ -527,6 +628,12 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
     if getattr(args, "sampling_steps", 0) > 0 and name in SAMPLING_WORKLOADS:
         sampled = time_sampling(torch, dr_gpu, b, B, d.vocab, feats_t, cu, R, last_t, th, rewind,
                                 args.sampling_steps, ms_step)
+    anchors = policy = None
+    if n4:
+        anchors = time_anchors(torch, dr_gpu, d, b, ctx, last, args.anchor_steps)
+        policy = time_block_policy(torch, dr_gpu, d, b, rows, feats_t, last_t, th, rewind, p_acc, seed,
+                                   args.anchor_steps)
+    status = dr_gpu.read_status()
     got_draft = draft_out.cpu().numpy()
     got_acc = acc.cpu().numpy()
     parity = None
@@ -622,6 +729,8 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
                    ("oracle draft (sequence 0), random tokens elsewhere" if cpu_leg == "one" else "random tokens")},
         "draft_parity": parity,
         "sampling_T1": sampled,
+        "multi_anchor": anchors,
+        "block_policy": policy,
         "status": status,
     }
 
@@ -645,6 +754,9 @@ def main(argv=None):
                     help="timed temperature-1 steps on the batch-1 and batch-32 workloads (0: none)")
     ap.add_argument("--target-steps", type=int, default=10,
                     help="timed passes of the 36-layer target on the batch-1 and batch-32 workloads (0: none)")
+    ap.add_argument("--anchor-steps", type=int, default=10,
+                    help="timed multi-anchor drafting passes and block-size policy steps per size on the "
+                         "batch-1 workload (0: none)")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the headline workload only")
     ap.add_argument("--extras", default="",

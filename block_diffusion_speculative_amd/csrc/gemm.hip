@@ -326,8 +326,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     }
     return r;
   };
-  auto mma_tile = [&](int u, int b, const uint4 (&w)[U][NB], const uint4 (&x)[MT][XS], int mblk) {
-    const bool ok = k0 + b * U + u < k1;
+  // chk: zero the weights of k-tiles past the wavefront's chunk (a chunk of
+  // exactly the resident length needs no check).
+  auto mma_tile = [&](int u, int b, const uint4 (&w)[U][NB], const uint4 (&x)[MT][XS], int mblk, bool chk = true) {
+    const bool ok = !chk || k0 + b * U + u < k1;
     bool row_ok[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) row_ok[mt] = !XROW || (mblk * MT + mt) * 16 + (lane & 15) < p.M;
@@ -472,14 +474,37 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   zero_acc();
   if constexpr (XRES) {
     constexpr int NBAT = KC / U;
+    // A wavefront whose chunk is exactly KC k-tiles long (every chunk of the
+    // drafter's shapes) addresses its weights through a resource based at
+    // the chunk start: every load offset is then a compile-time constant, so
+    // no per-k-tile offsets occupy (and spill out of) the scalar registers.
+    // Other chunks clamp their k-tile indices into the chunk.
+    const bool exact = NB <= 2 && k1 - k0 == KC;
+    auto w_rsrc_chunk = [&](int item) {
+      const int nt0 = (item % p.n_blocks) * NB;
+      const int seg = nt0 / p.seg_ntiles;
+      const char *base = uniform_ptr(p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride +
+                                     size_t(k0) * NB * 1024);
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, KC * NB * 1024, BUF_DWORD3);
+    };
+    auto body = [&](auto ex) {
+    constexpr bool EX = decltype(ex)::value;
     WBatch<U, NB> wb[2];
     auto issue_w = [&](int item, int b, WBatch<U, NB> &f) {
-      const auto rs = w_rsrc(item);
+      if constexpr (EX) {
+        const auto rs = w_rsrc_chunk(item);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kt = min(k0 + b * U + u, kclamp);
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
+          for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, ((b * U + u) * NB + nb) * 1024);
+      } else {
+        const auto rs = w_rsrc(item);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kt = min(k0 + b * U + u, kclamp);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
+        }
       }
     };
     rs_issue();
@@ -525,7 +550,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0);
+        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, !EX);
       }
       finish_item(item);
     }
@@ -538,10 +563,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         else issue_w(next, 0, wb[0]);
         __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0);
+        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, !EX);
       }
       finish_item(item);
     }
+    };
+    if (exact) body(std::integral_constant<bool, true>{});
+    else body(std::integral_constant<bool, false>{});
   } else {
     // Activations stream with the weights; two batches in flight.
     XWBatch<U, MT, NB, XS> fa, fb;
