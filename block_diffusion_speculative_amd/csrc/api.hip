@@ -164,9 +164,10 @@ DraftLayout draft_layout(const dflash_dims *d, int batch, int rows = 0, bool tar
   L.rs_inline = gemm_inline_rs_ok(L.qkv.m_blocks, L.qkv.MT, H);
   L.part = L.M > STEP_TILED_MIN_ROWS ? b.take(SPLIT_PART_BYTES) : 0;
   L.anc = b.take(size_t(2) * MAX_BATCH * 4);   // anchored blocks: checked context lengths, cache regions
-  // draft trees: per slot row the log-sum-exp, its chunk partials and the
-  // top-K (value, index); target tree passes: per row depth and ancestor mask
-  L.tree = b.take(size_t(L.M) * (4 + ARGMAX_SLOTS * 8 + 8 * 8) + size_t(L.M) * 8);
+  // draft trees: per slot row the log-sum-exp, its chunk partials, the
+  // top-K (value, index) and the top-K chunk keys; target tree passes: per
+  // row depth and ancestor mask
+  L.tree = b.take(size_t(L.M) * (4 + ARGMAX_SLOTS * 8 + 8 * 8 + TOPK_CHUNKS * 8 * 8) + size_t(L.M) * 8);
   L.end = b.off;
   return L;
 }
@@ -1079,8 +1080,9 @@ int dflash_draft_tree(const dflash_dims *d, const dflash_weights *w, const dflas
   float2 *part = reinterpret_cast<float2 *>(lse + rows);
   float *tv = reinterpret_cast<float *>(part + size_t(rows) * ARGMAX_SLOTS);
   int *ti = reinterpret_cast<int *>(tv + size_t(rows) * 8);
+  auto *ck = reinterpret_cast<unsigned long long *>(ti + size_t(rows) * 8);
   hipError_t e = launch_row_lse(draft_logits, V, V, 1.0f, rows, ch, part, lse, stream);
-  if (e == hipSuccess) e = launch_row_topk(draft_logits, V, V, rows, topk, lse, tv, ti, stream);
+  if (e == hipSuccess) e = launch_row_topk(draft_logits, V, V, rows, topk, lse, ck, tv, ti, stream);
   if (e == hipSuccess)
     e = launch_tree_build(tv, ti, last_tok, batch, d->block_size, topk, nodes, tree_tok, tree_parent, stream);
   return e == hipSuccess ? DFLASH_OK : hip_fail(e, "draft tree");

@@ -224,12 +224,16 @@ hipError_t launch_row_lse(const float *logits, int ld, int vocab, float inv_t, i
                           float *lse, hipStream_t s);
 hipError_t launch_spec_sample(const SampleParams &p, int batch, hipStream_t s);
 
+// Vocabulary chunks per row of the top-K (its first launch); the workspace
+// holds TOPK_CHUNKS * K keys per row for the second.
+constexpr int TOPK_CHUNKS = 32;
+
 // Draft trees (tree.hip).
 // Per row of logits, the K most probable entries as (log-probability,
 // index), highest first (lowest index on ties): topk_val / topk_idx
 // [rows][K]; lse[row] the row's log-sum-exp.
 hipError_t launch_row_topk(const float *logits, int ld, int vocab, int rows, int K, const float *lse,
-                           float *topk_val, int *topk_idx, hipStream_t s);
+                           unsigned long long *chunk_keys, float *topk_val, int *topk_idx, hipStream_t s);
 // Best-first trees, one per sequence: from the top-K of its B slots
 // (rows s * B + j), N nodes after the anchor; tree_tok / tree_parent
 // [batch][N + 1].

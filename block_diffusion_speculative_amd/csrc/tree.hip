@@ -23,29 +23,17 @@ constexpr int TREE_MAX_K = 8;
 constexpr int TREE_MAX_NODES = 32;   // N + 1 rows of one target pass
 constexpr int TOPK_THREADS = 256;
 
-// Top-K keys of one row: every thread keeps its K best (logit, index) keys
-// over its strided elements, then K rounds of a workgroup max extract them in
-// order (the owner of each extracted key moves to its next one).
-__global__ __launch_bounds__(TOPK_THREADS) void row_topk_kernel(const float *logits, int ld, int vocab, int K,
-                                                                 const float *lse, float *topk_val, int *topk_idx) {
-  __shared__ unsigned long long part[TOPK_THREADS / 64];
-  __shared__ int owner_sh;
-  const int row = blockIdx.x;
-  const float *lg = logits + size_t(row) * ld;
-  unsigned long long best[TREE_MAX_K];
-#pragma unroll
-  for (int i = 0; i < TREE_MAX_K; ++i) best[i] = 0;
-  for (int v = threadIdx.x; v < vocab; v += TOPK_THREADS) {
-    unsigned long long k = argmax_key(lg[v], v);
-#pragma unroll
-    for (int i = 0; i < TREE_MAX_K; ++i) {   // insertion into a sorted list
-      if (i < K && k > best[i]) {
-        const unsigned long long t = best[i];
-        best[i] = k;
-        k = t;
-      }
-    }
-  }
+// Top-K keys per row (64-bit (logit, index) keys: larger logit first, then
+// lower index), in two launches so that a row's vocabulary is read by many
+// workgroups: row_topk_part_kernel takes the K best keys of each of
+// TOPK_CHUNKS vocabulary chunks of a row, row_topk_merge_kernel the K best of
+// a row's TOPK_CHUNKS * K chunk keys.  Keys are unique, so the result is the
+// row's exact top-K in key order.
+// K rounds of a workgroup max over the threads' sorted key lists (each
+// thread's keys in best[0 .. K), best first; 0 marks no key): round r
+// writes the r-th best key of the workgroup to out[r] (thread 0).
+__device__ inline void wg_extract_topk(const unsigned long long (&best)[TREE_MAX_K], int K, unsigned long long *out,
+                                       unsigned long long *part, int *owner_sh) {
   int head = 0;   // this thread's next unextracted key
   for (int r = 0; r < K; ++r) {
     unsigned long long mine = 0;
@@ -63,29 +51,81 @@ __global__ __launch_bounds__(TOPK_THREADS) void row_topk_kernel(const float *log
     k = part[0];
 #pragma unroll
     for (int w = 1; w < TOPK_THREADS / 64; ++w) k = part[w] > k ? part[w] : k;
-    if (k != 0 && mine == k) owner_sh = threadIdx.x;   // keys are unique (the index is part of it)
+    if (k != 0 && mine == k) *owner_sh = threadIdx.x;
     __syncthreads();
-    if (int(threadIdx.x) == owner_sh && k != 0) ++head;
-    if (threadIdx.x == 0) {
-      // K <= vocab, so every round extracts a real key
-      const int idx = min(max(key_index(k), 0), vocab - 1);
-      topk_idx[row * K + r] = idx;
-      topk_val[row * K + r] = lg[idx] - lse[row];
+    if (int(threadIdx.x) == *owner_sh && k != 0) ++head;
+    if (threadIdx.x == 0) out[r] = k;
+    __syncthreads();
+  }
+}
+
+__device__ inline void topk_insert(unsigned long long (&best)[TREE_MAX_K], int K, unsigned long long k) {
+#pragma unroll
+  for (int i = 0; i < TREE_MAX_K; ++i) {   // insertion into a sorted list
+    if (i < K && k > best[i]) {
+      const unsigned long long t = best[i];
+      best[i] = k;
+      k = t;
     }
-    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void row_topk_part_kernel(const float *logits, int ld, int vocab, int K,
+                                                                      unsigned long long *chunk_keys) {
+  __shared__ unsigned long long part[TOPK_THREADS / 64];
+  __shared__ unsigned long long out[TREE_MAX_K];
+  __shared__ int owner_sh;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int len = (vocab + TOPK_CHUNKS - 1) / TOPK_CHUNKS;
+  const int v0 = c * len, v1 = min(v0 + len, vocab);
+  const float *lg = logits + size_t(row) * ld;
+  unsigned long long best[TREE_MAX_K];
+#pragma unroll
+  for (int i = 0; i < TREE_MAX_K; ++i) best[i] = 0;
+  for (int v = v0 + int(threadIdx.x); v < v1; v += TOPK_THREADS) topk_insert(best, K, argmax_key(lg[v], v));
+  wg_extract_topk(best, K, out, part, &owner_sh);
+  if (int(threadIdx.x) < K) chunk_keys[(size_t(row) * TOPK_CHUNKS + c) * K + threadIdx.x] = out[threadIdx.x];
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void row_topk_merge_kernel(const float *logits, int ld, int vocab, int K,
+                                                                       const unsigned long long *chunk_keys,
+                                                                       const float *lse, float *topk_val,
+                                                                       int *topk_idx) {
+  __shared__ unsigned long long part[TOPK_THREADS / 64];
+  __shared__ unsigned long long out[TREE_MAX_K];
+  __shared__ int owner_sh;
+  const int row = blockIdx.x;
+  unsigned long long best[TREE_MAX_K];
+#pragma unroll
+  for (int i = 0; i < TREE_MAX_K; ++i) best[i] = 0;
+  for (int i = threadIdx.x; i < TOPK_CHUNKS * K; i += TOPK_THREADS)
+    topk_insert(best, K, chunk_keys[size_t(row) * TOPK_CHUNKS * K + i]);
+  wg_extract_topk(best, K, out, part, &owner_sh);
+  if (int(threadIdx.x) < K) {
+    // K <= vocab, so every round extracts a real key
+    const int idx = min(max(key_index(out[threadIdx.x]), 0), vocab - 1);
+    topk_idx[row * K + threadIdx.x] = idx;
+    topk_val[row * K + threadIdx.x] = logits[size_t(row) * ld + idx] - lse[row];
   }
 }
 
 // One thread per sequence: the best-first heap over (score, depth, rank,
 // parent node); ties go to the smaller depth, then to the smaller rank.
-__global__ void tree_build_kernel(const float *topk_val, const int *topk_idx, const int *anchor, int batch, int B,
-                                  int K, int N, int *tree_tok, int *tree_parent) {
+// Each thread's heap and node scores live in LDS (a private array indexed
+// at run time would live in scratch memory).
+constexpr int TREE_THREADS = 64;
+struct TreeCand { float score; int depth, rank, parent; };
+
+__global__ __launch_bounds__(TREE_THREADS) void tree_build_kernel(const float *topk_val, const int *topk_idx,
+                                                                  const int *anchor, int batch, int B, int K, int N,
+                                                                  int *tree_tok, int *tree_parent) {
+  __shared__ TreeCand heap_sh[2 * TREE_MAX_NODES + 2][TREE_THREADS];
+  __shared__ float nscore_sh[TREE_MAX_NODES][TREE_THREADS];
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= batch) return;
-  struct Cand { float score; int depth, rank, parent; };
-  Cand heap[2 * TREE_MAX_NODES + 2];
-  float nscore[TREE_MAX_NODES];
-  int ndepth[TREE_MAX_NODES];
+  using Cand = TreeCand;
+  auto heap_at = [&](int i) -> Cand & { return heap_sh[i][threadIdx.x]; };
+  auto nscore = [&](int i) -> float & { return nscore_sh[i][threadIdx.x]; };
   int hn = 0;
   auto better = [](const Cand &a, const Cand &b) {
     if (a.score != b.score) return a.score > b.score;
@@ -96,25 +136,25 @@ __global__ void tree_build_kernel(const float *topk_val, const int *topk_idx, co
     int i = hn++;
     while (i > 0) {
       const int pi = (i - 1) / 2;
-      if (!better(c, heap[pi])) break;
-      heap[i] = heap[pi];
+      if (!better(c, heap_at(pi))) break;
+      heap_at(i) = heap_at(pi);
       i = pi;
     }
-    heap[i] = c;
+    heap_at(i) = c;
   };
   auto pop = [&]() {
-    const Cand top = heap[0];
-    const Cand last = heap[--hn];
+    const Cand top = heap_at(0);
+    const Cand last = heap_at(--hn);
     int i = 0;
     while (true) {
       int c = 2 * i + 1;
       if (c >= hn) break;
-      if (c + 1 < hn && better(heap[c + 1], heap[c])) ++c;
-      if (!better(heap[c], last)) break;
-      heap[i] = heap[c];
+      if (c + 1 < hn && better(heap_at(c + 1), heap_at(c))) ++c;
+      if (!better(heap_at(c), last)) break;
+      heap_at(i) = heap_at(c);
       i = c;
     }
-    if (hn > 0) heap[i] = last;
+    if (hn > 0) heap_at(i) = last;
     return top;
   };
   const float *val = topk_val + size_t(s) * B * K;
@@ -123,8 +163,7 @@ __global__ void tree_build_kernel(const float *topk_val, const int *topk_idx, co
   int *par = tree_parent + size_t(s) * (N + 1);
   tok[0] = anchor[s];
   par[0] = -1;
-  nscore[0] = 0.f;
-  ndepth[0] = 0;
+  nscore(0) = 0.f;
   push(Cand{val[0], 1, 0, 0});
   int nodes = 1;
   while (hn > 0 && nodes < N + 1) {
@@ -132,9 +171,8 @@ __global__ void tree_build_kernel(const float *topk_val, const int *topk_idx, co
     const int node = nodes++;
     tok[node] = idx[(c.depth - 1) * K + c.rank];
     par[node] = c.parent;
-    nscore[node] = c.score;
-    ndepth[node] = c.depth;
-    if (c.rank + 1 < K) push(Cand{nscore[c.parent] + val[(c.depth - 1) * K + c.rank + 1], c.depth, c.rank + 1, c.parent});
+    nscore(node) = c.score;
+    if (c.rank + 1 < K) push(Cand{nscore(c.parent) + val[(c.depth - 1) * K + c.rank + 1], c.depth, c.rank + 1, c.parent});
     if (c.depth < B) push(Cand{c.score + val[c.depth * K], c.depth + 1, 0, node});
   }
   for (; nodes < N + 1; ++nodes) {   // fewer continuations than N: a chain of repeats is never produced
@@ -143,29 +181,32 @@ __global__ void tree_build_kernel(const float *topk_val, const int *topk_idx, co
   }
 }
 
-__global__ void tree_prep_kernel(const int *parent, int batch, int n, int *depth, unsigned *mask, unsigned *status) {
+__global__ __launch_bounds__(TREE_THREADS) void tree_prep_kernel(const int *parent, int batch, int n, int *depth,
+                                                                 unsigned *mask, unsigned *status) {
+  __shared__ int dep_sh[TREE_MAX_NODES][TREE_THREADS];
+  __shared__ unsigned msk_sh[TREE_MAX_NODES][TREE_THREADS];
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= batch) return;
   const int *par = parent + size_t(s) * n;
-  int dep[TREE_MAX_NODES];
-  unsigned msk[TREE_MAX_NODES];
+  auto dep = [&](int i) -> int & { return dep_sh[i][threadIdx.x]; };
+  auto msk = [&](int i) -> unsigned & { return msk_sh[i][threadIdx.x]; };
   bool bad = false;
   for (int i = 0; i < n; ++i) {
     int pi = par[i];
     if (i == 0) {
       bad = bad || pi != -1;
-      dep[0] = 0;
-      msk[0] = 1u;
+      dep(0) = 0;
+      msk(0) = 1u;
     } else {
       if (pi < 0 || pi >= i) {
         bad = true;
         pi = i - 1;
       }
-      dep[i] = dep[pi] + 1;
-      msk[i] = msk[pi] | (1u << i);
+      dep(i) = dep(pi) + 1;
+      msk(i) = msk(pi) | (1u << i);
     }
-    depth[s * n + i] = dep[i];
-    mask[s * n + i] = msk[i];
+    depth[s * n + i] = dep(i);
+    mask[s * n + i] = msk(i);
   }
   if (bad) atomicOr(status, DFLASH_STATUS_TREE);
 }
@@ -233,17 +274,20 @@ __global__ void commit_len_kernel(int *ctx_len, const int *accept_len, int batch
 }
 
 hipError_t launch_row_topk(const float *logits, int ld, int vocab, int rows, int K, const float *lse,
-                           float *topk_val, int *topk_idx, hipStream_t s) {
-  if (K < 1 || K > TREE_MAX_K) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(row_topk_kernel, dim3(rows), dim3(TOPK_THREADS), 0, s, logits, ld, vocab, K, lse, topk_val,
-                     topk_idx);
+                           unsigned long long *chunk_keys, float *topk_val, int *topk_idx, hipStream_t s) {
+  if (K < 1 || K > TREE_MAX_K || TOPK_CHUNKS * K > TOPK_THREADS * TREE_MAX_K) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_topk_part_kernel, dim3(TOPK_CHUNKS, rows), dim3(TOPK_THREADS), 0, s, logits, ld, vocab, K,
+                     chunk_keys);
+  hipLaunchKernelGGL(row_topk_merge_kernel, dim3(rows), dim3(TOPK_THREADS), 0, s, logits, ld, vocab, K, chunk_keys,
+                     lse, topk_val, topk_idx);
   return hipGetLastError();
 }
 
 hipError_t launch_tree_build(const float *topk_val, const int *topk_idx, const int *anchor, int batch, int B,
                              int K, int N, int *tree_tok, int *tree_parent, hipStream_t s) {
   if (K < 1 || K > TREE_MAX_K || N < 1 || N + 1 > TREE_MAX_NODES) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tree_build_kernel, dim3((batch + 63) / 64), dim3(64), 0, s, topk_val, topk_idx, anchor, batch,
+  hipLaunchKernelGGL(tree_build_kernel, dim3((batch + TREE_THREADS - 1) / TREE_THREADS), dim3(TREE_THREADS), 0, s,
+                     topk_val, topk_idx, anchor, batch,
                      B, K, N, tree_tok, tree_parent);
   return hipGetLastError();
 }
@@ -251,7 +295,8 @@ hipError_t launch_tree_build(const float *topk_val, const int *topk_idx, const i
 hipError_t launch_tree_prep(const int *parent, int batch, int n, int *depth, unsigned *mask, unsigned *status,
                             hipStream_t s) {
   if (n < 1 || n > TREE_MAX_NODES) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tree_prep_kernel, dim3((batch + 63) / 64), dim3(64), 0, s, parent, batch, n, depth, mask, status);
+  hipLaunchKernelGGL(tree_prep_kernel, dim3((batch + TREE_THREADS - 1) / TREE_THREADS), dim3(TREE_THREADS), 0, s,
+                     parent, batch, n, depth, mask, status);
   return hipGetLastError();
 }
 
