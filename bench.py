@@ -51,8 +51,11 @@ CPU_SAMPLE_MAX = 20
 # the skinny GEMM's).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_verify_head_{}.md")
 TRAFFIC_SOURCES = ["gemm.hip", "gemm_util.hpp", "common.hpp", "kernels.hpp", "api.hip"]
-# Draft and verify GEMMs of more rows than this run on the tiled kernel (the
-# library's routing rule; a CPU test pins both sides of it).
+# The library's routing rule for the heads (a CPU test pins both sides of
+# it): skinny up to HEAD_TILED_MIN_ROWS rows while two row tiles of
+# activations fit the registers (k chunks of at most 16 tiles of 32 bf16
+# columns per wavefront, i.e. hidden <= 4096), else up to STEP_TILED_MIN_ROWS.
+HEAD_TILED_MIN_ROWS = 32
 STEP_TILED_MIN_ROWS = 17
 # Workloads timed after the headline one: (name, block size), fewer steps.
 EXTRAS = [("qwen3-8b-b32", 16), ("qwen3-8b-long", 16), ("larger-b8", 4), ("larger-b8", 8),
@@ -162,10 +165,12 @@ def blas_threads():
         return 1
 
 
-def head_kernel_label(lm_rows: int) -> str:
-    """The kernels that run the verify head at this many rows (the library's
-    skinny/tiled routing rule)."""
-    if lm_rows > STEP_TILED_MIN_ROWS:
+def head_kernel_label(lm_rows: int, hidden: int = 4096) -> str:
+    """The kernels that run the verify head at this many rows and this bf16
+    hidden size (the library's skinny/tiled routing rule)."""
+    k_tiles = (hidden + 31) // 32
+    limit = HEAD_TILED_MIN_ROWS if (k_tiles + 7) // 8 <= 16 else STEP_TILED_MIN_ROWS
+    if lm_rows > limit:
         return ("gemm_tiled_kernel<bf16, ARGMAX> + argmax_finish_kernel "
                 "(verify lm_head + argmax, then the accept scan)")
     return "gemm_kernel<bf16, ARGMAX> (verify lm_head + argmax + accept)"
@@ -656,7 +661,7 @@ def run_workload(args, torch, name: str, block: int, steps: int, warmup: int, cp
     # its MFMA work at peak (few rows), MFMA otherwise.
     lm_t_hbm = lm_bytes / (HBM_PEAK_GBS * 1e9)
     lm_t_mfma = lm_flops / (BF16_PEAK_TFLOPS * 1e12)
-    lm_kernel = head_kernel_label(lm_rows)
+    lm_kernel = head_kernel_label(lm_rows, d.hidden)
     traffic_key = name if not block or block == max(w.block_sizes) else f"{name}-B{block}"
     if lm_t_mfma > lm_t_hbm:
         ach = lm_flops / (verify_ms * 1e-3) / 1e12

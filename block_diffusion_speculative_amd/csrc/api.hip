@@ -36,13 +36,17 @@ constexpr int MAX_TARGET_LAYERS = 128;
 // Launches of more rows than these use the tiled kernel: from two row tiles
 // on, the skinny kernel's activation stream per item (every row tile and
 // plane through each workgroup) outweighs the tiled kernel's LDS traffic and
-// split-K partial tiles.  The draft and verify GEMMs switch above 17 rows
-// (one sequence's 16 draft and 17 verify rows stay skinny).  The injection
+// split-K partial tiles.  The draft and verify layer GEMMs switch above 17
+// rows (one sequence's 16 draft and 17 verify rows stay skinny).  The injection
 // GEMMs stay skinny up to 32 rows: there the skinny kernel's summation order
 // is the same for every row count, so an injection split over two such calls
 // writes the same cache bits as one call.
 constexpr int STEP_TILED_MIN_ROWS = 17;
 constexpr int INJECT_TILED_MIN_ROWS = 32;
+// The heads (one activation plane) stay skinny up to 32 rows when two row
+// tiles of their activations fit the registers (k chunks of at most 16
+// tiles: hidden <= 4096 in bf16); otherwise they switch with the layer GEMMs.
+constexpr int HEAD_TILED_MIN_ROWS = 32;
 
 struct GemmPlan {
   int M, N, K;
@@ -68,6 +72,12 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int nb, int tiled_above) {
   g.n_blocks = (g.n_tiles + g.NB - 1) / g.NB;
   g.k_tiles = (K + kt - 1) / kt;
   return g;
+}
+
+GemmPlan plan_head(int dtype, int M, int vocab, int hidden) {
+  const int k_tiles = (hidden + kt_of(dtype) - 1) / kt_of(dtype);
+  const bool resident = gemm_resident_ok(1, 2, 1, k_tiles);
+  return plan_gemm(dtype, M, vocab, hidden, 2, resident ? HEAD_TILED_MIN_ROWS : STEP_TILED_MIN_ROWS);
 }
 
 // Context splits of the block attention: about half a workgroup per compute
@@ -138,7 +148,7 @@ DraftLayout draft_layout(const dflash_dims *d, int batch, int rows = 0, bool tar
   L.o = plan_gemm(d->dtype, L.M, H, NQD, 1, STEP_TILED_MIN_ROWS);
   L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2, STEP_TILED_MIN_ROWS);
   L.down = plan_gemm(d->dtype, L.M, H, I, 1, STEP_TILED_MIN_ROWS);
-  L.lm = plan_gemm(d->dtype, L.M, d->vocab, H, 2, STEP_TILED_MIN_ROWS);
+  L.lm = plan_head(d->dtype, L.M, d->vocab, H);
   // packed activations hold whole row blocks (the GEMMs load them unguarded)
   L.Mp = L.qkv.m_blocks * L.qkv.MT * 16;
   Bump b;
@@ -181,7 +191,7 @@ struct VerifyLayout {
 // the log-sum-exp of its batch * (2B + 1) logit rows.
 VerifyLayout verify_layout(const dflash_dims *d, int batch, bool sampling = false) {
   VerifyLayout L{};
-  L.lm = plan_gemm(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden, 2, STEP_TILED_MIN_ROWS);
+  L.lm = plan_head(d->dtype, batch * (d->block_size + 1), d->vocab, d->hidden);
   Bump b;
   L.lse = sampling ? b.take(size_t(batch) * (2 * d->block_size + 1) * 4) : 0;
   // chunk partials of the log-sum-exp (one float2 per row and chunk)
@@ -1107,7 +1117,7 @@ int dflash_tree_accept(const dflash_dims *d, const void *lm_head, const void *ta
   if (ws_bytes < WS_COUNTER_BYTES) return fail(DFLASH_ERR_WORKSPACE, "workspace smaller than its counter area");
   char *wsb = static_cast<char *>(ws);
   GemmParams lm{};
-  fill_gemm(lm, plan_gemm(d->dtype, batch * n, d->vocab, d->hidden, 2, STEP_TILED_MIN_ROWS));
+  fill_gemm(lm, plan_head(d->dtype, batch * n, d->vocab, d->hidden));
   lm.w_seg[0] = static_cast<const char *>(lm_head);
   lm.x = static_cast<const char *>(target_hidden);
   lm.x_ld = d->hidden;

@@ -94,14 +94,23 @@ def test_block_size_outside_the_sweep_is_refused():
 
 
 def test_head_label_follows_the_routing_rule():
-    """The verify head runs skinny up to 17 rows (one sequence at B = 16) and
-    tiled above: 40 rows (hidden-5120 drafter, batch 8, B = 4) is tiled."""
-    assert bench.STEP_TILED_MIN_ROWS == 17
+    """The heads run skinny up to 32 rows while two row tiles of activations
+    fit the registers (hidden 4096: one sequence's 17 verify rows, two
+    anchored blocks) and tiled above (34 rows, two sequences' verify rows);
+    at hidden 5120 they switch above 17 rows (40 verify rows of the batch-8,
+    B = 4 workload are tiled, and so are 32)."""
+    assert bench.HEAD_TILED_MIN_ROWS == 32 and bench.STEP_TILED_MIN_ROWS == 17
     assert bench.head_kernel_label(17).startswith("gemm_kernel<")
-    assert bench.head_kernel_label(18).startswith("gemm_tiled_kernel<")
-    assert bench.head_kernel_label(40).startswith("gemm_tiled_kernel<")
+    assert bench.head_kernel_label(32).startswith("gemm_kernel<")
+    assert bench.head_kernel_label(34).startswith("gemm_tiled_kernel<")
+    assert bench.head_kernel_label(17, 5120).startswith("gemm_kernel<")
+    assert bench.head_kernel_label(32, 5120).startswith("gemm_tiled_kernel<")
+    assert bench.head_kernel_label(40, 5120).startswith("gemm_tiled_kernel<")
     api = open(os.path.join(ROOT, "block_diffusion_speculative_amd", "csrc", "api.hip")).read()
+    assert "constexpr int HEAD_TILED_MIN_ROWS = 32;" in api
     assert "constexpr int STEP_TILED_MIN_ROWS = 17;" in api
+    hpp = open(os.path.join(ROOT, "block_diffusion_speculative_amd", "csrc", "kernels.hpp")).read()
+    assert "(MT * planes <= 2 && per <= 16)" in hpp
 
 
 def test_extras_default_list_covers_the_measured_workloads():
