@@ -74,6 +74,24 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int nb, int tiled_above) {
   return g;
 }
 
+int compute_units();
+
+// Draft, verify and target layer GEMMs: skinny up to 17 rows; at 18-32 rows
+// (two row tiles) skinny when its items fill at least half of their last
+// round on the compute units (one item per workgroup at a time; a short last
+// round leaves the skinny kernel's two-row-tile items, which stream their
+// activations, less balanced than the tiled kernel's split-K parts), else
+// tiled.
+GemmPlan plan_layer(int dtype, int M, int N, int K, int nb) {
+  GemmPlan g = plan_gemm(dtype, M, N, K, nb, STEP_TILED_MIN_ROWS);
+  if (g.tiled && M <= 32) {
+    const int cu = compute_units();
+    const int rem = g.n_blocks % cu;
+    if (rem == 0 || 2 * rem >= cu) g.tiled = false;
+  }
+  return g;
+}
+
 GemmPlan plan_head(int dtype, int M, int vocab, int hidden) {
   const int k_tiles = (hidden + kt_of(dtype) - 1) / kt_of(dtype);
   const bool resident = gemm_resident_ok(1, 2, 1, k_tiles);
@@ -144,10 +162,10 @@ DraftLayout draft_layout(const dflash_dims *d, int batch, int rows = 0, bool tar
   L.q_tiles = (L.rows + 15) / 16;
   L.M = batch * L.rows;
   L.S = attn_splits(d, batch * L.q_tiles);
-  L.qkv = plan_gemm(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1, STEP_TILED_MIN_ROWS);
-  L.o = plan_gemm(d->dtype, L.M, H, NQD, 1, STEP_TILED_MIN_ROWS);
-  L.gu = plan_gemm(d->dtype, L.M, 2 * I, H, 2, STEP_TILED_MIN_ROWS);
-  L.down = plan_gemm(d->dtype, L.M, H, I, 1, STEP_TILED_MIN_ROWS);
+  L.qkv = plan_layer(d->dtype, L.M, (d->n_q_heads + 2 * d->n_kv_heads) * hd, H, 1);
+  L.o = plan_layer(d->dtype, L.M, H, NQD, 1);
+  L.gu = plan_layer(d->dtype, L.M, 2 * I, H, 2);
+  L.down = plan_layer(d->dtype, L.M, H, I, 1);
   L.lm = plan_head(d->dtype, L.M, d->vocab, H);
   // packed activations hold whole row blocks (the GEMMs load them unguarded)
   L.Mp = L.qkv.m_blocks * L.qkv.MT * 16;
