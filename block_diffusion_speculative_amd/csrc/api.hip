@@ -1085,6 +1085,7 @@ int dflash_draft_tree(const dflash_dims *d, const dflash_weights *w, const dflas
                       int32_t batch, int32_t topk, int32_t nodes, float *draft_logits, int32_t *tree_tok,
                       int32_t *tree_parent, void *ws, size_t ws_bytes, hipStream_t stream) {
   TRY(check_dims(d));
+  if (batch < 1 || batch > MAX_BATCH) return fail(DFLASH_ERR_SHAPE, "batch must be in [1, 64]");
   if (topk < 1 || topk > 8) return fail(DFLASH_ERR_SHAPE, "topk must be in [1, 8]");
   if (nodes < 1 || nodes > 31) return fail(DFLASH_ERR_SHAPE, "nodes must be in [1, 31]");
   long long avail = 0, pw = 1;   // continuations of length 1 .. B over topk tokens per slot

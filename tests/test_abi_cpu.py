@@ -135,3 +135,100 @@ def test_kv_and_inject_validation(lib):
     # zero rows: nothing to do
     layers[2] = _lib.Layer(16, 16, 16, 16, 16, 16)
     assert lib.dflash_inject_kv(ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), None, 16, 1, 0, 16, big, None) == 0
+
+
+def _drafter_structs(n_layers=5, capacity=2080, max_batch=1):
+    layers = (_lib.Layer * n_layers)()
+    for i in range(n_layers):
+        layers[i] = _lib.Layer(16, 16, 16, 16, 16, 16)
+    w = _lib.Weights(16, 16, 16, 16, 16, ctypes.cast(layers, ctypes.POINTER(_lib.Layer)))
+    kv = _lib.KV(16, 16, 16, 16, capacity, max_batch)
+    return layers, w, kv
+
+
+def test_target_pass_validation(lib):
+    """dflash_target_forward rejects bad row counts, feature layers, batches
+    and workspaces before any HIP call; dflash_target_workspace_bytes is 0
+    outside its ranges."""
+    td = cdims(C.QWEN3_8B_TARGET)
+    layers, w, kv = _drafter_structs(36, 4096, 2)
+    big = 1 << 40
+    fl = (ctypes.c_int32 * 3)(5, 11, 17)
+    call = lambda batch, rows, feats, n, ws=big: lib.dflash_target_forward(
+        ctypes.byref(td), ctypes.byref(w), ctypes.byref(kv), 16, None, batch, rows, feats, n, 16, 16, 16, ws, None)
+    assert lib.dflash_target_workspace_bytes(ctypes.byref(td), 1, 17) > (1 << 20)
+    assert lib.dflash_target_workspace_bytes(ctypes.byref(td), 1, 33) == 0
+    assert lib.dflash_target_workspace_bytes(ctypes.byref(td), 0, 17) == 0
+    assert call(1, 0, fl, 3) == _lib.DFLASH_ERR_SHAPE
+    assert call(1, 33, fl, 3) == _lib.DFLASH_ERR_SHAPE
+    assert call(3, 17, fl, 3) == _lib.DFLASH_ERR_SHAPE          # above kv->max_batch
+    assert call(1, 17, fl, 17) == _lib.DFLASH_ERR_SHAPE         # n_feat above 16
+    assert call(1, 17, None, 3) == _lib.DFLASH_ERR_NULL
+    dup = (ctypes.c_int32 * 3)(5, 11, 5)
+    assert call(1, 17, dup, 3) == _lib.DFLASH_ERR_SHAPE
+    out = (ctypes.c_int32 * 3)(5, 11, 36)
+    assert call(1, 17, out, 3) == _lib.DFLASH_ERR_SHAPE
+    assert call(1, 17, fl, 3, ws=4096) == _lib.DFLASH_ERR_WORKSPACE
+    layers[7] = _lib.Layer(16, 16, None, 16, 16, 16)
+    assert call(1, 17, fl, 3) == _lib.DFLASH_ERR_NULL
+    assert lib.dflash_kv_commit(ctypes.byref(td), ctypes.byref(kv), 16, 3, 17, None) == _lib.DFLASH_ERR_SHAPE
+    assert lib.dflash_kv_commit(ctypes.byref(td), ctypes.byref(kv), 16, 1, -1, None) == _lib.DFLASH_ERR_SHAPE
+    assert lib.dflash_kv_commit(ctypes.byref(td), ctypes.byref(kv), None, 1, 17, None) == _lib.DFLASH_ERR_NULL
+
+
+def test_tree_validation(lib):
+    """Draft trees: topk in [1, 8], nodes in [1, 31] and within the
+    continuations of the block, walk sizes in [1, 32], batches in range."""
+    d = cdims(C.QWEN3_8B_DRAFT)
+    layers, w, kv = _drafter_structs()
+    big = 1 << 40
+    tree = lambda batch, topk, nodes: lib.dflash_draft_tree(
+        ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), 16, batch, topk, nodes, 16, 16, 16, 16, big, None)
+    assert tree(1, 0, 8) == _lib.DFLASH_ERR_SHAPE
+    assert tree(1, 9, 8) == _lib.DFLASH_ERR_SHAPE
+    assert tree(1, 4, 0) == _lib.DFLASH_ERR_SHAPE
+    assert tree(1, 4, 32) == _lib.DFLASH_ERR_SHAPE
+    assert tree(0, 4, 8) == _lib.DFLASH_ERR_SHAPE
+    assert tree(65, 4, 8) == _lib.DFLASH_ERR_SHAPE
+    d4 = cdims(C.QWEN3_8B_DRAFT.with_block(4))
+    # K = 1 over 4 slots: 4 continuations, so 5 nodes cannot exist
+    assert lib.dflash_draft_tree(ctypes.byref(d4), ctypes.byref(w), ctypes.byref(kv), 16, 1, 1, 5, 16, 16, 16,
+                                 16, big, None) == _lib.DFLASH_ERR_SHAPE
+    acc = lambda batch, n: lib.dflash_tree_accept(ctypes.byref(d), 16, 16, 16, 16, batch, n, 16, 16, 16, 16, 16,
+                                                  big, None)
+    assert acc(1, 0) == _lib.DFLASH_ERR_SHAPE
+    assert acc(1, 33) == _lib.DFLASH_ERR_SHAPE
+    assert acc(65, 8) == _lib.DFLASH_ERR_SHAPE
+    assert lib.dflash_tree_accept(ctypes.byref(d), 16, 16, 16, 16, 1, 8, 16, 16, 16, None, 16, big,
+                                  None) == _lib.DFLASH_ERR_NULL
+    td = cdims(C.QWEN3_8B_TARGET)
+    _, _, tkv = _drafter_structs(36, 4096, 2)
+    path = lambda batch, n: lib.dflash_kv_commit_path(ctypes.byref(td), ctypes.byref(tkv), 16, 16, batch, n, None)
+    assert path(1, 33) == _lib.DFLASH_ERR_SHAPE
+    assert path(3, 8) == _lib.DFLASH_ERR_SHAPE
+    assert path(1, 0) == _lib.DFLASH_ERR_SHAPE
+
+
+def test_anchor_and_sampling_validation(lib):
+    """Anchored drafting takes 1-64 blocks; sampling needs a positive finite
+    temperature and its uniforms."""
+    d = cdims(C.QWEN3_8B_DRAFT)
+    layers, w, kv = _drafter_structs()
+    big = 1 << 40
+    anchors = lambda nb, pos=16: lib.dflash_draft_anchors(ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), 16,
+                                                        pos, 16, nb, 16, 16, big, None)
+    assert anchors(0) == _lib.DFLASH_ERR_SHAPE
+    assert anchors(65) == _lib.DFLASH_ERR_SHAPE
+    assert anchors(4, None) == _lib.DFLASH_ERR_NULL
+    sample = lambda t, u=16: lib.dflash_draft_sample(ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), 16, 1, t,
+                                                     u, 16, 16, 16, big, None)
+    for t in (0.0, -1.0, float("inf"), float("nan")):
+        assert sample(t) == _lib.DFLASH_ERR_SHAPE, t
+    assert sample(1.0, None) == _lib.DFLASH_ERR_NULL
+    ver = lambda t, batch=1, ua=16: lib.dflash_verify_sample(ctypes.byref(d), 16, 16, 16, 16, batch, t, ua, 16, 16,
+                                                             16, 16, 16, big, None)
+    assert ver(0.0) == _lib.DFLASH_ERR_SHAPE
+    assert ver(1.0, batch=0) == _lib.DFLASH_ERR_SHAPE
+    assert ver(1.0, ua=None) == _lib.DFLASH_ERR_NULL
+    assert lib.dflash_verify_sample(ctypes.byref(d), 16, 16, 16, 16, 1, 1.0, 16, 16, 16, 16, 16, 16, 4096,
+                                    None) == _lib.DFLASH_ERR_WORKSPACE
