@@ -472,7 +472,8 @@ static void launch_tiled_shape(const GemmParams &p, int grid, hipStream_t s) {
 // Tile choice, 8 wavefronts in a 2 x 4 grid:
 //   heads (argmax): TM x 16 fragments with TM even, at most 12: one token
 //     block covering every row when it fits (each weight byte read once),
-//     else 8 or 12, whichever pads the rows less;
+//     else 8 or 12, whichever pads the rows less; the TM = 8 head with one
+//     activation plane is 24 fragments wide;
 //   others: 8 x 16 (128 tokens x 256 features) when those items fill at
 //     least 3/4 of the compute units, else 4 x 8 (64 x 128), with split-K
 //     when the items still leave half the units idle.
@@ -488,7 +489,10 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     // without a row tile
     if (mt <= 12) p.tile_m = mt <= 4 ? 4 : (mt + 1) & ~1;
     else p.tile_m = blocks(mt, 12) * 12 < blocks(mt, 8) * 8 ? 12 : 8;
-    p.n_blocks = blocks(p.n_tiles, 16);
+    // the 128-row head tile is 384 features wide (one plane of activations
+    // leaves the registers for it; at 10 and 12 fragments that width spills):
+    // each staged weight fragment feeds more MFMAs
+    p.n_blocks = blocks(p.n_tiles, (XS == 1 && p.tile_m == 8) ? 24 : 16);
   } else {
     // (the rotary QKV epilogue keeps the 64 x 128 tile: at 128 x 256 its
     // partner exchange does not fit the registers)
@@ -515,7 +519,7 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     switch (p.tile_m) {
       case 4: launch_tiled_shape<T, EPI, XS, XROW, 4, 16, 2, 4>(p, grid, s); break;
       case 6: launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s); break;
-      case 8: launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s); break;
+      case 8: launch_tiled_shape<T, EPI, XS, XROW, 8, 24, 2, 4>(p, grid, s); break;
       case 10: launch_tiled_shape<T, EPI, XS, XROW, 10, 16, 2, 4>(p, grid, s); break;
       case 12: launch_tiled_shape<T, EPI, XS, XROW, 12, 16, 2, 4>(p, grid, s); break;
       default: return hipErrorInvalidValue;
