@@ -57,45 +57,54 @@ __device__ inline void gemm_epilogue(const GemmParams &p, const f32x4 *red, cons
   constexpr int KT = Ty<T>::KT, ES = Ty<T>::SIZE;
   constexpr int R = MT * 16, CN = NB * 16, NT = GEMM_THREADS;
   auto val = [&](int ml, int nl) { return rs ? tile_at(red, NB, ml, nl) * rs[ml] : tile_at(red, NB, ml, nl); };
+  // columns nl0 .. nl0 + 3 (nl0 a multiple of 4: one f32x4 of the tile)
+  auto val4 = [&](int ml, int nl0) {
+    const f32x4 t = red[((ml >> 4) * NB + (nl0 >> 4)) * 64 + (ml & 15) + 16 * ((nl0 & 15) >> 2)];
+    return rs ? t * rs[ml] : t;
+  };
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     // 16 consecutive threads hold one row of the 16-column tile, so the
-    // tile's sum of squares is one butterfly (tile_ssq16).
+    // tile's sum of squares is one butterfly (tile_ssq16).  The residual and
+    // the gain are loaded before any store (a load behind a store waits for
+    // it).
     static_assert(CN == 16, "row-major epilogues take one 16-column tile");
     for (int e = threadIdx.x; e < R * CN; e += NT) {
       const int ml = e / CN, nl = e % CN;
       const int m = mblk * R + ml, n = nblk * CN + nl;
       const bool ok = m < p.M && n < p.N;
+      const bool nx = p.nx_packed && n < p.N && m < p.nx_rows;
+      const size_t o = size_t(m) * p.ld_out + n;
       float v = 0.f;
+      if constexpr (EPI == EPI_RESID) {
+        if (ok) v = p.resid[o];
+      }
+      const float gain = nx ? to_f32<T>(reinterpret_cast<const T *>(p.nx_gain)[n]) : 0.f;
       if (ok) {
-        v = val(ml, nl);
-        const size_t o = size_t(m) * p.ld_out + n;
-        if constexpr (EPI == EPI_RESID) v += p.resid[o];
+        v = EPI == EPI_RESID ? val(ml, nl) + v : val(ml, nl);
         p.out_f32[o] = v;
         if (p.aux_out) store_elem<T>(p.aux_out + (size_t(m) * p.aux_ld + n) * ES, v);
       }
-      if (p.nx_packed && n < p.N && m < p.nx_rows) {
-        const float y = ok ? v * to_f32<T>(reinterpret_cast<const T *>(p.nx_gain)[n]) : 0.f;
-        store_split<T>(p.nx_packed + packed_offset<T>(m, n, p.nx_kt), p.nx_plane, p.nx_planes, y);
-      }
+      if (nx) store_split<T>(p.nx_packed + packed_offset<T>(m, n, p.nx_kt), p.nx_plane, p.nx_planes, v * gain);
       if (p.ssq_out) {
         const float t = tile_ssq16(v);
         if (nl == 0 && ok) p.ssq_out[size_t(m) * p.ssq_ld + nblk] = t;
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
+    // four consecutive columns per thread: one store per plane
     constexpr int HALF = NB / 2;
-    for (int e = threadIdx.x; e < R * HALF * 16; e += NT) {
-      const int ml = e / (HALF * 16), q = e % (HALF * 16);
-      const int pr = q >> 4, c = q & 15;
+    for (int e = threadIdx.x; e < R * HALF * 4; e += NT) {
+      const int ml = e / (HALF * 4), q = e % (HALF * 4);
+      const int pr = q >> 2, c4 = 4 * (q & 3);
       const int m = mblk * R + ml;  // padded rows get zeros
-      const int col = (nblk * HALF + pr) * 16 + c;
-      float out = 0.f;
+      f32x4 out = f32x4{0.f, 0.f, 0.f, 0.f};
       if (m < p.M) {
-        const float gt = val(ml, 2 * pr * 16 + c);
-        const float up = val(ml, (2 * pr + 1) * 16 + c);
-        out = gt / (1.0f + __expf(-gt)) * up;
+        const f32x4 gt = val4(ml, 2 * pr * 16 + c4), up = val4(ml, (2 * pr + 1) * 16 + c4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = gt[i] / (1.0f + __expf(-gt[i])) * up[i];
       }
-      store_split<T>(p.out_packed + packed_offset<T>(m, col, p.out_kt), p.out_plane, p.out_planes, out);
+      store_split4<T>(p.out_packed + packed_offset<T>(m, (nblk * HALF + pr) * 16 + c4, p.out_kt), p.out_plane,
+                      p.out_planes, out);
     }
   } else if constexpr (EPI == EPI_QKV) {
     const int d = p.head_dim, nqd = p.n_q * d, nkd = p.n_kv * d;
@@ -281,11 +290,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   // stay inside the item's NB rows of tiles.  NB == 2 weights use the paired
   // layout (the two row tiles interleave per k-tile), so a wavefront's chunk
   // of an item is one contiguous run.
-  auto w_rsrc = [&](int item) {
+  // live == false: a resource of no bytes, so the loads of a prefetch past
+  // the last item return zeros without a memory access (and do not hold up
+  // the epilogue's own loads behind them).
+  auto w_rsrc = [&](int item, bool live = true) {
     const int nt0 = (item % p.n_blocks) * NB;
     const int seg = nt0 / p.seg_ntiles;
     const char *base = uniform_ptr(p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, int(NB * wstride), BUF_DWORD3);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, live ? int(NB * wstride) : 0,
+                                             BUF_DWORD3);
   };
   const int w_lane = lane * 16;
   auto w_off = [&](int kt, int nb) { return NB == 2 ? (kt * 2 + nb) * 1024 : nb * int(wstride) + kt * 1024; };
@@ -480,25 +493,25 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     // no per-k-tile offsets occupy (and spill out of) the scalar registers.
     // Other chunks clamp their k-tile indices into the chunk.
     const bool exact = NB <= 2 && k1 - k0 == KC;
-    auto w_rsrc_chunk = [&](int item) {
+    auto w_rsrc_chunk = [&](int item, bool live) {
       const int nt0 = (item % p.n_blocks) * NB;
       const int seg = nt0 / p.seg_ntiles;
       const char *base = uniform_ptr(p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride +
                                      size_t(k0) * NB * 1024);
-      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, KC * NB * 1024, BUF_DWORD3);
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, live ? KC * NB * 1024 : 0, BUF_DWORD3);
     };
     auto body = [&](auto ex) {
     constexpr bool EX = decltype(ex)::value;
     WBatch<U, NB> wb[2];
-    auto issue_w = [&](int item, int b, WBatch<U, NB> &f) {
+    auto issue_w = [&](int item, int b, WBatch<U, NB> &f, bool live = true) {
       if constexpr (EX) {
-        const auto rs = w_rsrc_chunk(item);
+        const auto rs = w_rsrc_chunk(item, live);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, ((b * U + u) * NB + nb) * 1024);
       } else {
-        const auto rs = w_rsrc(item);
+        const auto rs = w_rsrc(item, live);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int kt = min(k0 + b * U + u, kclamp);
@@ -546,7 +559,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
           issue_w(item, b + 1, wb[(b + 1) & 1]);
           load_x(b + 1);
         } else {
-          issue_w(next, 0, wb[0]);
+          issue_w(next, 0, wb[0], my_items > 1);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
 #pragma unroll
@@ -560,7 +573,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
       for (int b = 0; b < NBAT; ++b) {
         if (b + 1 < NBAT) issue_w(item, b + 1, wb[(b + 1) & 1]);
-        else issue_w(next, 0, wb[0]);
+        else issue_w(next, 0, wb[0], i + 1 < my_items);
         __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
 #pragma unroll
         for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, !EX);

@@ -26,6 +26,16 @@ namespace dflash {
 
 constexpr int TL_XCDS = 8;   // workgroups are dispatched round-robin over 8 XCDs
 
+// Which tiled instantiations may split their k-tiles over workgroups: not the
+// vocabulary-wide heads, and of the tiles with more than 8 fragments a
+// wavefront only the plain stores (the others have no registers left for the
+// exchange).  WM x WN: fragments a wavefront.
+template <int EPI, int WM, int WN>
+__host__ __device__ constexpr bool tl_can_split() {
+  if (EPI == EPI_ARGMAX || EPI == EPI_LOGITS) return false;
+  return WM * WN <= 8 || EPI == EPI_STORE || EPI == EPI_RESID;
+}
+
 // S: stages of the LDS ring; S - 1 of them are in flight while one is consumed.
 // WGM x WGN wavefronts; each owns (TM / WGM) x (TN / WGN) fragments.
 template <typename T, int EPI, int XS, bool XROW, int TM, int TN, int S, int WGM, int WGN>
@@ -39,6 +49,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   static_assert(TM * 16 <= TL_WAVES * 64, "one thread per token row of the tile");
   // two-tile items (gate/up pairs, the heads) use the paired weight layout
   constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_ARGMAX || EPI == EPI_LOGITS;
+  // Only these instantiations carry the split-K exchange (the launcher never
+  // splits the others)
+  constexpr bool SPLIT_CODE = tl_can_split<EPI, TM / WGM, TN / WGN>();
   constexpr bool RS = !XROW && (EPI == EPI_QKV || EPI == EPI_KVINJ || EPI == EPI_SWIGLU || EPI == EPI_ARGMAX ||
                                 EPI == EPI_LOGITS);
   constexpr int XT = TL_MT * XS;                              // activation fragments per stage
@@ -49,6 +62,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   __shared__ uint4 ring[TL_STAGES * SP * 64];
   __shared__ unsigned long long best_row[TL_MT * 16];
   __shared__ int flag;
+  constexpr bool ROPE = EPI == EPI_QKV || EPI == EPI_KVINJ;
+  __shared__ double turns_s[ROPE ? MAX_ROPE_HALF : 1];
+  __shared__ int ctx_s[ROPE ? MAX_SEQS : 1];
+  __shared__ int cu_s[EPI == EPI_KVINJ ? MAX_SEQS + 1 : 1];
+  __shared__ float rs_s[RS ? MAX_KEY_ROWS : 1];
+  const bool rs_in_lds = RS && p.rs_direct && p.M <= MAX_KEY_ROWS;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -60,7 +79,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   // walk those blocks' units with the part fastest, then the token block.
   const int xcd = int(blockIdx.x) % TL_XCDS, r = int(blockIdx.x) / TL_XCDS;
   const int per_xcd = int(gridDim.x) / TL_XCDS;
-  const int ks = p.ksplit;
+  const int ks = SPLIT_CODE ? p.ksplit : 1;
   const int nb_x = (p.n_blocks - xcd + TL_XCDS - 1) / TL_XCDS;
   const int units_x = nb_x * p.m_blocks * ks;
   const int my_items = (units_x - r + per_xcd - 1) / per_xcd;
@@ -181,6 +200,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
     }
   };
 
+  // Epilogue.  A global load issued after a global store waits for that
+  // store and for every stage load in flight before it (vector memory
+  // counts retire in order), so each epilogue issues all of its global loads
+  // (residual rows, norm gains, tree positions) in one batch before its
+  // first store; the per-row scales, context lengths, segment bounds and
+  // rotary frequencies come from LDS tables filled at kernel start.
   auto epilogue = [&](int item) {
     const int nblk = item / p.m_blocks, mblk = item % p.m_blocks;
     if constexpr (EPI == EPI_ARGMAX) {
@@ -189,16 +214,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
         cur_mblk = mblk;
       }
     }
+    int m_a[TL_WM];
+    bool mok_a[TL_WM];
+    float rs_a[TL_WM];
 #pragma unroll
     for (int a = 0; a < TL_WM; ++a) {
-      const int ml = (wm * TL_WM + a) * 16 + c;   // token within the tile
-      const int m = mblk * TL_MT * 16 + ml;
-      const bool mok = m < p.M;
-      float rs = 1.f;
+      m_a[a] = mblk * TL_MT * 16 + (wm * TL_WM + a) * 16 + c;
+      mok_a[a] = m_a[a] < p.M;
+      rs_a[a] = 1.f;
       if constexpr (RS) {
-        if (p.rs_direct) rs = mok ? p.rs_direct[m] : 0.f;
+        if (p.rs_direct) rs_a[a] = !mok_a[a] ? 0.f : rs_in_lds ? rs_s[m_a[a]] : p.rs_direct[m_a[a]];
       }
-      if constexpr (EPI == EPI_ARGMAX) {
+    }
+    if constexpr (EPI == EPI_ARGMAX) {
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a) {
+        const int ml = (wm * TL_WM + a) * 16 + c;
         unsigned long long k = 0;
 #pragma unroll
         for (int b = 0; b < TL_WN; ++b) {
@@ -206,7 +237,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (n0 + i < p.vocab) {
-              const unsigned long long kk = argmax_key(acc[a][b][i] * rs, n0 + i);
+              const unsigned long long kk = argmax_key(acc[a][b][i] * rs_a[a], n0 + i);
               k = kk > k ? kk : k;
             }
           }
@@ -215,130 +246,216 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
         k = o > k ? o : k;
         o = __shfl_xor(k, 32, 64);
         k = o > k ? o : k;
-        if (g == 0 && mok) __hip_atomic_fetch_max(best_row + ml, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else if constexpr (EPI == EPI_LOGITS) {
+        if (g == 0 && mok_a[a]) __hip_atomic_fetch_max(best_row + ml, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    } else if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a)
 #pragma unroll
         for (int b = 0; b < TL_WN; ++b) {
           const int n0 = (nblk * TL_NT + wn * TL_WN + b) * 16 + 4 * g;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (mok && n0 + i < p.vocab) p.out_f32[size_t(m) * p.ld_out + n0 + i] = acc[a][b][i] * rs;
+            if (mok_a[a] && n0 + i < p.vocab) p.out_f32[size_t(m_a[a]) * p.ld_out + n0 + i] = acc[a][b][i] * rs_a[a];
         }
-      } else if constexpr (EPI == EPI_SWIGLU) {
+    } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a)
 #pragma unroll
         for (int b = 0; b < TL_WN; b += 2) {
           const int pair = (nblk * TL_NT + wn * TL_WN + b) >> 1;
+          f32x4 out = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (mok_a[a]) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int col = pair * 16 + 4 * g + i;
-            float out = 0.f;
-            if (mok) {
-              const float gt = acc[a][b][i] * rs, up = acc[a][b + 1][i] * rs;
-              out = gt / (1.0f + __expf(-gt)) * up;
+            for (int i = 0; i < 4; ++i) {
+              const float gt = acc[a][b][i] * rs_a[a], up = acc[a][b + 1][i] * rs_a[a];
+              out[i] = gt / (1.0f + __expf(-gt)) * up;
             }
-            if (m < p.x_mtiles * 16 && pair < p.n_tiles / 2)  // padded rows get zeros
-              store_split<T>(p.out_packed + packed_offset<T>(m, col, p.out_kt), p.out_plane, p.out_planes, out);
+          }
+          if (m_a[a] < p.x_mtiles * 16 && pair < p.n_tiles / 2)  // padded rows get zeros
+            store_split4<T>(p.out_packed + packed_offset<T>(m_a[a], pair * 16 + 4 * g, p.out_kt), p.out_plane,
+                            p.out_planes, out);
+        }
+    } else if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+      // Rows A0 .. A0 + NA - 1 of the wavefront's fragments: loads first
+      // (residual fragments, the next norm's gains), then the values (zero
+      // outside the output), their stores and the tile sums.  Small tiles
+      // take every row in one pass; large ones (no registers for all the
+      // residual fragments at once) one row of fragments at a time.
+      constexpr int NA = TL_WM * TL_WN <= 8 ? TL_WM : 1;
+      f32x4 gain[TL_WN];
+#pragma unroll
+      for (int b = 0; b < TL_WN; ++b) {
+        const int ntg = nblk * TL_NT + wn * TL_WN + b;
+        const int n0 = ntg * 16 + 4 * g;
+        gain[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.nx_packed && ntg < p.n_tiles) {
+          if constexpr (ES == 2) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(p.nx_gain + size_t(n0) * 2);
+            gain[b] = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                            __uint_as_float(w.y & 0xffff0000u)};
+          } else {
+            gain[b] = *reinterpret_cast<const f32x4 *>(p.nx_gain + size_t(n0) * 4);
           }
         }
-      } else {
+      }
+#pragma unroll
+      for (int A0 = 0; A0 < TL_WM; A0 += NA) {
+        f32x4 val[NA][TL_WN];
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int b = 0; b < TL_WN; ++b) {
+            const int ntg = nblk * TL_NT + wn * TL_WN + b;
+            val[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI == EPI_RESID) {
+              if (mok_a[A0 + a] && ntg < p.n_tiles)
+                val[a][b] = *reinterpret_cast<const f32x4 *>(p.resid + size_t(m_a[A0 + a]) * p.ld_out + ntg * 16 + 4 * g);
+            }
+          }
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int b = 0; b < TL_WN; ++b) {
+            const bool ok = mok_a[A0 + a] && nblk * TL_NT + wn * TL_WN + b < p.n_tiles;
+            f32x4 v = acc[A0 + a][b] * rs_a[A0 + a];
+            if constexpr (EPI == EPI_RESID) v += val[a][b];
+            val[a][b] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int b = 0; b < TL_WN; ++b) {
+            const int ntg = nblk * TL_NT + wn * TL_WN + b;
+            const int n0 = ntg * 16 + 4 * g;
+            const int m = m_a[A0 + a];
+            if (mok_a[A0 + a] && ntg < p.n_tiles) {
+              *reinterpret_cast<f32x4 *>(p.out_f32 + size_t(m) * p.ld_out + n0) = val[a][b];
+              if (p.aux_out) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store_elem<T>(p.aux_out + (size_t(m) * p.aux_ld + n0 + i) * ES, val[a][b][i]);
+              }
+            }
+            if (p.nx_packed && ntg < p.n_tiles && m < p.nx_rows)
+              store_split4<T>(p.nx_packed + packed_offset<T>(m, n0, p.nx_kt), p.nx_plane, p.nx_planes, val[a][b] * gain[b]);
+          }
+        if (p.ssq_out) {
+          // the balanced tree of tile_ssq16: in-lane pairs, then g ^ 1, g ^ 2
+#pragma unroll
+          for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int b = 0; b < TL_WN; ++b) {
+              const f32x4 v = val[a][b];
+              float q = (__fmul_rn(v[0], v[0]) + __fmul_rn(v[1], v[1])) + (__fmul_rn(v[2], v[2]) + __fmul_rn(v[3], v[3]));
+              q += __shfl_xor(q, 16, 64);
+              q += __shfl_xor(q, 32, 64);
+              const int ntg = nblk * TL_NT + wn * TL_WN + b;
+              if (g == 0 && mok_a[A0 + a] && ntg < p.n_tiles) p.ssq_out[size_t(m_a[A0 + a]) * p.ssq_ld + ntg] = q;
+            }
+        }
+      }
+    } else if constexpr (EPI == EPI_QKV) {
+      // A lane's four features n0 .. n0 + 3 of a fragment are four
+      // consecutive channels of one head in the packed rotary order, so the
+      // q and k rows take one store per lane chunk; v (position-interleaved
+      // layout) takes one per element.
+      const int d = p.head_dim, nqd = p.n_q * d, nkd = p.n_kv * d;
+      const int dt_count = d / KT;
+      int rp[TL_WM];   // rotary position offset of each row: its tree depth, else its block slot
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a) rp[a] = p.row_pos && mok_a[a] ? p.row_pos[m_a[a]] : m_a[a] % p.block;
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a) {
+        const int m = m_a[a];
+        const int sq = m / p.block, j = m % p.block;
+        const int ctx = mok_a[a] ? ctx_s[min(sq, MAX_SEQS - 1)] : 0;
+#pragma unroll
+        for (int b = 0; b < TL_WN; ++b) {
+          const int ntg = nblk * TL_NT + wn * TL_WN + b;
+          const int n0 = ntg * 16 + 4 * g;
+          const f32x4 v = acc[a][b] * rs_a[a];
+          f32x4 partner;   // features n ^ 8: lane g ^ 2
+#pragma unroll
+          for (int i = 0; i < 4; ++i) partner[i] = __shfl_xor(v[i], 32, 64);
+          if (!(mok_a[a] && ntg < p.n_tiles)) continue;
+          if (n0 < nqd + nkd) {
+            const int dd0 = rot_channel(n0 % d, d);
+            f32x4 x = v;
+            if (p.rope_on) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                x[i] = rope_rotate(v[i], partner[i], dd0 + i, d, ctx + rp[a], turns_s[(dd0 + i) % (d >> 1)]);
+            }
+            if (n0 < nqd) {
+              char *base = p.qbuf + (size_t(sq) * p.n_q + n0 / d) * p.q_tiles * dt_count * 1024;
+              store_split4<T>(base + packed_offset<T>(j, dd0, dt_count), p.q_plane, p.q_planes, x);
+            } else {
+              char *base = p.kblk + (size_t(sq) * p.n_kv + (n0 - nqd) / d) * size_t(KT) * d * ES;
+              store_elem4<T>(base + kcache_offset<T>(j, dd0, d), x);
+              if (p.qkv_to_cache) qkv_cache_store_k4<T>(p, sq, (n0 - nqd) / d, ctx + j, dd0, x);
+            }
+          } else {
+            const int cc0 = n0 - nqd - nkd;
+            char *base = p.vblk + (size_t(sq) * p.n_kv + cc0 / d) * size_t(KT) * d * ES;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              store_elem<T>(base + vcache_offset<T>(j, cc0 % d + i, d), v[i]);
+              if (p.qkv_to_cache) qkv_cache_store<T>(p, false, sq, cc0 / d, ctx + j, cc0 % d + i, v[i]);
+            }
+          }
+        }
+      }
+    } else if constexpr (EPI == EPI_KVINJ) {
+      const int d = p.head_dim, nkd = p.n_kv * d, segn = 2 * nkd;
+      const size_t region = size_t(p.capacity) * d * ES;
+#pragma unroll
+      for (int a = 0; a < TL_WM; ++a) {
+        const int m = m_a[a];
+        const bool mok = mok_a[a];
+        int sq = 0, start = 0, ns = 0, C = 0;
+        if (mok) {
+          int lo = 0, hi = p.batch;  // cu_new[lo] <= m < cu_new[lo + 1]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu_s[mid] <= m) lo = mid; else hi = mid;
+          }
+          sq = lo;
+          start = cu_s[sq];
+          ns = cu_s[sq + 1] - start;
+          C = ctx_s[sq];
+        }
+        const bool fits = C + ns <= p.capacity;
 #pragma unroll
         for (int b = 0; b < TL_WN; ++b) {
           const int ntg = nblk * TL_NT + wn * TL_WN + b;
           const int n0 = ntg * 16 + 4 * g;
           const bool nok = ntg < p.n_tiles;
-          f32x4 v = acc[a][b] * rs;
-          if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-            const size_t o = size_t(m) * p.ld_out + n0;
-            if (mok && nok) {
-              if constexpr (EPI == EPI_RESID) v += *reinterpret_cast<const f32x4 *>(p.resid + o);
-              *reinterpret_cast<f32x4 *>(p.out_f32 + o) = v;
-              if (p.aux_out) {
+          const f32x4 v = acc[a][b] * rs_a[a];
+          f32x4 partner;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) store_elem<T>(p.aux_out + (size_t(m) * p.aux_ld + n0 + i) * ES, v[i]);
-              }
-            } else {
-              v = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            if (p.nx_packed && nok && m < p.nx_rows) {
+          for (int i = 0; i < 4; ++i) partner[i] = __shfl_xor(v[i], 32, 64);
+          if (!(mok && nok)) continue;
+          if (!fits) {
+            if (m == start && n0 == 0) atomicOr(p.status, DFLASH_STATUS_CAPACITY);
+            continue;
+          }
+          const int pos = C + (m - start);
+          const int layer = p.layer0 + n0 / segn, cc0 = n0 % segn;
+          if (cc0 < nkd) {
+            const int dd0 = rot_channel(cc0 % d, d);
+            f32x4 r = v;
+            if (p.rope_on) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float y = v[i] * to_f32<T>(reinterpret_cast<const T *>(p.nx_gain)[n0 + i]);
-                store_split<T>(p.nx_packed + packed_offset<T>(m, n0 + i, p.nx_kt), p.nx_plane, p.nx_planes, y);
-              }
+              for (int i = 0; i < 4; ++i)
+                r[i] = rope_rotate(v[i], partner[i], dd0 + i, d, pos, turns_s[(dd0 + i) % (d >> 1)]);
             }
-            if (p.ssq_out) {
-              // the balanced tree of tile_ssq16: in-lane pairs, then g ^ 1, g ^ 2
-              float s = (__fmul_rn(v[0], v[0]) + __fmul_rn(v[1], v[1])) + (__fmul_rn(v[2], v[2]) + __fmul_rn(v[3], v[3]));
-              s += __shfl_xor(s, 16, 64);
-              s += __shfl_xor(s, 32, 64);
-              if (g == 0 && mok && nok) p.ssq_out[size_t(m) * p.ssq_ld + ntg] = s;
-            }
-          } else if constexpr (EPI == EPI_QKV) {
-            const int d = p.head_dim, nqd = p.n_q * d, nkd = p.n_kv * d;
-            const int dt_count = d / KT;
-            const int sq = m / p.block, j = m % p.block;
+            char *base = p.kcache + ((size_t(layer) * p.max_batch + sq) * p.n_kv + cc0 / d) * region;
+            store_elem4<T>(base + kcache_offset<T>(pos, dd0, d), r);
+          } else {
+            const int c2 = cc0 - nkd;
+            char *base = p.vcache + ((size_t(layer) * p.max_batch + sq) * p.n_kv + c2 / d) * region;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float partner = __shfl_xor(v[i], 32, 64);  // feature n ^ 8: lane g ^ 2
-              const int n = n0 + i;
-              if (!(mok && nok)) continue;
-              float x = v[i];
-              if (n < nqd + nkd) {
-                const int dd = rot_channel(n % d, d);
-                x = rope_apply(x, partner, dd, d, p.ctx_len[sq] + (p.row_pos ? p.row_pos[m] : j), p);
-                if (n < nqd) {
-                  char *base = p.qbuf + (size_t(sq) * p.n_q + n / d) * p.q_tiles * dt_count * 1024;
-                  store_split<T>(base + packed_offset<T>(j, dd, dt_count), p.q_plane, p.q_planes, x);
-                } else {
-                  char *base = p.kblk + (size_t(sq) * p.n_kv + (n - nqd) / d) * size_t(KT) * d * ES;
-                  store_elem<T>(base + kcache_offset<T>(j, dd, d), x);
-                  if (p.qkv_to_cache) qkv_cache_store<T>(p, true, sq, (n - nqd) / d, p.ctx_len[sq] + j, dd, x);
-                }
-              } else {
-                const int cc = n - nqd - nkd;
-                char *base = p.vblk + (size_t(sq) * p.n_kv + cc / d) * size_t(KT) * d * ES;
-                store_elem<T>(base + vcache_offset<T>(j, cc % d, d), x);
-                if (p.qkv_to_cache) qkv_cache_store<T>(p, false, sq, cc / d, p.ctx_len[sq] + j, cc % d, x);
-              }
-            }
-          } else if constexpr (EPI == EPI_KVINJ) {
-            const int d = p.head_dim, nkd = p.n_kv * d, segn = 2 * nkd;
-            const size_t region = size_t(p.capacity) * d * ES;
-            int sq = 0, start = 0, ns = 0, C = 0;
-            if (mok) {
-              int lo = 0, hi = p.batch;  // cu_new[lo] <= m < cu_new[lo + 1]
-              while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (p.cu_new[mid] <= m) lo = mid; else hi = mid;
-              }
-              sq = lo;
-              start = p.cu_new[sq];
-              ns = p.cu_new[sq + 1] - start;
-              C = p.ctx_len[sq];
-            }
-            const bool fits = C + ns <= p.capacity;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float partner = __shfl_xor(v[i], 32, 64);
-              const int n = n0 + i;
-              if (!(mok && nok)) continue;
-              if (!fits) {
-                if (m == start && n == 0) atomicOr(p.status, DFLASH_STATUS_CAPACITY);
-                continue;
-              }
-              const int pos = C + (m - start);
-              const int layer = p.layer0 + n / segn, cc = n % segn;
-              if (cc < nkd) {
-                const int dd = rot_channel(cc % d, d);
-                const float r = rope_apply(v[i], partner, dd, d, pos, p);
-                char *base = p.kcache + ((size_t(layer) * p.max_batch + sq) * p.n_kv + cc / d) * region;
-                store_elem<T>(base + kcache_offset<T>(pos, dd, d), r);
-              } else {
-                const int c2 = cc - nkd;
-                char *base = p.vcache + ((size_t(layer) * p.max_batch + sq) * p.n_kv + c2 / d) * region;
-                store_elem<T>(base + vcache_offset<T>(pos, c2 % d, d), v[i]);
-              }
-            }
+            for (int i = 0; i < 4; ++i) store_elem<T>(base + vcache_offset<T>(pos, c2 % d + i, d), v[i]);
           }
         }
       }
@@ -348,8 +465,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
 
   if constexpr (EPI == EPI_ARGMAX) {
     if (int(threadIdx.x) < TL_MT * 16) best_row[threadIdx.x] = 0;
-    __syncthreads();
   }
+  // The epilogue's small tables, read before any stage is issued (so the
+  // wait for them is one round trip, not a drain of the ring).
+  if constexpr (ROPE) {
+    if (wave == 0) {
+      double v = 0.0;
+#pragma unroll
+      for (int i = 0; i < MAX_ROPE_HALF; ++i) v = lane == i ? p.rope_turns[i] : v;   // kernel-argument reads
+      turns_s[lane] = v;
+    }
+    const int nseq = EPI == EPI_KVINJ ? p.batch : min((p.M + p.block - 1) / p.block, MAX_SEQS);
+    for (int i = threadIdx.x; i < nseq; i += blockDim.x) ctx_s[i] = p.ctx_len[i];
+    if constexpr (EPI == EPI_KVINJ) {
+      for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) cu_s[i] = p.cu_new[i];
+    }
+  }
+  if constexpr (RS) {
+    if (rs_in_lds) {
+      for (int i = threadIdx.x; i < p.M; i += blockDim.x) rs_s[i] = p.rs_direct[i];
+    }
+  }
+  __syncthreads();
   zero();
   if (my_items > 0) set_item(0);
 #pragma unroll
@@ -388,40 +525,69 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
     read_frags(0, fa);
   }
   // The parts of a split item meet in the workspace: each stores its partial
-  // tile (agent-coherent stores, one f32x4 slot per lane and fragment),
+  // tile (16-byte agent-coherent stores, one f32x4 per lane and fragment),
   // waits for them and counts itself in; the last to arrive sums the parts
   // in part order from the workspace, so the result does not depend on
   // which part finished last, resets the count and runs the epilogue.
   auto split_last = [&](int unit) -> bool {
     const int item = unit / ks;
-    // Fragment (a, b) of a wavefront is 256 floats; element i of every lane
-    // is a run of 64 consecutive floats, so each coherent store and load
-    // instruction moves one contiguous 256-byte run.
-    auto slot = [&](int u, int a, int b) {
-      return p.part_ws + ((size_t(u) * TL_WAVES + wave) * (TL_WM * TL_WN) + a * TL_WN + b) * 256 + lane;
-    };
+    // A unit's partial tile: per wavefront its TL_WM x TL_WN fragments, 1 KiB
+    // each, one 16-byte run per lane; the unit and wavefront part of the
+    // offset is uniform.
+    constexpr int FR = TL_WM * TL_WN;
+    const auto prs = __builtin_amdgcn_make_buffer_rsrc(p.part_ws, (short)0, int(SPLIT_PART_BYTES), BUF_DWORD3);
+    auto base_of = [&](int u) { return __builtin_amdgcn_readfirstlane((u * TL_WAVES + wave) * FR * 1024); };
+    const int lane_off = lane * 16;
+    {
+      const int sb = base_of(unit);
 #pragma unroll
-    for (int a = 0; a < TL_WM; ++a)
+      for (int a = 0; a < TL_WM; ++a)
 #pragma unroll
-      for (int b = 0; b < TL_WN; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(slot(unit, a, b) + i * 64, acc[a][b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int b = 0; b < TL_WN; ++b) st16_agent(prs, lane_off + (a * TL_WN + b) * 1024, sb, acc[a][b]);
+    }
     if (!last_arriver_of(p.part_cnt + item, unsigned(ks), &flag)) {
       zero();
       return false;
     }
     if (threadIdx.x == 0) __hip_atomic_store(p.part_cnt + item, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int j = 0; j < ks; ++j) {
+    // Small tiles: GP parts' loads in flight together (16 fragments a
+    // wavefront), summed in part order; a group past the last part reloads
+    // the last part and drops it.  Large tiles: one part at a time, a row of
+    // fragments per load group.
+    if constexpr (FR <= 8) {
+      constexpr int GP = 16 / FR;
+      for (int j0 = 0; j0 < ks; j0 += GP) {
+        f32x4 v[GP][TL_WM][TL_WN];
 #pragma unroll
-      for (int a = 0; a < TL_WM; ++a)
+        for (int q = 0; q < GP; ++q) {
+          const int sb = base_of(item * ks + min(j0 + q, ks - 1));
 #pragma unroll
-        for (int b = 0; b < TL_WN; ++b)
+          for (int a = 0; a < TL_WM; ++a)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = __hip_atomic_load(slot(item * ks + j, a, b) + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            acc[a][b][i] = j == 0 ? v : acc[a][b][i] + v;
+            for (int b = 0; b < TL_WN; ++b) v[q][a][b] = ld16_agent(prs, lane_off + (a * TL_WN + b) * 1024, sb);
+        }
+#pragma unroll
+        for (int q = 0; q < GP; ++q) {
+          if (j0 + q < ks) {
+#pragma unroll
+            for (int a = 0; a < TL_WM; ++a)
+#pragma unroll
+              for (int b = 0; b < TL_WN; ++b) acc[a][b] = j0 + q == 0 ? v[q][a][b] : acc[a][b] + v[q][a][b];
           }
+        }
+      }
+    } else {
+      for (int j = 0; j < ks; ++j) {
+        const int sb = base_of(item * ks + j);
+#pragma unroll
+        for (int a = 0; a < TL_WM; ++a) {
+          f32x4 v[TL_WN];
+#pragma unroll
+          for (int b = 0; b < TL_WN; ++b) v[b] = ld16_agent(prs, lane_off + (a * TL_WN + b) * 1024, sb);
+#pragma unroll
+          for (int b = 0; b < TL_WN; ++b) acc[a][b] = j == 0 ? v[b] : acc[a][b] + v[b];
+        }
+      }
     }
     return true;
   };
@@ -439,7 +605,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
       step(fa, fb2);
       fa = fb2;
     }
-    if (ks == 1 || split_last(unit)) epilogue(unit / ks);
+    bool run_epi = true;
+    if constexpr (SPLIT_CODE) run_epi = ks == 1 || split_last(unit);
+    if (run_epi) epilogue(unit / ks);
     after_epi = true;
   }
   if constexpr (EPI == EPI_ARGMAX) {

@@ -17,6 +17,10 @@ constexpr int MAX_KEY_ROWS = 1088;   // 64 sequences x 17 verify rows
 constexpr size_t WS_COUNTER_BYTES = size_t(1) << 20;
 static_assert(size_t(MAX_KEY_ROWS) * ARGMAX_SLOTS * 8 <= WS_COUNTER_BYTES, "key slots exceed the fixed area");
 constexpr int MAX_SEGMENTS = 16;
+// Sequences of one launch (the largest batch the library takes) and rotary
+// pairs of a head (head_dim <= 128).
+constexpr int MAX_SEQS = 64;
+constexpr int MAX_ROPE_HALF = 64;
 // Arrival counter of the last-arriver handshakes, at the end of the fixed area.
 constexpr size_t WS_ARRIVE_OFFSET = WS_COUNTER_BYTES - 256;
 // Split-K: partial tiles in a workspace region of SPLIT_PART_BYTES (tiled
