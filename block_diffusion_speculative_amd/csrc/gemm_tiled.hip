@@ -637,14 +637,63 @@ static void launch_tiled_shape(const GemmParams &p, int grid, hipStream_t s) {
   hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, XS, XROW, TM, TN, S, WGM, WGN>), dim3(grid), dim3(WGM * WGN * 64), 0, s, p);
 }
 
+// Tile and split choice of the non-head launches.  The kernel is bound by
+// staging fragments through LDS, so a choice costs its busiest workgroup's
+// 1 KiB fragment loads (per k-tile: the tile's activation fragments, one or
+// two planes, and its weight fragments), weighted by how few ring stages the
+// tile leaves in flight (measured per fragment: 9 stages 1.0, 6 about 1.1,
+// 4 about 1.15, 3 about 1.25), plus about 100 fragments' time per unit for
+// its epilogue and, for split items, about 120 more per unit for storing its
+// partial tile and counting in and about 50 per round trip of the last
+// part's gather.  Tiles: 64 x 128 for every epilogue; 64 x 192 for
+// QKV (its rotary partner exchange does not fit a 128-row tile); 128 x 256
+// for the others; 128 x 384 for gate/up.  k-tiles split into at most 8 parts
+// of at least 8 when the workspace holds the partial tiles.
+struct TileChoice {
+  int tm, tn, ks;
+};
+template <int EPI, int XS>
+static TileChoice choose_tile(int M, int n_tiles, int k_tiles, int cu, bool split_ws) {
+  auto blocks = [](long n, long b) { return (n + b - 1) / b; };
+  TileChoice best{4, 8, 1};
+  long best_cost = -1;
+  auto consider = [&](int tm, int tn, bool splittable) {
+    const long mb = blocks(M, 16 * tm), nb = blocks(n_tiles, tn);
+    const int fr = (tm / 2) * (tn / 4);   // fragments a wavefront
+    for (int ks = 1; ks <= 8; ++ks) {
+      if (ks > 1 && !(splittable && split_ws && k_tiles / ks >= 8)) break;
+      const long units = mb * nb * ks;
+      if (ks > 1 && (units * tm * tn * 1024 > long(SPLIT_PART_BYTES) || mb * nb > MAX_SPLIT_ITEMS)) break;
+      long grid = units < cu ? units : cu;
+      grid = grid < TL_XCDS ? TL_XCDS : grid - grid % TL_XCDS;
+      const long per_wg = blocks(blocks(nb, TL_XCDS) * mb * ks, grid / TL_XCDS);   // the busiest XCD's share
+      const long rounds = ks == 1 ? 0 : fr <= 8 ? blocks(ks, 16 / fr) + 2 : long(ks) * (tm / 2) + 2;
+      const long stages = 144 / (blocks(XS * tm + tn, 8) * 8);
+      const long weight = stages >= 8 ? 100 : stages >= 6 ? 110 : stages >= 4 ? 115 : 125;   // percent
+      const long cost = per_wg * (blocks(k_tiles, ks) * (XS * tm + tn) * weight / 100 + 100 + (ks > 1 ? 120 : 0)) +
+                        50 * rounds;
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = TileChoice{tm, tn, ks};
+      }
+    }
+  };
+  consider(4, 8, tl_can_split<EPI, 2, 2>());
+  if constexpr (EPI == EPI_QKV) {
+    consider(4, 12, tl_can_split<EPI, 2, 3>());
+  } else {
+    consider(8, 16, tl_can_split<EPI, 4, 4>());
+    if constexpr (EPI == EPI_SWIGLU) consider(8, 24, tl_can_split<EPI, 4, 6>());
+  }
+  return best;
+}
+
 // Tile choice, 8 wavefronts in a 2 x 4 grid:
 //   heads (argmax): TM x 16 fragments with TM even, at most 12: one token
 //     block covering every row when it fits (each weight byte read once),
 //     else 8 or 12, whichever pads the rows less; the TM = 8 head with one
 //     activation plane is 24 fragments wide;
-//   others: 8 x 16 (128 tokens x 256 features) when those items fill at
-//     least 3/4 of the compute units, else 4 x 8 (64 x 128), with split-K
-//     when the items still leave half the units idle.
+//   others: by choose_tile.
 template <typename T, int EPI, int XS, bool XROW>
 static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   GemmParams p = p0;
@@ -652,6 +701,8 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   auto blocks = [](int n, int b) { return (n + b - 1) / b; };
   const int mt = blocks(p.M, 16);
   constexpr bool HEAD = EPI == EPI_ARGMAX || EPI == EPI_LOGITS;   // vocabulary-wide heads
+  int tn = 16;
+  p.ksplit = 1;
   if (HEAD) {
     // at least 4 fragments: 2 (17-32 rows) would leave half the wave grid
     // without a row tile
@@ -662,23 +713,14 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     // each staged weight fragment feeds more MFMAs
     p.n_blocks = blocks(p.n_tiles, (XS == 1 && p.tile_m == 8) ? 24 : 16);
   } else {
-    // (the rotary QKV epilogue keeps the 64 x 128 tile: at 128 x 256 its
-    // partner exchange does not fit the registers)
-    const bool big = EPI != EPI_QKV && blocks(p.M, 128) * blocks(p.n_tiles, 16) * 4 >= 3 * cu;
-    p.tile_m = big ? 8 : 4;
-    p.n_blocks = big ? blocks(p.n_tiles, 16) : blocks(p.n_tiles, 8);
+    const TileChoice tc = choose_tile<EPI, XS>(p.M, p.n_tiles, p.k_tiles, cu, p.part_ws && p.part_cnt);
+    p.tile_m = tc.tm;
+    p.n_blocks = blocks(p.n_tiles, tc.tn);
+    p.ksplit = tc.ks;
+    tn = tc.tn;
   }
   p.m_blocks = blocks(p.M, 16 * p.tile_m);
   const int items = p.m_blocks * p.n_blocks;
-  // Too few items for the compute units: split each item's k-tiles into
-  // parts of at least 16.
-  p.ksplit = 1;
-  if (!HEAD && p.part_ws && p.part_cnt && 2 * items <= cu) {
-    const int cap = cu < MAX_SPLIT_UNITS ? cu : MAX_SPLIT_UNITS;
-    int ks = cap / items;
-    if (ks > p.k_tiles / 16) ks = p.k_tiles / 16;
-    p.ksplit = ks > 1 ? ks : 1;
-  }
   // grid: a multiple of the 8 XCDs, at most one workgroup per compute unit
   const int units = items * p.ksplit;
   int grid = units < cu ? units : cu;
@@ -692,11 +734,33 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
       case 12: launch_tiled_shape<T, EPI, XS, XROW, 12, 16, 2, 4>(p, grid, s); break;
       default: return hipErrorInvalidValue;
     }
+  } else if constexpr (HEAD) {
+    if (p.tile_m != 8) return hipErrorInvalidValue;
+    launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
   } else {
-    if (HEAD && p.tile_m != 8) return hipErrorInvalidValue;
-    if constexpr (EPI == EPI_QKV) launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
-    else if (p.tile_m == 8) launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
-    else launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
+    const int shape = p.tile_m * 100 + tn;
+    if (shape == 408) {
+      launch_tiled_shape<T, EPI, XS, XROW, 4, 8, 2, 4>(p, grid, s);
+      return hipGetLastError();
+    }
+    if constexpr (EPI == EPI_QKV) {
+      if (shape == 412) {
+        launch_tiled_shape<T, EPI, XS, XROW, 4, 12, 2, 4>(p, grid, s);
+        return hipGetLastError();
+      }
+    } else {
+      if (shape == 816) {
+        launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
+        return hipGetLastError();
+      }
+      if constexpr (EPI == EPI_SWIGLU) {
+        if (shape == 824) {
+          launch_tiled_shape<T, EPI, XS, XROW, 8, 24, 2, 4>(p, grid, s);
+          return hipGetLastError();
+        }
+      }
+    }
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
