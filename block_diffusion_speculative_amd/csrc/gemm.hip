@@ -302,8 +302,20 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   };
   const int w_lane = lane * 16;
   auto w_off = [&](int kt, int nb) { return NB == 2 ? (kt * 2 + nb) * 1024 : nb * int(wstride) + kt * 1024; };
+  // With streamed activations or two row tiles of row-major input, lanes of rows past M load
+  // nothing (the packed buffers hold zeros there): the second row tile of a
+  // 17-row launch then moves 64 bytes a fragment instead of 1 KiB.  (A
+  // resident single tile loads once; the guard would only cost registers.)
   auto x_load = [&](int mtg, int kt, int xp) -> uint4 {
-    if constexpr (XROW) {
+    if constexpr (KC == 0 || (MT > 1 && XROW)) {
+      const int row = mtg * 16 + (lane & 15);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < p.M) {
+        if constexpr (XROW) v = ld16(p.x + (size_t(row) * p.x_ld + kt * KT + (lane >> 4) * E) * ES);
+        else v = ld16(p.x + xp * p.x_plane + (size_t(mtg) * p.k_tiles + kt) * 1024 + lane * 16);
+      }
+      return v;
+    } else if constexpr (XROW) {
       const int row = min(mtg * 16 + (lane & 15), p.M - 1);
       return ld16(p.x + (size_t(row) * p.x_ld + kt * KT + (lane >> 4) * E) * ES);
     } else {

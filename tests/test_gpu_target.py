@@ -112,10 +112,11 @@ def test_target_pass_and_commit_small():
     _check_pass(tc, I.target_tokens(d, 80, 1, 2, 5), [1])
 
 
-@pytest.mark.parametrize("rows", [1, 16, 32])
+@pytest.mark.parametrize("rows", [1, 16, 17, 32])
 def test_target_row_counts(rows):
-    """One row (the autoregressive step), one full query tile, and the
-    largest pass (32 rows, a full key step of new rows)."""
+    """One row (the autoregressive step), one full query tile, the verify
+    pass of a 16-slot block (17 rows: a second row tile holding one row),
+    and the largest pass (32 rows, a full key step of new rows)."""
     d = SMALL_TARGET
     tc = TargetCase(d, 1, [61], seed=81 + rows)
     _check_pass(tc, I.target_tokens(d, 81, rows, 1, rows), [3])
