@@ -35,6 +35,8 @@ __device__ inline float tile_at(const f32x4 *t, int NB, int ml, int nl) {
 // and wavefronts are summed in a fixed order.  The summation order of a row therefore never depends on how
 // many other rows share the launch.
 constexpr int GEMM_WAVES = 8;
+// 17-row launches (X1): most k-tiles a wavefront's chunk may hold (K <= 12288 for bf16)
+constexpr int X1_MAX_KTILES = 48;
 // LDS staging of an inline RMSNorm's tile sums: rows x tiles <= 8192 floats.
 constexpr int RS_STAGE_FLOATS = 8192;
 constexpr int GEMM_THREADS = GEMM_WAVES * 64;
@@ -248,10 +250,18 @@ __device__ inline void fused_argmax_finish(const ArgmaxFinishParams &f, int M, i
 // RMSNorm: the activations arrive as (x * gain) and the epilogue scales each
 // output row by 1 / rms(x) (the scale commutes with the product), so the norm
 // needs neither its own launch nor a pass over the activations here.
-template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
+//
+// X1 (17 rows: two row tiles, the second holding only row 16): the first
+// tile's activations are resident or streamed as for one tile, and row 16's
+// chunk of each wavefront sits in LDS, from which each k-tile's second-tile
+// fragment is formed (lanes of rows 17-31 zero).  A 17-row launch then
+// issues no more global loads than a 16-row one.
+template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC, bool X1>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) {
+  static_assert(!X1 || MT == 2, "one extra row rides on the second row tile");
   constexpr int E = Ty<T>::E, KT = Ty<T>::KT, ES = Ty<T>::SIZE;
-  constexpr int WAVES = GEMM_WAVES, NT = GEMM_THREADS, U = gemm_u<MT, NB>();
+  constexpr int MX = X1 ? 1 : MT;   // row tiles whose activations come from global memory
+  constexpr int WAVES = GEMM_WAVES, NT = GEMM_THREADS, U = X1 ? (NB == 2 && XS == 2 ? 2 : 4) : gemm_u<MT, NB>();
   constexpr int NF = MT * NB;
   constexpr int R = MT * 16;
   constexpr bool XRES = KC > 0;
@@ -268,6 +278,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
                                 EPI == EPI_LOGITS);
   __shared__ float rs_row[RS ? R : 1];
   __shared__ f32x4 rs_stage[RS ? RS_STAGE_FLOATS / 4 : 1];  // tile sums of the block's rows
+  // X1: row 16 of every wavefront's k-tiles and planes, four 16-byte chunks each
+  __shared__ uint4 x1_lds[X1 ? WAVES * X1_MAX_KTILES * XS * 4 : 1];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_items = p.m_blocks * p.n_blocks;
@@ -353,8 +365,20 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   };
   // chk: zero the weights of k-tiles past the wavefront's chunk (a chunk of
   // exactly the resident length needs no check).
-  auto mma_tile = [&](int u, int b, const uint4 (&w)[U][NB], const uint4 (&x)[MT][XS], int mblk, bool chk = true) {
+  // kk: the k-tile's index within the wavefront's chunk (X1's LDS row)
+  auto mma_tile = [&](int u, int b, const uint4 (&w)[U][NB], const uint4 (&x)[MX][XS], int mblk, int kk,
+                      bool chk = true) {
     const bool ok = !chk || k0 + b * U + u < k1;
+    uint4 x1v[XS];
+    if constexpr (X1) {
+#pragma unroll
+      for (int xp = 0; xp < XS; ++xp) {
+        // (k-tiles past the chunk, whose weights are zeroed, read zeros too:
+        // that LDS was never written)
+        const uint4 r = x1_lds[(wave * X1_MAX_KTILES + kk) * XS * 4 + xp * 4 + (lane >> 4)];
+        x1v[xp] = (lane & 15) == 0 && kk < k1 - k0 ? r : make_uint4(0, 0, 0, 0);
+      }
+    }
     bool row_ok[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) row_ok[mt] = !XROW || (mblk * MT + mt) * 16 + (lane & 15) < p.M;
@@ -365,7 +389,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int xp = 0; xp < XS; ++xp) {
-          const uint4 xv = row_ok[mt] ? x[mt][xp] : make_uint4(0, 0, 0, 0);
+          uint4 xv;
+          if constexpr (X1) xv = mt == 1 ? x1v[xp] : x[0][xp];
+          else xv = x[mt][xp];
+          xv = row_ok[mt] ? xv : make_uint4(0, 0, 0, 0);
           acc[u % UC][xp][mt][nb] = mma<T>(acc[u % UC][xp][mt][nb], wv, xv);  // chain = k-tile parity
         }
     }
@@ -497,6 +524,17 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   };
 
   zero_acc();
+  if constexpr (X1) {
+    // row 16 of this wavefront's chunk into LDS (only this wavefront reads it)
+    const int n = (k1 - k0) * XS * 4;
+    for (int c = lane; c < n; c += 64) {
+      const int kk = c / (XS * 4), xp = (c / 4) % XS, g = c % 4, kt = k0 + kk;
+      uint4 v;
+      if constexpr (XROW) v = ld16(p.x + (size_t(16) * p.x_ld + kt * KT + g * E) * ES);
+      else v = ld16(p.x + xp * p.x_plane + (size_t(p.k_tiles) + kt) * 1024 + g * 256);
+      x1_lds[(wave * X1_MAX_KTILES + kk) * XS * 4 + xp * 4 + g] = v;
+    }
+  }
   if constexpr (XRES) {
     constexpr int NBAT = KC / U;
     // A wavefront whose chunk is exactly KC k-tiles long (every chunk of the
@@ -540,13 +578,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     // further batch beside the first item's weight batch before it, so the
     // chunk arrives with the first item's weight stream instead of ahead of
     // it.
-    uint4 xr[KC][MT][XS];
+    uint4 xr[KC][MX][XS];
     auto load_x = [&](int b) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kt = min(k0 + b * U + u, kclamp);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MX; ++mt)
 #pragma unroll
           for (int xp = 0; xp < XS; ++xp) xr[b * U + u][mt][xp] = x_load(mt, kt, xp);
       }
@@ -575,7 +613,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, !EX);
+        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, b * U + u, !EX);
       }
       finish_item(item);
     }
@@ -588,7 +626,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         else issue_w(next, 0, wb[0], i + 1 < my_items);
         __builtin_amdgcn_sched_barrier(0);  // keep the next batch's loads ahead of these MFMAs
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, !EX);
+        for (int u = 0; u < U; ++u) mma_tile(u, b, wb[b & 1].w, xr[b * U + u], 0, b * U + u, !EX);
       }
       finish_item(item);
     }
@@ -597,10 +635,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     else body(std::integral_constant<bool, false>{});
   } else {
     // Activations stream with the weights; two batches in flight.
-    XWBatch<U, MT, NB, XS> fa, fb;
+    XWBatch<U, MX, NB, XS> fa, fb;
     const int T_steps = my_items * nbat;
     const int t_last = T_steps - 1;
-    auto issue = [&](int t, XWBatch<U, MT, NB, XS> &f) {
+    auto issue = [&](int t, XWBatch<U, MX, NB, XS> &f) {
       const int item = item_of(t / nbat);
       const int b = t % nbat;
       const int mblk = item / p.n_blocks;
@@ -611,16 +649,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MX; ++mt)
 #pragma unroll
           for (int xp = 0; xp < XS; ++xp) f.x[u][mt][xp] = x_load(mblk * MT + mt, kt, xp);
       }
     };
-    auto compute = [&](int t, const XWBatch<U, MT, NB, XS> &f) {
+    auto compute = [&](int t, const XWBatch<U, MX, NB, XS> &f) {
       const int b = t % nbat;
       const int mblk = item_of(t / nbat) / p.n_blocks;
 #pragma unroll
-      for (int u = 0; u < U; ++u) mma_tile(u, b, f.w, f.x[u], mblk);
+      for (int u = 0; u < U; ++u) mma_tile(u, b, f.w, f.x[u], mblk, min(k0 + b * U + u, kclamp) - k0);
     };
     rs_issue();
     __builtin_amdgcn_sched_barrier(0);
@@ -696,11 +734,11 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const ArgmaxFinishPa
   }
 }
 
-template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC>
+template <typename T, int MT, int NB, int EPI, int XS, bool XROW, int KC, bool X1 = false>
 static hipError_t launch_one(const GemmParams &p, hipStream_t s) {
   const int items = p.m_blocks * p.n_blocks;
   const dim3 grid(items < p.grid_cap ? items : p.grid_cap);
-  hipLaunchKernelGGL((gemm_kernel<T, MT, NB, EPI, XS, XROW, KC>), grid, dim3(GEMM_THREADS), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, MT, NB, EPI, XS, XROW, KC, X1>), grid, dim3(GEMM_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -726,11 +764,29 @@ static hipError_t launch_kc(const GemmParams &p, hipStream_t s) {
   return launch_one<T, MT, NB, EPI, XS, XROW, 0>(p, s);
 }
 
+// 17 rows (a 16-slot block's verify pass at batch 1): the first row tile as
+// one tile, row 16 through LDS; the first tile's activations resident when
+// its chunk is at most 16 tiles, else streamed.
+template <typename T, int NB, int EPI, int XS, bool XROW>
+static hipError_t launch_x1(const GemmParams &p, hipStream_t s) {
+  const int per = (p.k_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
+  if constexpr (XS <= 2) {
+    if (gemm_resident_ok(p.m_blocks, 1, XS, p.k_tiles)) {
+      if (per <= 8) return launch_one<T, 2, NB, EPI, XS, XROW, 8, true>(p, s);
+      if (per <= 16) return launch_one<T, 2, NB, EPI, XS, XROW, 16, true>(p, s);
+    }
+  }
+  return launch_one<T, 2, NB, EPI, XS, XROW, 0, true>(p, s);
+}
+
 template <typename T, int EPI, int NB, int XS, bool XROW>
 static hipError_t launch_xs(const GemmParams &p, hipStream_t s) {
+  const int per = (p.k_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
   switch (p.MT) {
     case 1: return launch_kc<T, 1, NB, EPI, XS, XROW>(p, s);
-    case 2: return launch_kc<T, 2, NB, EPI, XS, XROW>(p, s);
+    case 2:
+      if (p.M == 17 && p.m_blocks == 1 && per <= X1_MAX_KTILES) return launch_x1<T, NB, EPI, XS, XROW>(p, s);
+      return launch_kc<T, 2, NB, EPI, XS, XROW>(p, s);
     default: return hipErrorInvalidValue;   // more than 32 rows run tiled
   }
 }
