@@ -2,11 +2,10 @@
 // more than 17 rows, injections of more than 32: the batched draft step and
 // its heads, large injections).
 //
-// A workgroup owns a TM x TN tile of 16 x 16 output fragments (128 tokens x
-// 256 features, or 64 x 128 when the large tiles would leave compute units
-// idle) and the whole K range; its 8 wavefronts form a 2 x 4 grid of
-// sub-tiles, each accumulating (TM / 2) x (TN / 4) MFMA fragments over all of
-// K.  Per 32-column k-tile the tile's activation fragments (TM row tiles, one
+// A workgroup owns a TM x TN tile of 16 x 16 output fragments (64 to 192
+// tokens x 128 to 384 features, chosen per launch) and the whole K range or
+// one of up to 8 parts of it; its 8 wavefronts form a 2 x 4 grid of
+// sub-tiles, each accumulating (TM / 2) x (TN / 4) MFMA fragments.  Per 32-column k-tile the tile's activation fragments (TM row tiles, one
 // or two planes) and weight fragments (TN row tiles) are copied straight from
 // global memory into an LDS ring of as many stages as fit 144 KiB (global_load_lds_dwordx4, one
 // 1 KiB fragment per wavefront instruction, the same number for every

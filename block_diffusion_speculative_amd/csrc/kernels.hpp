@@ -24,9 +24,9 @@ constexpr int MAX_ROPE_HALF = 64;
 // Arrival counter of the last-arriver handshakes, at the end of the fixed area.
 constexpr size_t WS_ARRIVE_OFFSET = WS_COUNTER_BYTES - 256;
 // Split-K: partial tiles in a workspace region of SPLIT_PART_BYTES (tiled
-// launches: at most MAX_SPLIT_UNITS units of at most 128 x 256 fp32), and one
-// arrival count per item (zero between launches, at most MAX_SPLIT_ITEMS)
-// just below the arrive counter.
+// launches split only while their units' fp32 tiles fit it: 256 of 128 x 256,
+// 1024 of 64 x 128), and one arrival count per item (zero between launches,
+// at most MAX_SPLIT_ITEMS) just below the arrive counter.
 constexpr int MAX_SPLIT_UNITS = 256;
 constexpr size_t SPLIT_TILE_BYTES = size_t(128) * 256 * 4;
 constexpr size_t SPLIT_PART_BYTES = MAX_SPLIT_UNITS * SPLIT_TILE_BYTES;
