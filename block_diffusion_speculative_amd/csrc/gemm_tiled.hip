@@ -645,9 +645,11 @@ static void launch_tiled_shape(const GemmParams &p, int grid, hipStream_t s) {
 // its epilogue and, for split items, about 120 more per unit for storing its
 // partial tile and counting in and about 50 per round trip of the last
 // part's gather.  Tiles: 64 x 128 for every epilogue; 64 x 192 for
-// QKV (its rotary partner exchange does not fit a 128-row tile); 128 x 256
-// for the others; 128 x 384 for gate/up.  k-tiles split into at most 8 parts
-// of at least 8 when the workspace holds the partial tiles.
+// QKV (its rotary partner exchange does not fit a 128-row tile); 64 x 256
+// and 128 x 256 for the others; 128 x 384 for gate/up.  k-tiles split into
+// at most 8 parts of at least 8 when the workspace holds the partial tiles;
+// a split must beat the unsplit choices by 10%, about the model's error
+// against the kernel times it was fitted to.
 struct TileChoice {
   int tm, tn, ks;
 };
@@ -669,8 +671,9 @@ static TileChoice choose_tile(int M, int n_tiles, int k_tiles, int cu, bool spli
       const long rounds = ks == 1 ? 0 : fr <= 8 ? blocks(ks, 16 / fr) + 2 : long(ks) * (tm / 2) + 2;
       const long stages = 144 / (blocks(XS * tm + tn, 8) * 8);
       const long weight = stages >= 8 ? 100 : stages >= 6 ? 110 : stages >= 4 ? 115 : 125;   // percent
-      const long cost = per_wg * (blocks(k_tiles, ks) * (XS * tm + tn) * weight / 100 + 100 + (ks > 1 ? 120 : 0)) +
-                        50 * rounds;
+      long cost = per_wg * (blocks(k_tiles, ks) * (XS * tm + tn) * weight / 100 + 100 + (ks > 1 ? 120 : 0)) +
+                  50 * rounds;
+      if (ks > 1) cost += cost / 10;   // a split must win by a margin the model can resolve
       if (best_cost < 0 || cost < best_cost) {
         best_cost = cost;
         best = TileChoice{tm, tn, ks};
@@ -681,6 +684,7 @@ static TileChoice choose_tile(int M, int n_tiles, int k_tiles, int cu, bool spli
   if constexpr (EPI == EPI_QKV) {
     consider(4, 12, tl_can_split<EPI, 2, 3>());
   } else {
+    consider(4, 16, tl_can_split<EPI, 2, 4>());
     consider(8, 16, tl_can_split<EPI, 4, 4>());
     if constexpr (EPI == EPI_SWIGLU) consider(8, 24, tl_can_split<EPI, 4, 6>());
   }
@@ -748,6 +752,10 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
         return hipGetLastError();
       }
     } else {
+      if (shape == 416) {
+        launch_tiled_shape<T, EPI, XS, XROW, 4, 16, 2, 4>(p, grid, s);
+        return hipGetLastError();
+      }
       if (shape == 816) {
         launch_tiled_shape<T, EPI, XS, XROW, 8, 16, 2, 4>(p, grid, s);
         return hipGetLastError();

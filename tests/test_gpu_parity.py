@@ -145,6 +145,14 @@ def test_small_bf16_step():
     _compare_step(case, 0, [5, 17])
 
 
+def test_batch1_inject_17_rows():
+    """One sequence injecting 17 rows (a fully accepted 16-slot block plus
+    its fallback token): the fc and KV-injection launches take the skinny
+    kernel's 17-row variant (row 16 through LDS), as does the verify head."""
+    case = Hn.build_case(SMALL_BF16, 1, [90], seed=5)
+    _compare_step(case, 0, [17])
+
+
 @pytest.mark.parametrize("rows", [[15, 17], [16, 17]])
 def test_routing_boundaries(rows):
     """Launch sizes on both sides of the skinny/tiled switch: injections of
