@@ -8,7 +8,7 @@
 // and output features 4g..4g+3.
 //
 // A workgroup owns NB 16-column weight tiles for MT 16-row token tiles and the
-// whole K range.  Its 16 wavefronts split K, stream their weight tiles
+// whole K range.  Its 8 wavefronts split K, stream their weight tiles
 // with non-temporal loads, and add their partial tiles in LDS in a fixed
 // order, so the result does not depend on scheduling and no workgroup ever
 // waits on another.  The epilogue runs in the same workgroup.  The vocabulary
@@ -28,9 +28,9 @@ __device__ inline float tile_at(const f32x4 *t, int NB, int ml, int nl) {
 }
 
 // Every GEMM workgroup has 8 wavefronts (two per SIMD, so each may hold up to
-// 256 VGPRs) and splits K into the same 8 contiguous chunks whatever the
-// row-tile count.  Within a chunk, k-tiles are consumed in batches (of four
-// for one-tile items of one row tile, else two); even and odd k-tiles feed two accumulator
+// 256 VGPRs) and deals the k-tiles out to them round-robin (wavefront w takes
+// w, w + 8, ...) whatever the row-tile count.  A wavefront consumes its share
+// in batches (of four for one-tile items of one row tile, else two); even and odd k-tiles feed two accumulator
 // chains per activation plane (one chain per plane when NB * XS >= 4); chains
 // and wavefronts are summed in a fixed order.  The summation order of a row therefore never depends on how
 // many other rows share the launch.
@@ -284,10 +284,14 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_items = p.m_blocks * p.n_blocks;
   const int my_items = (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
-  const int per = (p.k_tiles + WAVES - 1) / WAVES;      // k-tiles of every wavefront's chunk
-  const int k0 = min(wave * per, p.k_tiles);
-  const int k1 = min(k0 + per, p.k_tiles);
-  const int kclamp = k1 > 0 ? k1 - 1 : 0;
+  // Wavefront w takes the k-tiles w, w + 8, w + 16, ... (its j-th is
+  // ktile(j)): the workgroup's loads in flight then cover one contiguous run
+  // of the item's weights, and the wavefronts reach the fold together
+  // (contiguous per-wavefront chunks arrived several microseconds apart).
+  const int per = (p.k_tiles + WAVES - 1) / WAVES;      // k-tiles of the longest wavefront share
+  const int nj = p.k_tiles > wave ? (p.k_tiles - wave + WAVES - 1) / WAVES : 0;   // this wavefront's
+  const int jlast = nj > 0 ? nj - 1 : 0;
+  auto ktile = [&](int j) { return min(wave + WAVES * min(j, jlast), p.k_tiles - 1); };
   const int nbat = XRES ? KC / U : (per + U - 1) / U;   // batches per item, uniform over wavefronts
   const size_t wstride = size_t(p.k_tiles) * 1024;
 
@@ -298,10 +302,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   auto item_of = [&](int i) { return int(blockIdx.x) + i * int(gridDim.x); };
   // Weight tiles of an item through a buffer resource: the item base and the
   // k-tile offset are uniform (scalar registers); a lane adds only lane * 16.
-  // Every k-tile index is clamped into the wavefront's chunk, so all offsets
+  // Every k-tile index is clamped into the wavefront's share, so all offsets
   // stay inside the item's NB rows of tiles.  NB == 2 weights use the paired
-  // layout (the two row tiles interleave per k-tile), so a wavefront's chunk
-  // of an item is one contiguous run.
+  // layout (the two row tiles interleave per k-tile), so one k-tile of an
+  // item is one contiguous run.
   // live == false: a resource of no bytes, so the loads of a prefetch past
   // the last item return zeros without a memory access (and do not hold up
   // the epilogue's own loads behind them).
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   // kk: the k-tile's index within the wavefront's chunk (X1's LDS row)
   auto mma_tile = [&](int u, int b, const uint4 (&w)[U][NB], const uint4 (&x)[MX][XS], int mblk, int kk,
                       bool chk = true) {
-    const bool ok = !chk || k0 + b * U + u < k1;
+    const bool ok = !chk || b * U + u < nj;
     uint4 x1v[XS];
     if constexpr (X1) {
 #pragma unroll
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
         // (k-tiles past the chunk, whose weights are zeroed, read zeros too:
         // that LDS was never written)
         const uint4 r = x1_lds[(wave * X1_MAX_KTILES + kk) * XS * 4 + xp * 4 + (lane >> 4)];
-        x1v[xp] = (lane & 15) == 0 && kk < k1 - k0 ? r : make_uint4(0, 0, 0, 0);
+        x1v[xp] = (lane & 15) == 0 && kk < nj ? r : make_uint4(0, 0, 0, 0);
       }
     }
     bool row_ok[MT];
@@ -526,9 +530,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   zero_acc();
   if constexpr (X1) {
     // row 16 of this wavefront's chunk into LDS (only this wavefront reads it)
-    const int n = (k1 - k0) * XS * 4;
+    const int n = nj * XS * 4;
     for (int c = lane; c < n; c += 64) {
-      const int kk = c / (XS * 4), xp = (c / 4) % XS, g = c % 4, kt = k0 + kk;
+      const int kk = c / (XS * 4), xp = (c / 4) % XS, g = c % 4, kt = wave + WAVES * kk;
       uint4 v;
       if constexpr (XROW) v = ld16(p.x + (size_t(16) * p.x_ld + kt * KT + g * E) * ES);
       else v = ld16(p.x + xp * p.x_plane + (size_t(p.k_tiles) + kt) * 1024 + g * 256);
@@ -537,18 +541,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
   }
   if constexpr (XRES) {
     constexpr int NBAT = KC / U;
-    // A wavefront whose chunk is exactly KC k-tiles long (every chunk of the
+    // A wavefront whose share is exactly KC k-tiles (every share at the
     // drafter's shapes) addresses its weights through a resource based at
-    // the chunk start: every load offset is then a compile-time constant, so
+    // its first k-tile: every load offset is then a compile-time constant, so
     // no per-k-tile offsets occupy (and spill out of) the scalar registers.
-    // Other chunks clamp their k-tile indices into the chunk.
-    const bool exact = NB <= 2 && k1 - k0 == KC;
+    // Other shares clamp their k-tile indices.
+    const bool exact = NB <= 2 && nj == KC;
     auto w_rsrc_chunk = [&](int item, bool live) {
       const int nt0 = (item % p.n_blocks) * NB;
       const int seg = nt0 / p.seg_ntiles;
       const char *base = uniform_ptr(p.w_seg[seg] + size_t(nt0 - seg * p.seg_ntiles) * wstride +
-                                     size_t(k0) * NB * 1024);
-      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, live ? KC * NB * 1024 : 0, BUF_DWORD3);
+                                     size_t(wave) * NB * 1024);
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0,
+                                               live ? ((KC - 1) * WAVES + 1) * NB * 1024 : 0, BUF_DWORD3);
     };
     auto body = [&](auto ex) {
     constexpr bool EX = decltype(ex)::value;
@@ -559,12 +564,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, ((b * U + u) * NB + nb) * 1024);
+          for (int nb = 0; nb < NB; ++nb)
+            f.w[u][nb] = ld16_buf_stream(rs, w_lane, ((b * U + u) * WAVES * NB + nb) * 1024);
       } else {
         const auto rs = w_rsrc(item, live);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int kt = min(k0 + b * U + u, kclamp);
+          const int kt = ktile(b * U + u);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
         }
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
     auto load_x = [&](int b) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kt = min(k0 + b * U + u, kclamp);
+        const int kt = ktile(b * U + u);
 #pragma unroll
         for (int mt = 0; mt < MX; ++mt)
 #pragma unroll
@@ -645,7 +651,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
       const auto rs = w_rsrc(item);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kt = min(k0 + b * U + u, kclamp);
+        const int kt = ktile(b * U + u);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) f.w[u][nb] = ld16_buf_stream(rs, w_lane, w_off(kt, nb));
 #pragma unroll
@@ -658,7 +664,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmParams p) 
       const int b = t % nbat;
       const int mblk = item_of(t / nbat) / p.n_blocks;
 #pragma unroll
-      for (int u = 0; u < U; ++u) mma_tile(u, b, f.w, f.x[u], mblk, min(k0 + b * U + u, kclamp) - k0);
+      for (int u = 0; u < U; ++u) mma_tile(u, b, f.w, f.x[u], mblk, min(b * U + u, jlast));
     };
     rs_issue();
     __builtin_amdgcn_sched_barrier(0);
