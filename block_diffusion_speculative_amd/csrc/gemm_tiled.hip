@@ -695,7 +695,10 @@ static TileChoice choose_tile(int M, int n_tiles, int k_tiles, int cu, bool spli
 //   heads (argmax): TM x 16 fragments with TM even, at most 12: one token
 //     block covering every row when it fits (each weight byte read once),
 //     else 8 or 12, whichever pads the rows less; the TM = 8 head with one
-//     activation plane is 24 fragments wide;
+//     activation plane is 24 fragments wide, and so are the TM = 4 and 6
+//     heads when that takes fewer rounds of items on the compute units (a
+//     full round streams at the chip's HBM rate whatever the width, a short
+//     last round is bound by the k-step chain, so a round saved is worth it);
 //   others: by choose_tile.
 template <typename T, int EPI, int XS, bool XROW>
 static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
@@ -714,7 +717,19 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     // the 128-row head tile is 384 features wide (one plane of activations
     // leaves the registers for it; at 10 and 12 fragments that width spills):
     // each staged weight fragment feeds more MFMAs
-    p.n_blocks = blocks(p.n_tiles, (XS == 1 && p.tile_m == 8) ? 24 : 16);
+    bool wide = XS == 1 && p.tile_m == 8;
+    if (XS == 1 && (p.tile_m == 4 || p.tile_m == 6)) {
+      // items of the busiest workgroup at width tn (XCD-aware dealing)
+      auto rounds = [&](int tn_) {
+        const int mb = blocks(p.M, 16 * p.tile_m), nb = blocks(p.n_tiles, tn_);
+        int g = mb * nb < cu ? mb * nb : cu;
+        g = g < TL_XCDS ? TL_XCDS : g - g % TL_XCDS;
+        return blocks(blocks(nb, TL_XCDS) * mb, g / TL_XCDS);
+      };
+      wide = rounds(24) < rounds(16);
+    }
+    p.n_blocks = blocks(p.n_tiles, wide ? 24 : 16);
+    tn = wide ? 24 : 16;
   } else {
     const TileChoice tc = choose_tile<EPI, XS>(p.M, p.n_tiles, p.k_tiles, cu, p.part_ws && p.part_cnt);
     p.tile_m = tc.tm;
@@ -730,8 +745,14 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
   grid = grid < TL_XCDS ? TL_XCDS : grid - grid % TL_XCDS;
   if constexpr (HEAD && XS == 1) {
     switch (p.tile_m) {
-      case 4: launch_tiled_shape<T, EPI, XS, XROW, 4, 16, 2, 4>(p, grid, s); break;
-      case 6: launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s); break;
+      case 4:
+        if (tn == 24) launch_tiled_shape<T, EPI, XS, XROW, 4, 24, 2, 4>(p, grid, s);
+        else launch_tiled_shape<T, EPI, XS, XROW, 4, 16, 2, 4>(p, grid, s);
+        break;
+      case 6:
+        if (tn == 24) launch_tiled_shape<T, EPI, XS, XROW, 6, 24, 2, 4>(p, grid, s);
+        else launch_tiled_shape<T, EPI, XS, XROW, 6, 16, 2, 4>(p, grid, s);
+        break;
       case 8: launch_tiled_shape<T, EPI, XS, XROW, 8, 24, 2, 4>(p, grid, s); break;
       case 10: launch_tiled_shape<T, EPI, XS, XROW, 10, 16, 2, 4>(p, grid, s); break;
       case 12: launch_tiled_shape<T, EPI, XS, XROW, 12, 16, 2, 4>(p, grid, s); break;
