@@ -76,17 +76,49 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tiled_kernel(const GemmPa
   // one of ksplit parts of its k-tile range.  XCD-aware order (the grid is a
   // multiple of 8): XCD x takes feature blocks x, x + 8, ...; its workgroups
   // walk those blocks' units with the part fastest, then the token block.
+  // The vocabulary heads cap every workgroup at the grid's even share of
+  // items: when the feature blocks do not split evenly over the XCDs, the few
+  // items past the cap in the fuller XCDs go, in XCD order, to the workgroups
+  // left below it (a weight block fetched once more, instead of a whole extra
+  // round for one workgroup).  The other launches keep the plain dealing,
+  // whose scalar registers they cannot spare.
+  constexpr bool EVEN = EPI == EPI_ARGMAX || EPI == EPI_LOGITS;
+  static_assert(!(EVEN && SPLIT_CODE), "the even dealing assumes unsplit items");
   const int xcd = int(blockIdx.x) % TL_XCDS, r = int(blockIdx.x) / TL_XCDS;
   const int per_xcd = int(gridDim.x) / TL_XCDS;
   const int ks = SPLIT_CODE ? p.ksplit : 1;
-  const int nb_x = (p.n_blocks - xcd + TL_XCDS - 1) / TL_XCDS;
-  const int units_x = nb_x * p.m_blocks * ks;
-  const int my_items = (units_x - r + per_xcd - 1) / per_xcd;
-  // unit index (item * ks + part) of this workgroup's i-th unit
+  const int per_nb = p.m_blocks * ks;
+  auto units_in = [&](int x) { return (p.n_blocks - x + TL_XCDS - 1) / TL_XCDS * per_nb; };
+  const int units_x = units_in(xcd);
+  // unit index (item * ks + part) of XCD x's li-th unit
+  auto unit_at = [&](int x, int li) { return (x + TL_XCDS * (li / per_nb)) * per_nb + li % per_nb; };
+  int base = (units_x - r + per_xcd - 1) / per_xcd, my_items = base, spare_before = 0, cap = 0;
+  if constexpr (EVEN) {
+    cap = (p.n_blocks * per_nb + int(gridDim.x) - 1) / int(gridDim.x);
+    const int q_x = units_x / per_xcd, rem_x = units_x % per_xcd;
+    base = min(cap, q_x + (r < rem_x ? 1 : 0));
+    // this workgroup's first slot among the grid's free slots (below the
+    // cap), and the items past the cap over the grid
+    spare_before = units_x < cap * per_xcd ? r * (cap - q_x) - min(r, rem_x) : 0;
+    int over = 0;
+    for (int x = 0; x < TL_XCDS; ++x) {
+      const int u = units_in(x);
+      over += max(0, u - cap * per_xcd);
+      if (x < xcd) spare_before += max(0, cap * per_xcd - u);
+    }
+    my_items = base + min(cap - base, max(0, over - spare_before));
+  }
+  // unit index of this workgroup's i-th unit
   auto item_of = [&](int i) {
-    const int li = r + i * per_xcd;
-    const int per_nb = p.m_blocks * ks;
-    return (xcd + TL_XCDS * (li / per_nb)) * per_nb + li % per_nb;
+    if (!EVEN || i < base) return unit_at(xcd, r + i * per_xcd);
+    int k = spare_before + (i - base);   // the k-th item past the cap
+    int x = 0;
+    for (; x < TL_XCDS - 1; ++x) {
+      const int o = max(0, units_in(x) - cap * per_xcd);
+      if (k < o) break;
+      k -= o;
+    }
+    return unit_at(x, cap * per_xcd + k);
   };
   auto k_begin = [&](int unit) { return (unit % ks) * K / ks; };
   auto k_end = [&](int unit) { return (unit % ks + 1) * K / ks; };
