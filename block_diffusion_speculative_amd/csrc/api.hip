@@ -100,9 +100,13 @@ GemmPlan plan_head(int dtype, int M, int vocab, int hidden) {
 
 // Context splits of the block attention: about half a workgroup per compute
 // unit over all (sequence, KV head) pairs, at most 16 (more splits cost the
-// merge more than they save here).
+// merge more than they save here).  Pairs that fill the compute units on
+// their own are split in two, so that with the longest contexts dispatched
+// first (sort_seqs) the halves of a ragged batch pack the compute units
+// instead of its longest sequence setting the launch's length.
 int attn_splits(const dflash_dims *d, int batch) {
   const int s = 256 / std::max(1, batch * d->n_kv_heads);
+  if (s <= 1 && batch > 1) return 2;
   return std::min(16, std::max(1, s));
 }
 
@@ -503,6 +507,8 @@ int run_layer(const LayerRun &r, const dflash_layer &lw, int l, const void *next
   a.group = d->n_q_heads / d->n_kv_heads;
   a.splits = L.S;
   a.head_split = attn_head_split(d, r.batch * L.q_tiles, L.S);
+  // more workgroups than compute units: the longest contexts go first
+  a.sort_seqs = r.batch > 1 && L.S * r.batch * L.q_tiles * d->n_kv_heads * a.head_split > compute_units() ? 1 : 0;
   a.capacity = r.capacity;
   a.scale_log2 = 1.4426950408889634f / sqrtf(float(hd));
   a.attn_out = attn_out;

@@ -72,7 +72,26 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   __shared__ uint4 lds[RING > MREC ? RING : MREC];
 
   const int z = blockIdx.x;
-  const int QT = p.q_tiles, s = blockIdx.z / QT, qt = blockIdx.z % QT;   // sequence, query tile
+  const int QT = p.q_tiles, qt = blockIdx.z % QT;   // query tile
+  int s = blockIdx.z / QT;                           // sequence
+  if (p.sort_seqs) {
+    // Workgroups are dispatched in grid order with the sequence slowest, so
+    // taking the sequences by rank (longest context first, ties by index)
+    // starts the longest work first when the grid needs more than one wave
+    // of workgroups.
+    __shared__ int ctx_s[MAX_SEQS], seq_of_rank[MAX_SEQS];
+    const int nseq = int(gridDim.z) / QT;
+    if (int(threadIdx.x) < nseq) ctx_s[threadIdx.x] = min(p.ctx_len[threadIdx.x], p.capacity);
+    __syncthreads();
+    if (int(threadIdx.x) < nseq) {
+      const int t = threadIdx.x, lt = ctx_s[t];
+      int rank = 0;
+      for (int u = 0; u < nseq; ++u) rank += ctx_s[u] > lt || (ctx_s[u] == lt && u < t);
+      seq_of_rank[rank] = t;
+    }
+    __syncthreads();
+    s = seq_of_rank[s];
+  }
   const int g = blockIdx.y / p.head_split, hs = blockIdx.y % p.head_split;
   const int gw = p.group / p.head_split;            // query heads of this workgroup
   const int waves = blockDim.x >> 6;
@@ -367,10 +386,12 @@ static hipError_t launch_merge_t(const AttnParams &p, int batch, hipStream_t s) 
   if (p.q_tiles < 1) return hipErrorInvalidValue;
   if (p.splits > ATTN_MAX_SPLITS) return hipErrorInvalidValue;
   if (p.head_dim == 128) {
-    if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 128, 16>), grid, block, 0, s, p);
+    if (p.splits <= 2) hipLaunchKernelGGL((attn_merge_kernel<T, 128, 2>), grid, block, 0, s, p);
+    else if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 128, 16>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_merge_kernel<T, 128, ATTN_MAX_SPLITS>), grid, block, 0, s, p);
   } else if (p.head_dim == 64) {
-    if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 64, 16>), grid, block, 0, s, p);
+    if (p.splits <= 2) hipLaunchKernelGGL((attn_merge_kernel<T, 64, 2>), grid, block, 0, s, p);
+    else if (p.splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<T, 64, 16>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_merge_kernel<T, 64, ATTN_MAX_SPLITS>), grid, block, 0, s, p);
   } else {
     return hipErrorInvalidValue;

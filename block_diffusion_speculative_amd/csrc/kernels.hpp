@@ -168,6 +168,7 @@ struct AttnParams {
   int block, n_q, n_kv, head_dim, group, splits, capacity;
   int head_split;                   // workgroups sharing one KV head's query group
   int q_tiles;                      // 16-row query tiles per sequence (block rows up to 16 * q_tiles)
+  int sort_seqs;                    // 1: workgroups take the sequences longest context first
   int causal;                       // block row i sees block positions <= i only
   const unsigned *row_mask;         // tree rows: block row i sees block positions j with bit j set
   float scale_log2;                 // log2(e) / sqrt(head_dim)

@@ -202,6 +202,24 @@ def test_max_batch64():
     assert rep["tokens"].compared >= 1
 
 
+def test_ragged_batch_longest_first():
+    """A batch whose (sequence, KV head) pairs fill the compute units on their
+    own (32 sequences x 8 KV heads): the block attention splits every context
+    in two, and with twice as many workgroups as compute units the workgroups
+    take the sequences longest context first, ties by index.  Ragged contexts
+    with a tie; the oracle follows the longest, the shortest, the tied pair
+    and a middle one."""
+    dims = C.Dims(hidden=512, n_q_heads=16, n_kv_heads=8, head_dim=64, n_layers=2,
+                  intermediate=1024, vocab=4096, n_feat_layers=3, dtype="bf16")
+    ctx = [(53 * s) % 257 for s in range(32)]
+    ctx[19] = ctx[7]
+    order = sorted(range(32), key=lambda s: (-ctx[s], s))
+    seqs = sorted({order[0], order[-1], 7, 19, order[16]})
+    case = Hn.build_case(dims, 32, ctx, seed=29)
+    rep = _compare_step(case, 0, [1 + s % 17 for s in range(32)], seqs=seqs)
+    assert rep["tokens"].compared >= 1
+
+
 def test_inject_exactly_to_capacity():
     """An injection that fills the cache to its last position is accepted
     (no status bit) and the draft reads every cached position."""
