@@ -24,6 +24,7 @@
 // sum) records that attn_merge_kernel combines.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "gemm_util.hpp"
 
 namespace dflash {
 
@@ -269,14 +270,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     }
     if (final_out) {
       if (qt * 16 + q < p.block) {
+        // four consecutive channels: one 16-byte and one packed store
         const int row = s * p.block + qt * 16 + q;
-        const int nqd = p.n_q * HD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = h * HD + dv * 16 + 4 * (lane >> 4) + i;
-          p.attn_out[size_t(row) * nqd + col] = acc[i] * inv;
-          store_split<T>(p.xo + packed_offset<T>(row, col, p.xo_kt), p.xo_plane, p.xs, acc[i] * inv);
-        }
+        const int col = h * HD + dv * 16 + 4 * (lane >> 4);
+        const f32x4 v = acc * inv;
+        *reinterpret_cast<f32x4 *>(p.attn_out + size_t(row) * (p.n_q * HD) + col) = v;
+        store_split4<T>(p.xo + packed_offset<T>(row, col, p.xo_kt), p.xo_plane, p.xs, v);
       }
     } else {
       reinterpret_cast<f32x4 *>(rec)[dv * 64 + lane] = acc;
@@ -322,16 +321,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
     }
   }
   if (qt * 16 + q >= p.block) return;
-  const float inv = 1.0f / L;
+  // four consecutive channels: one 16-byte and one packed store
   const int row = s * p.block + qt * 16 + q;
-  const int nqd = p.n_q * HD;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int col = h * HD + dv * 16 + 4 * (lane >> 4) + i;
-    const float v = acc[i] * inv;
-    p.attn_out[size_t(row) * nqd + col] = v;
-    store_split<T>(p.xo + packed_offset<T>(row, col, p.xo_kt), p.xo_plane, p.xs, v);
-  }
+  const int col = h * HD + dv * 16 + 4 * (lane >> 4);
+  const f32x4 v = acc * (1.0f / L);
+  *reinterpret_cast<f32x4 *>(p.attn_out + size_t(row) * (p.n_q * HD) + col) = v;
+  store_split4<T>(p.xo + packed_offset<T>(row, col, p.xo_kt), p.xo_plane, p.xs, v);
 }
 
 template <typename T, int HD, int XS, int NW, bool MASK>
