@@ -751,12 +751,13 @@ static hipError_t launch_tiled_one(const GemmParams &p0, hipStream_t s) {
     // each staged weight fragment feeds more MFMAs
     bool wide = XS == 1 && p.tile_m == 8;
     if (XS == 1 && (p.tile_m == 4 || p.tile_m == 6)) {
-      // items of the busiest workgroup at width tn (XCD-aware dealing)
+      // items of the busiest workgroup at width tn (heads deal their items
+      // evenly over the grid)
       auto rounds = [&](int tn_) {
-        const int mb = blocks(p.M, 16 * p.tile_m), nb = blocks(p.n_tiles, tn_);
-        int g = mb * nb < cu ? mb * nb : cu;
+        const int items_ = blocks(p.M, 16 * p.tile_m) * blocks(p.n_tiles, tn_);
+        int g = items_ < cu ? items_ : cu;
         g = g < TL_XCDS ? TL_XCDS : g - g % TL_XCDS;
-        return blocks(blocks(nb, TL_XCDS) * mb, g / TL_XCDS);
+        return blocks(items_, g);
       };
       wide = rounds(24) < rounds(16);
     }
