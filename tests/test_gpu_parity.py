@@ -187,6 +187,22 @@ def test_large_vocab_batch16_big_tiles():
     _compare_step(case, 0, [(5 * s) % 17 for s in range(16)], seqs=[0, 7, 15])
 
 
+@pytest.mark.parametrize("batch,vocab", [(4, 98304), (12, 4608)])
+def test_head_rounds_wide_and_even(batch, vocab):
+    """Head item dealing.  Batch 4 over a 98304-token vocabulary: the draft
+    head (64 rows) and the verify head (68 rows) run tiles 24 fragments wide
+    (256 items, one round, where 16 wide would take 384 items and two).  Batch
+    12 over 4608 tokens: the verify head's 204 rows run 128 x 384 tiles, 24
+    items on a 24-workgroup grid whose first four XCDs hold four items each
+    for three workgroups, so one item of each goes to a workgroup of another
+    XCD.  Tokens and acceptance against the oracle."""
+    d = C.Dims(**{**SMALL_BF16.__dict__, "vocab": vocab})
+    ctx = [(41 * s) % 120 for s in range(batch)]
+    case = Hn.build_case(d, batch, ctx, seed=31)
+    rep = _compare_step(case, 0, [1 + (3 * s) % 17 for s in range(batch)], seqs=[0, batch - 1])
+    assert rep["tokens"].compared >= 1
+
+
 def test_split_k_batch5():
     case = Hn.build_case(SPLIT_BF16, 5, [3, 70, 129, 200, 31], seed=13)
     _compare_step(case, 0, [17, 17, 17, 17, 17])
